@@ -1,0 +1,93 @@
+"""Pin checks for the oracle: each takes the oracle function(s) under test as
+arguments and raises AssertionError on a violation, so the same check is run
+against the real oracle (tests/test_oracle_*.py) and against deliberately
+broken copies of it (tests/test_oracle_mutations.py).
+
+Every check relies on something other than the oracle's own formula: a
+brute-force enumeration, exact rational arithmetic, an invariant the pages'
+claims imply, or a library routine."""
+import itertools
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+
+def check_box(page_box, keys: np.ndarray):
+    """Page bounding box (TinyServe §2.1) by brute force: m <= k <= M for every
+    key, and every m_i / M_i equals (bitwise) some key's value."""
+    m, M = page_box(keys)
+    assert m.shape == M.shape == keys.shape[1:]
+    assert np.all(keys >= m[None, :]) and np.all(keys <= M[None, :])
+    for i in range(keys.shape[1]):
+        col = keys[:, i]
+        assert any(np.float64(c).tobytes() == np.float64(m[i]).tobytes() for c in col), i
+        assert any(np.float64(c).tobytes() == np.float64(M[i]).tobytes() for c in col), i
+
+
+def check_corners(bound_score, q: np.ndarray, m: np.ndarray, M: np.ndarray):
+    """The largest value of the linear function x -> q.x over the box [m, M]
+    is attained at a corner; enumerate all 2^D corners with exact rationals.
+    The page score must equal that maximum (TinyServe §2.2)."""
+    D = len(q)
+    qf = [Fraction(float(x)) for x in q]
+    best = None
+    for bits in itertools.product((0, 1), repeat=D):
+        v = sum(qf[i] * Fraction(float(M[i] if bits[i] else m[i])) for i in range(D))
+        best = v if best is None else max(best, v)
+    s = bound_score(q, m, M)
+    assert Fraction(s) == best, (s, float(best))
+
+
+def check_bound(bound_score, page_box, q: np.ndarray, keys: np.ndarray):
+    """Upper-bound claim (TinyServe §2.2), exactly: score >= max_t q.k_t,
+    with equality when the page holds a single distinct key."""
+    m, M = page_box(keys)
+    s = Fraction(bound_score(q, m, M))
+    qf = [Fraction(float(x)) for x in q]
+    best = max(sum(qf[i] * Fraction(float(k[i])) for i in range(len(q))) for k in keys)
+    assert s >= best, (float(s), float(best))
+    if np.all(keys == keys[0:1]):
+        assert s == best
+
+
+def check_topk_row(topk_row, scores: np.ndarray, n: int, k: int):
+    """Selection invariant: |sel| = min(k, n), ascending, and every selected
+    page a beats every unselected page b: S_a > S_b, or S_a == S_b and a < b."""
+    sel = [int(x) for x in topk_row(scores, n, k)]
+    assert len(sel) == min(k, n)
+    assert sel == sorted(sel) and len(set(sel)) == len(sel)
+    chosen = set(sel)
+    s = np.asarray(scores, dtype=np.float64)
+    for a in chosen:
+        for b in range(n):
+            if b in chosen:
+                continue
+            assert s[a] > s[b] or (s[a] == s[b] and a < b), (a, b, s[a], s[b])
+    return sel
+
+
+def check_topk_unique(topk_row, scores: np.ndarray, k: int):
+    """Tiny n: enumerate every subset of size min(k, n); exactly one satisfies
+    the selection invariant, and it is the oracle's."""
+    n = len(scores)
+    keff = min(k, n)
+    s = np.asarray(scores, dtype=np.float64)
+    good = []
+    for sub in itertools.combinations(range(n), keff):
+        ch = set(sub)
+        if all(s[a] > s[b] or (s[a] == s[b] and a < b) for a in ch for b in range(n) if b not in ch):
+            good.append(list(sub))
+    assert len(good) == 1
+    assert [int(x) for x in topk_row(scores, n, k)] == good[0]
+
+
+def sdpa_reference(qv: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float):
+    """A library routine: torch's CPU scaled_dot_product_attention in float64
+    for one query; lse from torch.logsumexp."""
+    q = torch.from_numpy(qv).view(1, 1, 1, -1)
+    k = torch.from_numpy(np.ascontiguousarray(keys)).view(1, 1, keys.shape[0], -1)
+    v = torch.from_numpy(np.ascontiguousarray(vals)).view(1, 1, vals.shape[0], -1)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale)
+    lse = torch.logsumexp(scale * (k[0, 0] @ q[0, 0, 0]), dim=0)
+    return o.view(-1).numpy(), float(lse)
