@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark: sparse paged decode with query-aware page selection on one GPU.
+
+A step is one pass of the whole hot path over one batch of decode queries:
+  tail-page metadata refresh -> upper-bound page scores -> top-K pages ->
+  split-K flash-decode over the selected pages (+ log-sum-exp merge).
+The default workload is the sparse-decode configuration (batch 16, GQA 32/8,
+head_dim 128, 8192-token contexts, 153-page budget, bf16). Inputs are seeded
+synthetic data resident in HBM before timing starts. Steps rotate over
+several copies of the KV pool so that consecutive steps do not hit in the
+last-level cache.
+
+Prints one JSON line (see --help). Timed region 1 (the reported value)
+replays the steps as a HIP graph; timed region 2 launches the same calls
+eagerly with HIP events between the stages, giving the per-stage times and
+the decode kernel's roofline. The CPU oracle is timed on a bounded sample.
+"""
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse paged decode: queries/s and effective KV HBM GB/s vs MI355X peak"
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2_sparse",
+                    choices=["c2_sparse", "c3_dense", "c4_long", "c5_cascade"])
+    ap.add_argument("--replicas", type=int, default=4, help="KV pool copies rotated over steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    return ap.parse_args()
+
+
+def cpu_info():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the decode path shards over "
+                          "sequences and KV heads without any exchange, and no multi-GPU run is made; "
+                          "use --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    from query_aware_sparse_page_amd import accounting, qsa
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    if args.config == "c5_cascade":
+        case = workloads.c5_cascade(device=dev, selective=True)
+    else:
+        case = getattr(workloads, args.config)(device=dev)
+    print(f"[bench] {args.config}: B={case.B} Hq={case.Hq} Hkv={case.Hkv} D={case.D} "
+          f"lens={min(case.seq_lens_list())}..{max(case.seq_lens_list())} k={case.k_pages} "
+          f"(generated in {time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
+    B, Hq, Hkv, D = case.B, case.Hq, case.Hkv, case.D
+    lens = case.seq_lens_list()
+    k = case.k_pages
+    stride = max(-(-L // 16) for L in lens)
+    elem = 2 if case.dtype == "bf16" else 4
+
+    # ---- replicas of the pool (and their metadata), built untimed
+    R = max(1, args.replicas)
+    kvs, metas = [], []
+    for r in range(R):
+        kp = case.k_pool if r == 0 else case.k_pool.clone()
+        vp = case.v_pool if r == 0 else case.v_pool.clone()
+        kv = qsa.PagedKV(kp, vp, case.page_indptr, case.page_indices, case.seq_lens, lens)
+        kvs.append(kv)
+        metas.append(qsa.build_page_meta(kv))
+    torch.cuda.synchronize()
+
+    gs = torch.empty(B, Hkv, stride, dtype=torch.float32, device=dev)
+    sel = torch.empty(B, Hkv, max(k or 1, 1), dtype=torch.int32, device=dev)
+    cnt = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    cascade = args.config == "c5_cascade"
+    if cascade:
+        ws_bytes = qsa.cascade_workspace_size(kvs[0], Hq, case.prefix_len, k or 0)
+    else:
+        ws_bytes = qsa.decode_workspace_size(kvs[0], Hq, k or 0)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def stage_meta(r):
+        qsa.build_page_meta(kvs[r], meta=metas[r], tail_pages=1)
+
+    def stage_score(r):
+        qsa.score_pages(case.q, kvs[r], metas[r], stride=stride, out=gs)
+
+    def stage_topk(r):
+        qsa.topk_pages(gs, kvs[r], k, num_q_heads=Hq, with_phys=False, out=(sel, cnt, None))
+
+    def stage_decode(r):
+        s, c = (sel, cnt) if k else (None, None)
+        if cascade:
+            qsa.cascade_decode(case.q, case.prefix_pages, case.prefix_len, kvs[r], sel=s, sel_count=c,
+                               sm_scale=case.sm_scale, workspace=ws, out=(out, lse))
+        else:
+            qsa.paged_decode(case.q, kvs[r], sel=s, sel_count=c, sm_scale=case.sm_scale, workspace=ws,
+                             out=(out, lse))
+
+    stages = [("meta_tail", stage_meta)]
+    if k:
+        stages += [("score", stage_score), ("topk", stage_topk)]
+    stages += [("decode", stage_decode)]
+
+    def step(i):
+        r = i % R
+        for _, fn in stages:
+            fn(r)
+
+    # ---- warm-up (eager), reference output of replica 0
+    for i in range(args.warmup):
+        step(i)
+    step(0)
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+
+    # ---- timed region 1: the steps, replayed as a graph (or eager)
+    K = args.steps
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(R):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            # replica R-1 ran last; compare with an eager run of it
+        out_graph = out.clone()
+        step(R - 1)
+        torch.cuda.synchronize()
+        graph_matches = bool(torch.equal(out_graph, out))
+        reps = max(1, K // R)
+        K = reps * R
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        ev0.record()
+        for _ in range(reps):
+            graph.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms_total = ev0.elapsed_time(ev1)
+    else:
+        graph_matches = None
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        ev0.record()
+        for i in range(K):
+            step(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / K
+
+    # ---- timed region 2: eager, HIP events between the stages
+    K2 = min(args.steps, 100)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K2)]
+    torch.cuda.synchronize()
+    for i in range(K2):
+        r = i % R
+        evs[i][0].record()
+        for si, (_, fn) in enumerate(stages):
+            fn(r)
+            evs[i][si + 1].record()
+    torch.cuda.synchronize()
+    stage_ms = {}
+    for si, (name, _) in enumerate(stages):
+        vals = sorted(evs[i][si].elapsed_time(evs[i][si + 1]) for i in range(K2))
+        stage_ms[name] = {"mean": sum(vals) / K2, "median": vals[K2 // 2], "p90": vals[int(0.9 * (K2 - 1))]}
+    eager_step_ms = sum(v["mean"] for v in stage_ms.values())
+
+    # ---- byte accounting (algorithmic)
+    if cascade:
+        dec = accounting.decode_bytes(lens, Hq, Hkv, D, elem, k=k)
+        pre_kv = case.prefix_len * Hkv * D * 2 * elem
+        dec["kv"] += pre_kv
+        dec["total"] += pre_kv
+    else:
+        dec = accounting.decode_bytes(lens, Hq, Hkv, D, elem, k=k)
+    sc = accounting.score_bytes(lens, Hq, Hkv, D, elem) if k else {"total": 0}
+    tk = accounting.topk_bytes(lens, Hkv, k) if k else {"total": 0}
+    mt = accounting.meta_bytes(lens, Hkv, D, elem, tail_pages=1)
+    step_bytes = dec["total"] + sc["total"] + tk["total"] + mt["total"]
+    qps = B / (ms_step / 1e3)
+    dec_ms = stage_ms["decode"]["mean"]
+    achieved = dec["total"] / (dec_ms / 1e3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic (seeded; inputs resident in HBM)",
+        "config": {
+            "workload": f"{args.config}: batch {B}, GQA {Hq}/{Hkv}, head_dim {D}, page 16, "
+                        f"context {min(lens)}..{max(lens)}, "
+                        + (f"top-{k} pages per (sequence, KV head)" if k else "all pages (dense)")
+                        + (f", shared prefix {case.prefix_len}" if cascade else ""),
+            "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": 16,
+            "budget_pages": k, "kv_pool_replicas": R, "timing": "hip graph replay" if graph else "eager",
+        },
+        "effective_kv_gbps": round(dec["kv"] / (ms_step / 1e3) / 1e9, 1),
+        "step_algorithmic_gbps": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
+        "step_bytes": step_bytes,
+        "stage_ms": {n: round(v["mean"], 5) for n, v in stage_ms.items()},
+        "eager_step_ms": round(eager_step_ms, 5),
+        "wall_s_timed_region": round(wall, 4),
+        "graph_replay_matches_eager": graph_matches,
+        "roofline": {
+            "kernel": "paged decode (split-K + LSE merge)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": dec["total"],
+            "avg_launch_ms": round(dec_ms, 5),
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args, kvs[0], metas[0])
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(case, args, kv, meta):
+    """The CPU oracle, as it stands, on a bounded sample of the workload: whole
+    decode steps (tail metadata, scores, top-K, attention) for a few sequences
+    of the batch, BLAS pinned to one thread."""
+    import numpy as np
+    import torch
+
+    from oracle import qsa_oracle as O
+
+    from threadpoolctl import threadpool_limits
+    limiter = threadpool_limits(1)
+
+    def st(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    lens = case.seq_lens_list()
+    indptr = case.page_indptr.cpu().tolist()
+    done = 0
+    t_work = 0.0
+    b = 0
+    while t_work < args.cpu_seconds and done < 8 * case.B:
+        # one sequence: gather its pages to a compact pool (input marshalling, untimed)
+        phys = case.page_indices[indptr[b]:indptr[b + 1]].to(torch.int64)
+        pool_k = st(case.k_pool[phys])
+        pool_v = st(case.v_pool[phys])
+        q = st(case.q[b:b + 1])
+        ip = np.array([0, len(phys)], dtype=np.int32)
+        ix = np.arange(len(phys), dtype=np.int32)
+        sl = np.array([lens[b]], dtype=np.int32)
+        meta0 = O.build_page_meta(pool_k, case.dtype, ip, ix, sl)
+        t0 = time.perf_counter()
+        m1 = O.build_page_meta(pool_k, case.dtype, ip, ix, sl, tail_pages=1, meta_init=meta0)
+        if case.k_pages:
+            _, grp = O.score_pages(q, case.dtype, m1, case.dtype, ip, ix, sl, case.Hkv)
+            s, c = O.topk_pages(grp, sl, case.k_pages)
+            O.paged_decode(q, pool_k, pool_v, case.dtype, ip, ix, sl, case.sm_scale, sel=s, sel_count=c)
+        else:
+            O.paged_decode(q, pool_k, pool_v, case.dtype, ip, ix, sl, case.sm_scale)
+        t_work += time.perf_counter() - t0
+        done += 1
+        b = (b + 1) % case.B
+    limiter.restore_original_limits()
+    return {
+        "value": round(done / t_work, 3),
+        "unit": "queries/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} decode queries (sequences of the batch, cycled), full step each: tail "
+                  f"metadata, scores, top-K, attention (NumPy fp64, BLAS 1 thread), {t_work:.1f} s of CPU work",
+        "cpu": cpu_info(),
+        "host_cpus_available": len(os.sched_getaffinity(0)),
+    }
+
+
+if __name__ == "__main__":
+    main()

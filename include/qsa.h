@@ -1,0 +1,181 @@
+/*
+ * libqsa - query-aware sparse paged decode for AMD MI355X (gfx950).
+ *
+ * Single-token decode attention over a paged KV cache with query-aware page
+ * selection, as stated on the TinyServe page ("KV缓存优化的核心挑战与TinyServe
+ * 解决方案"): per-page min/max key metadata (§2.1), an upper-bound page score
+ * (§2.2), top-K page selection and attention over only the selected pages
+ * (§2.3); plus a shared-prefix cascade merged by log-sum-exp (Quail page,
+ * join attention). The page table follows PagedAttention (CS336 lecture 10
+ * page, §9.2) and Vortex's (b, p, I) paged-layout view (Vortex digest page,
+ * vTensor).
+ *
+ * Conventions for every call:
+ *  - Ownership: the caller owns every buffer. The library never allocates or
+ *    frees device memory and keeps no state between calls; scratch space is a
+ *    caller-provided workspace of the size the *_workspace_size query returns.
+ *  - Ordering: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and the call returns without synchronising. Outputs are valid
+ *    once the stream reaches that point.
+ *  - Pointers are device pointers unless named *_host.
+ *  - Errors: every call returns a qsa_status; on failure nothing has been
+ *    enqueued (argument errors) or the launch failed (QSA_ERR_DEVICE), and
+ *    qsa_last_error() returns a message for the calling thread. Nothing
+ *    throws across this interface.
+ *  - Supported shapes: page_size 16; (dtype, head_dim) = (QSA_BF16, 128) or
+ *    (QSA_F32, 64) - both make one (page, KV head) tile 4 KiB; group size
+ *    g = Hq / Hkv in {1, 2, 4, 8}. Other shapes return QSA_ERR_UNSUPPORTED.
+ *  - Robustness: a logical page index outside [0, n_b) or a physical page id
+ *    outside [0, num_phys_pages) is skipped (treated as holding no tokens),
+ *    never dereferenced.
+ */
+#ifndef QSA_H_
+#define QSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qsa_status {
+  QSA_OK = 0,
+  QSA_ERR_INVALID_ARG = 1, /* NULL pointer, inconsistent sizes, k < 1, ...   */
+  QSA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim/dtype/group size */
+  QSA_ERR_WORKSPACE = 3,   /* workspace smaller than the size query returns */
+  QSA_ERR_DEVICE = 4       /* a HIP launch or runtime call failed            */
+} qsa_status;
+
+typedef enum qsa_dtype { QSA_F32 = 0, QSA_BF16 = 1 } qsa_dtype;
+
+/* Problem sizes. B = num_seqs, Hq = num_q_heads, Hkv = num_kv_heads
+ * (Hq % Hkv == 0; query head hq belongs to KV head hq / (Hq/Hkv)),
+ * D = head_dim, page_size = tokens per page (16). dtype is the element type
+ * of q, both pools and the page metadata. */
+typedef struct qsa_dims {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t dtype; /* qsa_dtype */
+} qsa_dims;
+
+/* A paged KV cache seen through a block table (CS336 page §9.2; Vortex's
+ * (b, p, I)). Logical page j of sequence b lives at physical slot
+ * page_indices[page_indptr[b] + j], for j < n_b = ceil(seq_lens[b] / 16);
+ * the last page holds seq_lens[b] - 16 (n_b - 1) valid tokens. Table entries
+ * beyond n_b are ignored. Physical slots may be shared between sequences
+ * (prefix sharing) and are visited once per referencing sequence. */
+typedef struct qsa_paged_kv {
+  const void* k_pool;            /* [num_phys_pages, Hkv, page_size, D]  */
+  const void* v_pool;            /* same shape as k_pool                  */
+  int32_t num_phys_pages;
+  const int32_t* page_indptr;    /* [B + 1], non-decreasing               */
+  const int32_t* page_indices;   /* [page_indptr[B]] physical slots       */
+  const int32_t* seq_lens;       /* [B] tokens per sequence, each >= 1    */
+  const int32_t* seq_lens_host;  /* [B] host copy of seq_lens (planning)  */
+} qsa_paged_kv;
+
+/* Step 1 - per-page bounding-box metadata (TinyServe §2.1; refreshed every
+ * decode step per §5.3). For each sequence b, logical page j and KV head h,
+ * with p = the physical slot: meta[p][h][0][i] = min and meta[p][h][1][i] =
+ * max over the page's valid tokens of K[p][h][t][i], under IEEE total order
+ * (-0 < +0), so the values are exact copies of key elements (bit-exact).
+ * meta: [num_phys_pages, Hkv, 2, D] in dims->dtype; only slots reachable
+ * through the table are written. tail_pages = 0 rebuilds every page;
+ * tail_pages = n > 0 rebuilds only the last n pages of each sequence (the
+ * per-step update after a token is appended). Reads kv->k_pool only. */
+qsa_status qsa_build_page_meta(const qsa_dims* dims, const qsa_paged_kv* kv,
+                               int32_t tail_pages, void* meta,
+                               hipStream_t stream);
+
+/* Step 2 - upper-bound page score (TinyServe §2.2):
+ *   s[b][hq][j] = sum_i q[b][hq][i] * (q[b][hq][i] > 0 ? M_j[i] : m_j[i])
+ * with (m_j, M_j) the metadata of logical page j of sequence b for KV head
+ * hq / g, accumulated in fp32 (no softmax scale: the ranking does not
+ * depend on it). group_scores[b][h][j] = max over the g query heads of KV
+ * head h (this keeps the bound: it is >= every group head's largest q.k in
+ * the page). Layouts: q [B, Hq, D] in dtype; group_scores [B, Hkv, stride]
+ * fp32; head_scores [B, Hq, stride] fp32 or NULL. Entries n_b <= j < stride
+ * are written as -inf. Requires stride >= max_b n_b. */
+qsa_status qsa_score_pages(const qsa_dims* dims, const void* q,
+                           const qsa_paged_kv* kv, const void* meta,
+                           float* group_scores, float* head_scores,
+                           int32_t stride, hipStream_t stream);
+
+/* Step 3 - top-K page selection per (sequence, KV head) (TinyServe §2.3; the
+ * radix select of the Vortex digest, optimisations). For each (b, h):
+ * the K_eff = min(k, n_b) logical pages with the largest group score, ties
+ * (equal fp32 values, -0 == +0) broken towards the smaller page index.
+ * Outputs: sel [B, Hkv, k] int32, ascending page order, padded with -1;
+ * sel_count [B, Hkv] = K_eff; sel_phys [B, Hkv, k] (or NULL) = the physical
+ * slots of sel, -1 padded. Workspace: qsa_topk_workspace_size bytes (may be
+ * 0; ws may then be NULL). */
+qsa_status qsa_topk_pages(const qsa_dims* dims, const qsa_paged_kv* kv,
+                          const float* group_scores, int32_t stride, int32_t k,
+                          int32_t* sel, int32_t* sel_count, int32_t* sel_phys,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Step 4 - split-K flash-decode over the selected pages (TinyServe §2.3
+ * stages 3-4; flash decoding per the CS336 page §9.2 and the Quail page).
+ * For each (b, hq) with h = hq / g: attention of q[b][hq] over the valid
+ * tokens of the pages sel[b][h][0 .. sel_count[b][h]) of sequence b, read in
+ * place through the page table; sel == NULL means every page (dense paged
+ * decode - the same kernels, so selecting every page gives bit-identical
+ * results). z_t = sm_scale * q.k_t; out = sum_t e^{z_t} v_t / sum_t e^{z_t}
+ * (fp32 [B, Hq, D]); lse = ln sum_t e^{z_t} (fp32 [B, Hq], or NULL).
+ * sel: [B, Hkv, k] logical page indices; sel_count [B, Hkv] (each in
+ * [1, k]); k is the row stride of sel. Pages are split into work units that
+ * run in parallel and are merged by log-sum-exp. Workspace:
+ * qsa_decode_workspace_size(dims, seq_lens_host, sel ? k : 0). */
+qsa_status qsa_paged_decode(const qsa_dims* dims, const void* q,
+                            const qsa_paged_kv* kv, const int32_t* sel,
+                            const int32_t* sel_count, int32_t k, float sm_scale,
+                            float* out, float* lse, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Step 5 - shared-prefix cascade decode (Quail page, join attention: all
+ * queries attend the shared anchor once, each sequence attends its own
+ * suffix, the two partial results merge by LSE rescaling). The prefix is
+ * prefix_len tokens stored once at physical slots prefix_pages[0 ..
+ * ceil(prefix_len/16)) of kv->k_pool / kv->v_pool; it is attended whole by
+ * every sequence, as a dense [B*g, D] x [D, prefix_len] contraction per KV
+ * head on the matrix cores. The suffix is kv's per-sequence table, attended
+ * as in qsa_paged_decode (all pages when sel == NULL, else the selection).
+ * out/lse as in qsa_paged_decode, over prefix ∪ suffix. Requires bf16,
+ * head_dim 128. Workspace: qsa_cascade_workspace_size(...). */
+qsa_status qsa_cascade_decode(const qsa_dims* dims, const void* q,
+                              const int32_t* prefix_pages, int32_t prefix_len,
+                              const qsa_paged_kv* kv, const int32_t* sel,
+                              const int32_t* sel_count, int32_t k,
+                              float sm_scale, float* out, float* lse, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/* Workspace sizes in bytes (0 on invalid arguments). k <= 0 means dense. */
+size_t qsa_topk_workspace_size(const qsa_dims* dims, int32_t max_pages, int32_t k);
+size_t qsa_decode_workspace_size(const qsa_dims* dims, const int32_t* seq_lens_host, int32_t k);
+size_t qsa_cascade_workspace_size(const qsa_dims* dims, int32_t prefix_len,
+                                  const int32_t* suffix_lens_host, int32_t k);
+
+/* The decode work split the library will use: pages per work unit and the
+ * largest number of units of one (b, h). Returns QSA_ERR_INVALID_ARG on bad
+ * arguments. */
+qsa_status qsa_decode_plan(const qsa_dims* dims, const int32_t* seq_lens_host,
+                           int32_t k, int32_t* chunk_pages, int32_t* max_units);
+
+/* floor(budget_tokens / page_size): a token budget in whole pages (>= 0). */
+int32_t qsa_budget_pages(int32_t budget_tokens, int32_t page_size);
+
+const char* qsa_status_string(qsa_status status);
+const char* qsa_last_error(void);
+int32_t qsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H_ */

@@ -1,0 +1,347 @@
+// The libqsa C ABI: argument validation, work planning and kernel launches on
+// the caller's stream. Declarations and contracts are in include/qsa.h.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "../../include/qsa.h"
+#include "qsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qsa_status fail(qsa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+qsa_status ok() {
+  g_last_error.clear();
+  return QSA_OK;
+}
+
+qsa_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(QSA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int pages_of(int L) { return (L + 15) / 16; }
+
+// Shape checks shared by every entry point.
+qsa_status check_dims(const qsa_dims* d) {
+  if (d == nullptr) return fail(QSA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->num_seqs < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1)
+    return fail(QSA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d D=%d)", d->num_seqs,
+                d->num_q_heads, d->num_kv_heads, d->head_dim);
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(QSA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->page_size != 16) return fail(QSA_ERR_UNSUPPORTED, "page_size %d (only 16)", d->page_size);
+  if (d->dtype != QSA_BF16 && d->dtype != QSA_F32)
+    return fail(QSA_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (!((d->dtype == QSA_BF16 && d->head_dim == 128) || (d->dtype == QSA_F32 && d->head_dim == 64)))
+    return fail(QSA_ERR_UNSUPPORTED, "head_dim %d with dtype %d (built: bf16/128, f32/64)",
+                d->head_dim, d->dtype);
+  const int g = d->num_q_heads / d->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(QSA_ERR_UNSUPPORTED, "group size %d (built: 1, 2, 4, 8)", g);
+  return QSA_OK;
+}
+
+qsa_status check_kv(const qsa_dims* d, const qsa_paged_kv* kv, bool need_v, int* max_pages) {
+  if (kv == nullptr) return fail(QSA_ERR_INVALID_ARG, "kv is NULL");
+  if (kv->k_pool == nullptr || (need_v && kv->v_pool == nullptr))
+    return fail(QSA_ERR_INVALID_ARG, "k_pool/v_pool is NULL");
+  if (kv->page_indptr == nullptr || kv->page_indices == nullptr || kv->seq_lens == nullptr ||
+      kv->seq_lens_host == nullptr)
+    return fail(QSA_ERR_INVALID_ARG, "page table or seq_lens pointer is NULL");
+  if (kv->num_phys_pages < 1) return fail(QSA_ERR_INVALID_ARG, "num_phys_pages must be >= 1");
+  int mx = 0;
+  for (int b = 0; b < d->num_seqs; ++b) {
+    const int L = kv->seq_lens_host[b];
+    if (L < 1) return fail(QSA_ERR_INVALID_ARG, "seq_lens[%d] = %d (must be >= 1)", b, L);
+    mx = std::max(mx, pages_of(L));
+  }
+  *max_pages = mx;
+  return QSA_OK;
+}
+
+qsa::LaunchCommon common(const qsa_dims* d, const qsa_paged_kv* kv) {
+  qsa::LaunchCommon c;
+  c.B = d->num_seqs;
+  c.Hq = d->num_q_heads;
+  c.Hkv = d->num_kv_heads;
+  c.D = d->head_dim;
+  c.G = c.Hq / c.Hkv;
+  c.bf16 = d->dtype == QSA_BF16;
+  if (kv != nullptr) {
+    c.k_pool = kv->k_pool;
+    c.v_pool = kv->v_pool;
+    c.num_phys = kv->num_phys_pages;
+    c.page_indptr = kv->page_indptr;
+    c.page_indices = kv->page_indices;
+    c.seq_lens = kv->seq_lens;
+  }
+  return c;
+}
+
+// Work units wanted per launch: enough to give every CU several workgroups.
+int target_units() {
+  static const int t = [] {
+    const char* e = std::getenv("QSA_DECODE_TARGET_UNITS");
+    int v = e ? std::atoi(e) : 0;
+    return v > 0 ? v : 2048;
+  }();
+  return t;
+}
+
+// Pages per unit: the largest chunk that still yields target_units() units;
+// counts per (b, h) row are min(k, n_b) (every page when k <= 0).
+qsa::DecodePlan make_plan(const qsa_dims* d, const int32_t* lens, int32_t k) {
+  static const int kChunks[] = {256, 128, 64, 32, 16, 8, 4};
+  qsa::DecodePlan plan;
+  int maxc = 0;
+  for (int b = 0; b < d->num_seqs; ++b) {
+    int c = pages_of(lens[b]);
+    if (k > 0) c = std::min(c, (int)k);
+    maxc = std::max(maxc, c);
+  }
+  plan.chunk = 4;
+  for (int ch : kChunks) {
+    long long units = 0;
+    for (int b = 0; b < d->num_seqs; ++b) {
+      int c = pages_of(lens[b]);
+      if (k > 0) c = std::min(c, (int)k);
+      units += (long long)d->num_kv_heads * ((c + ch - 1) / ch);
+    }
+    if (units >= target_units()) {
+      plan.chunk = ch;
+      break;
+    }
+  }
+  plan.max_units = (maxc + plan.chunk - 1) / plan.chunk;
+  return plan;
+}
+
+struct DecodeWs {
+  size_t o_bytes = 0, ml_bytes = 0;
+  size_t total() const { return align_up(o_bytes) + align_up(ml_bytes); }
+};
+
+DecodeWs decode_ws(const qsa_dims* d, const qsa::DecodePlan& plan) {
+  const size_t units = (size_t)d->num_seqs * d->num_kv_heads * plan.max_units;
+  const int g = d->num_q_heads / d->num_kv_heads;
+  DecodeWs w;
+  w.o_bytes = units * g * d->head_dim * sizeof(float);
+  w.ml_bytes = units * g * 2 * sizeof(float);
+  return w;
+}
+
+constexpr int kPrefixSplitTokens = 1024;  // prefix tokens per cascade split
+
+int prefix_splits(int prefix_len) {
+  return std::max(1, (prefix_len + kPrefixSplitTokens - 1) / kPrefixSplitTokens);
+}
+
+size_t prefix_ws_bytes(const qsa_dims* d, int prefix_len) {
+  const size_t rows = (size_t)d->num_kv_heads * prefix_splits(prefix_len) * d->num_q_heads /
+                      d->num_kv_heads * d->num_seqs;
+  return align_up(rows * d->head_dim * sizeof(float)) + align_up(rows * 2 * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qsa_version(void) { return 1; }
+
+const char* qsa_status_string(qsa_status s) {
+  switch (s) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_INVALID_ARG: return "invalid argument";
+    case QSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case QSA_ERR_WORKSPACE: return "workspace too small";
+    case QSA_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* qsa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t qsa_budget_pages(int32_t budget_tokens, int32_t page_size) {
+  if (budget_tokens <= 0 || page_size <= 0) return 0;
+  return budget_tokens / page_size;
+}
+
+qsa_status qsa_build_page_meta(const qsa_dims* dims, const qsa_paged_kv* kv, int32_t tail_pages,
+                               void* meta, hipStream_t stream) {
+  qsa_status s = check_dims(dims);
+  if (s != QSA_OK) return s;
+  int max_pages = 0;
+  if ((s = check_kv(dims, kv, false, &max_pages)) != QSA_OK) return s;
+  if (meta == nullptr) return fail(QSA_ERR_INVALID_ARG, "meta is NULL");
+  if (tail_pages < 0) return fail(QSA_ERR_INVALID_ARG, "tail_pages %d < 0", tail_pages);
+  return device_status(qsa::launch_build_meta(common(dims, kv), max_pages, tail_pages, meta, stream),
+                       "build_page_meta launch");
+}
+
+qsa_status qsa_score_pages(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv,
+                           const void* meta, float* group_scores, float* head_scores,
+                           int32_t stride, hipStream_t stream) {
+  qsa_status s = check_dims(dims);
+  if (s != QSA_OK) return s;
+  int max_pages = 0;
+  if ((s = check_kv(dims, kv, false, &max_pages)) != QSA_OK) return s;
+  if (q == nullptr || meta == nullptr || group_scores == nullptr)
+    return fail(QSA_ERR_INVALID_ARG, "q/meta/group_scores is NULL");
+  if (stride < max_pages)
+    return fail(QSA_ERR_INVALID_ARG, "stride %d < longest sequence's page count %d", stride,
+                max_pages);
+  return device_status(
+      qsa::launch_score(common(dims, kv), q, meta, group_scores, head_scores, stride, stream),
+      "score_pages launch");
+}
+
+size_t qsa_topk_workspace_size(const qsa_dims* dims, int32_t max_pages, int32_t k) {
+  (void)dims;
+  (void)max_pages;
+  (void)k;
+  return 0;
+}
+
+qsa_status qsa_topk_pages(const qsa_dims* dims, const qsa_paged_kv* kv, const float* group_scores,
+                          int32_t stride, int32_t k, int32_t* sel, int32_t* sel_count,
+                          int32_t* sel_phys, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  qsa_status s = check_dims(dims);
+  if (s != QSA_OK) return s;
+  int max_pages = 0;
+  if ((s = check_kv(dims, kv, false, &max_pages)) != QSA_OK) return s;
+  if (group_scores == nullptr || sel == nullptr || sel_count == nullptr)
+    return fail(QSA_ERR_INVALID_ARG, "group_scores/sel/sel_count is NULL");
+  if (k < 1) return fail(QSA_ERR_INVALID_ARG, "k = %d (must be >= 1)", k);
+  if (stride < max_pages)
+    return fail(QSA_ERR_INVALID_ARG, "stride %d < longest sequence's page count %d", stride,
+                max_pages);
+  return device_status(
+      qsa::launch_topk(common(dims, kv), group_scores, stride, k, sel, sel_count, sel_phys, stream),
+      "topk_pages launch");
+}
+
+qsa_status qsa_decode_plan(const qsa_dims* dims, const int32_t* seq_lens_host, int32_t k,
+                           int32_t* chunk_pages, int32_t* max_units) {
+  qsa_status s = check_dims(dims);
+  if (s != QSA_OK) return s;
+  if (seq_lens_host == nullptr || chunk_pages == nullptr || max_units == nullptr)
+    return fail(QSA_ERR_INVALID_ARG, "NULL argument");
+  for (int b = 0; b < dims->num_seqs; ++b)
+    if (seq_lens_host[b] < 1) return fail(QSA_ERR_INVALID_ARG, "seq_lens[%d] < 1", b);
+  qsa::DecodePlan p = make_plan(dims, seq_lens_host, k);
+  *chunk_pages = p.chunk;
+  *max_units = p.max_units;
+  return ok();
+}
+
+size_t qsa_decode_workspace_size(const qsa_dims* dims, const int32_t* seq_lens_host, int32_t k) {
+  if (check_dims(dims) != QSA_OK || seq_lens_host == nullptr) return 0;
+  for (int b = 0; b < dims->num_seqs; ++b)
+    if (seq_lens_host[b] < 1) return 0;
+  return decode_ws(dims, make_plan(dims, seq_lens_host, k)).total();
+}
+
+qsa_status qsa_paged_decode(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv,
+                            const int32_t* sel, const int32_t* sel_count, int32_t k, float sm_scale,
+                            float* out, float* lse, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  qsa_status s = check_dims(dims);
+  if (s != QSA_OK) return s;
+  int max_pages = 0;
+  if ((s = check_kv(dims, kv, true, &max_pages)) != QSA_OK) return s;
+  if (q == nullptr || out == nullptr) return fail(QSA_ERR_INVALID_ARG, "q/out is NULL");
+  if (sel != nullptr && (sel_count == nullptr || k < 1))
+    return fail(QSA_ERR_INVALID_ARG, "sel given without sel_count or with k < 1");
+  if (!std::isfinite(sm_scale)) return fail(QSA_ERR_INVALID_ARG, "sm_scale is not finite");
+  const int32_t kk = sel != nullptr ? k : 0;
+  const qsa::DecodePlan plan = make_plan(dims, kv->seq_lens_host, kk);
+  const DecodeWs w = decode_ws(dims, plan);
+  if (ws_bytes < w.total() || (w.total() > 0 && ws == nullptr))
+    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, w.total());
+  qsa::Partials part;
+  part.o = static_cast<float*>(ws);
+  part.ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(w.o_bytes));
+  const qsa::LaunchCommon c = common(dims, kv);
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  hipError_t e = qsa::launch_decode_split(c, q, sel, sel_count, kk, scale_log2, plan, part, stream);
+  if (e != hipSuccess) return device_status(e, "paged_decode split launch");
+  e = qsa::launch_merge(c, sel != nullptr ? sel_count : nullptr, kk, plan, part, qsa::Partials{}, 0,
+                        out, lse, stream);
+  return device_status(e, "paged_decode merge launch");
+}
+
+size_t qsa_cascade_workspace_size(const qsa_dims* dims, int32_t prefix_len,
+                                  const int32_t* suffix_lens_host, int32_t k) {
+  if (check_dims(dims) != QSA_OK || suffix_lens_host == nullptr || prefix_len < 1) return 0;
+  for (int b = 0; b < dims->num_seqs; ++b)
+    if (suffix_lens_host[b] < 1) return 0;
+  return decode_ws(dims, make_plan(dims, suffix_lens_host, k)).total() +
+         prefix_ws_bytes(dims, prefix_len);
+}
+
+qsa_status qsa_cascade_decode(const qsa_dims* dims, const void* q, const int32_t* prefix_pages,
+                              int32_t prefix_len, const qsa_paged_kv* kv, const int32_t* sel,
+                              const int32_t* sel_count, int32_t k, float sm_scale, float* out,
+                              float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  qsa_status s = check_dims(dims);
+  if (s != QSA_OK) return s;
+  if (dims->dtype != QSA_BF16)
+    return fail(QSA_ERR_UNSUPPORTED, "cascade decode is built for bf16 / head_dim 128 only");
+  int max_pages = 0;
+  if ((s = check_kv(dims, kv, true, &max_pages)) != QSA_OK) return s;
+  if (q == nullptr || out == nullptr || prefix_pages == nullptr)
+    return fail(QSA_ERR_INVALID_ARG, "q/out/prefix_pages is NULL");
+  if (prefix_len < 1) return fail(QSA_ERR_INVALID_ARG, "prefix_len %d < 1", prefix_len);
+  if (sel != nullptr && (sel_count == nullptr || k < 1))
+    return fail(QSA_ERR_INVALID_ARG, "sel given without sel_count or with k < 1");
+  if (!std::isfinite(sm_scale)) return fail(QSA_ERR_INVALID_ARG, "sm_scale is not finite");
+  const int32_t kk = sel != nullptr ? k : 0;
+  const qsa::DecodePlan plan = make_plan(dims, kv->seq_lens_host, kk);
+  const DecodeWs w = decode_ws(dims, plan);
+  const size_t need = w.total() + prefix_ws_bytes(dims, prefix_len);
+  if (ws_bytes < need || ws == nullptr)
+    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  char* base = static_cast<char*>(ws);
+  qsa::Partials part;
+  part.o = reinterpret_cast<float*>(base);
+  part.ml = reinterpret_cast<float*>(base + align_up(w.o_bytes));
+  const int nsplit = prefix_splits(prefix_len);
+  const size_t rows = (size_t)dims->num_kv_heads * nsplit * (dims->num_q_heads / dims->num_kv_heads) *
+                      dims->num_seqs;
+  qsa::Partials pre;
+  pre.o = reinterpret_cast<float*>(base + w.total());
+  pre.ml = reinterpret_cast<float*>(base + w.total() + align_up(rows * dims->head_dim * sizeof(float)));
+  const qsa::LaunchCommon c = common(dims, kv);
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  hipError_t e = qsa::launch_cascade_prefix(c, q, prefix_pages, prefix_len, nsplit, scale_log2, pre,
+                                            stream);
+  if (e != hipSuccess) return device_status(e, "cascade prefix launch");
+  e = qsa::launch_decode_split(c, q, sel, sel_count, kk, scale_log2, plan, part, stream);
+  if (e != hipSuccess) return device_status(e, "cascade suffix launch");
+  e = qsa::launch_merge(c, sel != nullptr ? sel_count : nullptr, kk, plan, part, pre, nsplit, out,
+                        lse, stream);
+  return device_status(e, "cascade merge launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+// Device-side helpers shared by the libqsa kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+constexpr int kPage = 16;        // tokens per KV page
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kRowBytes = 256;   // one key/value/query row: D * sizeof(element)
+constexpr int kTileBytes = 4096; // one (page, KV head) tile: 16 rows x 256 B
+
+// Element storage types. bf16 is kept as raw 16-bit patterns; arithmetic
+// widens to fp32 (exact) or uses the bf16 dot instructions.
+struct bf16s {
+  uint16_t bits;
+};
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<bf16s> {
+  static constexpr int kPerChunk = 8;  // elements per 16-byte chunk
+};
+template <>
+struct Elem<float> {
+  static constexpr int kPerChunk = 4;
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, uint4 v) {
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+// bf16 pair packed in a dword -> fp32 (exact).
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
+// acc + a.lo*b.lo + a.hi*b.hi on bf16 pairs, fp32 accumulate (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Dot product of one 16-byte chunk of q with one 16-byte chunk of k.
+__device__ __forceinline__ float chunk_dot(const uint4& q, const uint4& k, float acc, bf16s) {
+  acc = dot2_bf16(q.x, k.x, acc);
+  acc = dot2_bf16(q.y, k.y, acc);
+  acc = dot2_bf16(q.z, k.z, acc);
+  acc = dot2_bf16(q.w, k.w, acc);
+  return acc;
+}
+__device__ __forceinline__ float chunk_dot(const uint4& q, const uint4& k, float acc, float) {
+  acc = __builtin_fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+  acc = __builtin_fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+  acc = __builtin_fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+  acc = __builtin_fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+  return acc;
+}
+
+// Unpack one 16-byte chunk to fp32.
+__device__ __forceinline__ void chunk_unpack(const uint4& c, float* f, bf16s) {
+  f[0] = bf_lo(c.x); f[1] = bf_hi(c.x);
+  f[2] = bf_lo(c.y); f[3] = bf_hi(c.y);
+  f[4] = bf_lo(c.z); f[5] = bf_hi(c.z);
+  f[6] = bf_lo(c.w); f[7] = bf_hi(c.w);
+}
+__device__ __forceinline__ void chunk_unpack(const uint4& c, float* f, float) {
+  f[0] = __uint_as_float(c.x); f[1] = __uint_as_float(c.y);
+  f[2] = __uint_as_float(c.z); f[3] = __uint_as_float(c.w);
+}
+
+// Sign split of a query chunk: neg keeps the negative-signed elements (others
+// +0), pos the rest. q.neg . m + q.pos . M equals sum_i q_i (q_i > 0 ? M_i : m_i)
+// (a zero q_i contributes zero either way).
+__device__ __forceinline__ void chunk_sign_split(const uint4& q, uint4& neg, uint4& pos, bf16s) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&q);
+  uint32_t* n = reinterpret_cast<uint32_t*>(&neg);
+  uint32_t* p = reinterpret_cast<uint32_t*>(&pos);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // per 16-bit half: all-ones mask where the sign bit is set
+    uint32_t s = (w[e] >> 15) & 0x00010001u;
+    uint32_t mask = s * 0xFFFFu;
+    n[e] = w[e] & mask;
+    p[e] = w[e] & ~mask;
+  }
+}
+__device__ __forceinline__ void chunk_sign_split(const uint4& q, uint4& neg, uint4& pos, float) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&q);
+  uint32_t* n = reinterpret_cast<uint32_t*>(&neg);
+  uint32_t* p = reinterpret_cast<uint32_t*>(&pos);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t mask = (uint32_t)((int32_t)w[e] >> 31);
+    n[e] = w[e] & mask;
+    p[e] = w[e] & ~mask;
+  }
+}
+
+// ---- order-preserving integer keys (IEEE total order, -0 < +0) ----------
+// bf16 pair: per 16-bit half, flip all bits of negatives, the sign of others.
+__device__ __forceinline__ uint32_t bf2_to_key(uint32_t x) {
+  uint32_t s = (x >> 15) & 0x00010001u;
+  return x ^ (s * 0x7FFFu | 0x80008000u);
+}
+__device__ __forceinline__ uint32_t key_to_bf2(uint32_t k) {
+  uint32_t s = ((~k) >> 15) & 0x00010001u;  // 1 where the value was negative
+  return k ^ (s * 0x7FFFu | 0x80008000u);
+}
+__device__ __forceinline__ uint32_t f32_to_key(uint32_t x) {
+  return x ^ ((uint32_t)((int32_t)x >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t key_to_f32(uint32_t k) {
+  return k ^ ((uint32_t)((int32_t)(~k) >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t umin2x16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, a),
+                                                                 __builtin_bit_cast(u16x2_t, b)));
+}
+__device__ __forceinline__ uint32_t umax2x16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                 __builtin_bit_cast(u16x2_t, b)));
+}
+
+// Score -> ascending uint32 key; -0 is folded onto +0 so equal values tie.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = (s == 0.0f) ? 0u : __float_as_uint(s);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+// ---- DPP lane exchange (wave64, gfx9 DPP controls) ----------------------
+enum : int {
+  kDppQuadXor1 = 0xB1,       // quad_perm [1,0,3,2]
+  kDppQuadXor2 = 0x4E,       // quad_perm [2,3,0,1]
+  kDppRowHalfMirror = 0x141, // lane i <-> 7-i within each 8-lane half row
+  kDppRowMirror = 0x140,     // lane i <-> 15-i within each 16-lane row
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of 8 lanes; every lane of the group gets the total.
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_mov<kDppQuadXor1>(v);
+  v += dpp_mov<kDppQuadXor2>(v);
+  v += dpp_mov<kDppRowHalfMirror>(v);
+  return v;
+}
+// Sum over aligned groups of 16 lanes (one DPP row); every lane gets it.
+__device__ __forceinline__ float sum16(float v) {
+  v = sum8(v);
+  v += dpp_mov<kDppRowMirror>(v);
+  return v;
+}
+
+// Cross-lane xor exchange through the LDS crossbar (no LDS allocation).
+__device__ __forceinline__ float xshfl(float v, int mask) {
+  int lane = __lane_id();
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ uint32_t xshfl_u(uint32_t v, int mask) {
+  int lane = __lane_id();
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, (int)v);
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Orders this wave's LDS accesses before and after the call point (all lanes
+// of one wave; no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace qsa

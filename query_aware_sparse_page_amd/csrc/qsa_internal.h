@@ -1,0 +1,62 @@
+// Internal (host-side) interface between the C ABI layer and the kernel
+// translation units of libqsa. Not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+// Shapes and table pointers every launcher needs, validated by the ABI layer.
+struct LaunchCommon {
+  int B = 0, Hq = 0, Hkv = 0, D = 0, G = 0;
+  bool bf16 = true;
+  const void* k_pool = nullptr;
+  const void* v_pool = nullptr;
+  int num_phys = 0;
+  const int* page_indptr = nullptr;
+  const int* page_indices = nullptr;
+  const int* seq_lens = nullptr;
+};
+
+// Split-K decode work split: `chunk` pages per work unit (a multiple of 4,
+// one quarter per wave), `max_units` units for the longest (b, h) row.
+struct DecodePlan {
+  int chunk = 4;
+  int max_units = 0;
+};
+
+// Per-unit partial results: part_o [units, G, D] (unnormalised, relative to
+// the unit's running max), part_ml [units, G, 2] = (max in log2 units, sum).
+struct Partials {
+  float* o = nullptr;
+  float* ml = nullptr;
+};
+
+hipError_t launch_build_meta(const LaunchCommon& c, int max_pages, int tail_pages, void* meta,
+                             hipStream_t stream);
+
+hipError_t launch_score(const LaunchCommon& c, const void* q, const void* meta, float* group_scores,
+                        float* head_scores, int stride, hipStream_t stream);
+
+hipError_t launch_topk(const LaunchCommon& c, const float* group_scores, int stride, int k,
+                       int* sel, int* sel_count, int* sel_phys, hipStream_t stream);
+
+hipError_t launch_decode_split(const LaunchCommon& c, const void* q, const int* sel,
+                               const int* sel_count, int k, float scale_log2,
+                               const DecodePlan& plan, Partials part, hipStream_t stream);
+
+// Merge the decode partials of every (b, hq) (and, if prefix != nullptr, the
+// per-query prefix partials: n_prefix_splits of them per query row
+// r = b*G + (hq % G) of KV head h, laid out [Hkv][n_prefix_splits][B*G]).
+hipError_t launch_merge(const LaunchCommon& c, const int* sel_count, int k, const DecodePlan& plan,
+                        Partials part, Partials prefix, int n_prefix_splits, float* out,
+                        float* lse, hipStream_t stream);
+
+// Cascade prefix on the matrix cores (bf16, D = 128): partials per
+// (KV head, split, query row).
+hipError_t launch_cascade_prefix(const LaunchCommon& c, const void* q, const int* prefix_pages,
+                                 int prefix_len, int n_splits, float scale_log2, Partials prefix,
+                                 hipStream_t stream);
+
+}  // namespace qsa

@@ -1,0 +1,126 @@
+// Step 2: upper-bound page score (TinyServe page, §2.2) and the group max.
+//
+// score_j = sum_i q_i * (q_i > 0 ? M_j[i] : m_j[i]) is evaluated as
+// q_neg . m_j + q_pos . M_j with q split by sign (q_neg keeps the negative
+// elements, q_pos the others), which turns it into one dot product of length
+// 2D between the split query and the page's 512-byte [m | M] metadata row.
+// bf16 products are exact in fp32; they accumulate with v_dot2_f32_bf16.
+//
+// Layout: 16 lanes (one DPP row) per page; lane c of the row holds chunk c
+// of m and chunk c of M (16 bytes each), so each load instruction reads two
+// full 256-byte rows per page. A wave covers 4 pages per step, a workgroup
+// (4 waves) 64 pages of one (sequence, KV head). Lane partials are summed
+// over the row with DPP; the group max over the g query heads is in-lane.
+#include "qsa_device.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kScorePagesPerBlock = 64;
+
+template <typename T, int G>
+__global__ void __launch_bounds__(256) score_kernel(
+    const T* __restrict__ q, const T* __restrict__ meta, int num_phys, int Hkv,
+    const int* __restrict__ page_indptr, const int* __restrict__ page_indices,
+    const int* __restrict__ seq_lens, float* __restrict__ group_scores,
+    float* __restrict__ head_scores, int stride) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int c = lane & 15;      // chunk within a metadata row
+  const int slot = lane >> 4;   // which of the wave's 4 pages
+  const int L = seq_lens[b];
+  const int n = L > 0 ? (L + kPage - 1) / kPage : 0;
+  const int base_j = blockIdx.x * kScorePagesPerBlock;
+  if (base_j >= stride) return;
+  const int* table = page_indices + page_indptr[b];
+
+  // Query chunks of the group's heads, split by sign.
+  uint4 qn[G], qp[G];
+  const int Hq = Hkv * G;
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const char* qrow = reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G + hh) * kRowBytes;
+    uint4 qc = ld16(qrow + c * 16);
+    chunk_sign_split(qc, qn[hh], qp[hh], T{});
+  }
+
+  constexpr int kSteps = kScorePagesPerBlock / 16;
+  uint4 mrow[kSteps], Mrow[kSteps];
+  int jj[kSteps];
+  bool ok[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    jj[s] = base_j + s * 16 + wave * 4 + slot;
+    ok[s] = false;
+    if (jj[s] < n) {
+      int p = table[jj[s]];
+      if (p >= 0 && p < num_phys) {
+        const char* tile = reinterpret_cast<const char*>(meta) + ((size_t)p * Hkv + h) * 512;
+        mrow[s] = ld16(tile + c * 16);
+        Mrow[s] = ld16(tile + 256 + c * 16);
+        ok[s] = true;
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int j = jj[s];
+    if (j >= stride) continue;
+    float hs[G];
+    float gmax = -__builtin_inff();
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float acc = 0.0f;
+      if (ok[s]) {
+        acc = chunk_dot(qn[hh], mrow[s], acc, T{});
+        acc = chunk_dot(qp[hh], Mrow[s], acc, T{});
+      }
+      acc = sum16(acc);
+      hs[hh] = ok[s] ? acc : -__builtin_inff();
+      gmax = fmaxf(gmax, hs[hh]);
+    }
+    if (c == 0) group_scores[((size_t)b * Hkv + h) * stride + j] = gmax;
+    if (head_scores != nullptr && c < G) {
+      float v = hs[0];
+#pragma unroll
+      for (int hh = 1; hh < G; ++hh) v = (c == hh) ? hs[hh] : v;
+      head_scores[((size_t)b * Hq + h * G + c) * stride + j] = v;
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_score_t(const LaunchCommon& c, const void* q, const void* meta, float* gs,
+                          float* hs, int stride, hipStream_t stream) {
+  dim3 grid((stride + kScorePagesPerBlock - 1) / kScorePagesPerBlock, c.Hkv, c.B);
+  const T* qq = static_cast<const T*>(q);
+  const T* mm = static_cast<const T*>(meta);
+#define QSA_SCORE_CASE(GG)                                                                       \
+  case GG:                                                                                       \
+    hipLaunchKernelGGL((score_kernel<T, GG>), grid, dim3(256), 0, stream, qq, mm, c.num_phys, \
+                       c.Hkv, c.page_indptr, c.page_indices, c.seq_lens, gs, hs, stride);        \
+    break;
+  switch (c.G) {
+    QSA_SCORE_CASE(1)
+    QSA_SCORE_CASE(2)
+    QSA_SCORE_CASE(4)
+    QSA_SCORE_CASE(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef QSA_SCORE_CASE
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score(const LaunchCommon& c, const void* q, const void* meta, float* group_scores,
+                        float* head_scores, int stride, hipStream_t stream) {
+  return c.bf16 ? launch_score_t<bf16s>(c, q, meta, group_scores, head_scores, stride, stream)
+                : launch_score_t<float>(c, q, meta, group_scores, head_scores, stride, stream);
+}
+
+}  // namespace qsa

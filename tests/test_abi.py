@@ -1,0 +1,104 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/qsa.h declares, and its host-side logic (validation, workspace sizes,
+work planning, status strings) behaves as documented. No call here launches
+a kernel: each either returns before touching the device or is host-only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from query_aware_sparse_page_amd import qsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "qsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return qsa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 13, names
+    for n in ["qsa_build_page_meta", "qsa_score_pages", "qsa_topk_pages", "qsa_paged_decode",
+              "qsa_cascade_decode"]:
+        assert n in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    assert L.qsa_version() >= 1
+    assert L.qsa_status_string(0) == b"ok"
+    assert L.qsa_status_string(3) == b"workspace too small"
+
+
+def test_budget_pages(L):
+    assert L.qsa_budget_pages(2048, 16) == 128       # the long-context budget
+    assert L.qsa_budget_pages(2047, 16) == 127
+    assert L.qsa_budget_pages(0, 16) == 0
+
+
+def _dims(B=4, Hq=32, Hkv=8, D=128, ps=16, dt=qsa.QSA_BF16):
+    return qsa.Dims(B, Hq, Hkv, D, ps, dt)
+
+
+def _lens(v):
+    return (ctypes.c_int32 * len(v))(*v)
+
+
+def test_validation_errors_return_before_any_device_work(L):
+    d = _dims()
+    st = L.qsa_paged_decode(None, None, None, None, None, 0, ctypes.c_float(1.0), None, None, None, 0, None)
+    assert st == qsa.QSA_ERR_INVALID_ARG and b"dims" in L.qsa_last_error()
+    bad = _dims(Hq=30)
+    st = L.qsa_score_pages(ctypes.byref(bad), None, None, None, None, None, 1, None)
+    assert st == qsa.QSA_ERR_INVALID_ARG and b"multiple" in L.qsa_last_error()
+    st = L.qsa_score_pages(ctypes.byref(_dims(D=96)), None, None, None, None, None, 1, None)
+    assert st == qsa.QSA_ERR_UNSUPPORTED
+    st = L.qsa_score_pages(ctypes.byref(_dims(ps=32)), None, None, None, None, None, 1, None)
+    assert st == qsa.QSA_ERR_UNSUPPORTED
+    st = L.qsa_score_pages(ctypes.byref(_dims(Hq=48, Hkv=4)), None, None, None, None, None, 1, None)
+    assert st == qsa.QSA_ERR_UNSUPPORTED                  # group size 12
+    st = L.qsa_topk_pages(ctypes.byref(d), None, None, 1, 1, None, None, None, None, 0, None)
+    assert st == qsa.QSA_ERR_INVALID_ARG
+    # a zero-length sequence is rejected from the host copy of seq_lens
+    lens = _lens([16, 0, 5, 5])
+    kv = qsa.PagedKVStruct(1, 1, 10, 1, 1, 1, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)))
+    st = L.qsa_build_page_meta(ctypes.byref(d), ctypes.byref(kv), 0, 1, None)
+    assert st == qsa.QSA_ERR_INVALID_ARG and b"seq_lens[1]" in L.qsa_last_error()
+    st = L.qsa_build_page_meta(ctypes.byref(d), ctypes.byref(kv), -1, 1, None)
+    assert st == qsa.QSA_ERR_INVALID_ARG
+    # cascade is bf16 / 128 only
+    st = L.qsa_cascade_decode(ctypes.byref(_dims(D=64, dt=qsa.QSA_F32)), None, None, 1, None, None, None, 0,
+                              ctypes.c_float(1.0), None, None, None, 0, None)
+    assert st == qsa.QSA_ERR_UNSUPPORTED
+
+
+def test_decode_plan_and_workspace(L):
+    d = _dims(B=16)
+    lens = _lens([8192] * 16)
+    c, m = ctypes.c_int32(), ctypes.c_int32()
+    assert L.qsa_decode_plan(ctypes.byref(d), lens, 153, ctypes.byref(c), ctypes.byref(m)) == 0
+    assert c.value % 4 == 0 and 4 <= c.value <= 256
+    assert m.value == -(-153 // c.value)
+    ws = L.qsa_decode_workspace_size(ctypes.byref(d), lens, 153)
+    units = 16 * 8 * m.value
+    assert ws >= units * 4 * 128 * 4 + units * 4 * 2 * 4
+    # dense: every page counts
+    assert L.qsa_decode_plan(ctypes.byref(d), lens, 0, ctypes.byref(c), ctypes.byref(m)) == 0
+    assert m.value == -(-512 // c.value)
+    assert L.qsa_decode_workspace_size(ctypes.byref(_dims(Hq=30)), lens, 0) == 0
+    cw = L.qsa_cascade_workspace_size(ctypes.byref(d), 4096, lens, 0)
+    assert cw > L.qsa_decode_workspace_size(ctypes.byref(d), lens, 0)
+
+
+def test_topk_workspace_query(L):
+    assert L.qsa_topk_workspace_size(ctypes.byref(_dims()), 8192, 128) >= 0

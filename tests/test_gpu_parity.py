@@ -1,0 +1,250 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on small
+seeded cases that span several tiles, ragged tails and the edge cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import qsa_oracle as O
+from query_aware_sparse_page_amd import qsa
+from tests._util import case_np, np_store
+from tests.gpu_helpers import (assert_close_out, check_selection_row, score_tol)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _case(name, lens, Hq, Hkv, dtype="bf16", seed=11, n_sentinel=5, **kw):
+    D = 128 if dtype == "bf16" else 64
+    c = workloads.build_case(name, len(lens), Hq, Hkv, D, list(lens), dtype, seed, n_sentinel=n_sentinel, **kw)
+    return c
+
+
+SMALL = [
+    # (label, lens, Hq, Hkv, dtype, k)
+    ("ragged_g4", [1000, 1537, 700, 16, 17, 1], 8, 2, "bf16", 30),
+    ("g8", [2100, 333, 4096], 16, 2, "bf16", 41),
+    ("g2", [517, 1024], 4, 2, "bf16", 9),
+    ("g1_f32", [1024, 77], 2, 2, "f32", 8),
+    ("g4_f32", [300, 1600], 4, 1, "f32", 20),
+    ("k1", [640, 129], 8, 2, "bf16", 1),
+    ("k_over_n", [200, 90], 8, 2, "bf16", 50),
+]
+
+
+def _kv(case):
+    print(f"[case] {case.name} B={case.B} Hq={case.Hq} Hkv={case.Hkv} dtype={case.dtype} "
+          f"lens={case.seq_lens_list()}", flush=True)
+    g = case.to(DEV)
+    return g, qsa.PagedKV.from_case(g)
+
+
+@pytest.mark.parametrize("label,lens,Hq,Hkv,dtype,k", SMALL)
+def test_meta_bit_exact(label, lens, Hq, Hkv, dtype, k):
+    c = _case(label, lens, Hq, Hkv, dtype)
+    d = case_np(c)
+    g, kv = _kv(c)
+    meta = qsa.build_page_meta(kv)
+    torch.cuda.synchronize()
+    ref = O.build_page_meta(d["k_pool"], dtype, d["page_indptr"], d["page_indices"], d["seq_lens"])
+    got = np_store(meta)
+    for b, L in enumerate(d["seq_lens"]):
+        for j in range(O.num_pages(L)):
+            p = O.physical_page(d["page_indptr"], d["page_indices"], b, j)
+            assert np.array_equal(got[p].view(np.uint8), ref[p].view(np.uint8)), (b, j, p)
+
+
+def test_meta_tail_update_and_signed_zero():
+    c = _case("tail", [33, 48, 5], 4, 2)
+    # plant signed zeros in the first page of sequence 0 (dims 0..3)
+    p0 = int(c.page_indices[0])
+    c.k_pool[p0, :, :, 0] = 0.0
+    c.k_pool[p0, :, 5, 0] = -0.0
+    c.k_pool[p0, :, :, 1] = -0.0
+    d = case_np(c)
+    g, kv = _kv(c)
+    full = qsa.build_page_meta(kv)
+    junk = torch.full_like(full, 7.0)
+    tail = qsa.build_page_meta(kv, meta=junk.clone(), tail_pages=1)
+    torch.cuda.synchronize()
+    ref = O.build_page_meta(d["k_pool"], "bf16", d["page_indptr"], d["page_indices"], d["seq_lens"])
+    fb, tb = np_store(full), np_store(tail)
+    assert int(fb[p0, 0, 0, 0]) == 0x8000 and int(fb[p0, 0, 1, 0]) == 0x0000
+    assert int(fb[p0, 0, 0, 1]) == 0x8000 and int(fb[p0, 0, 1, 1]) == 0x8000
+    last = {int(d["page_indices"][d["page_indptr"][b + 1] - 1]) for b in range(3)}
+    jb = np_store(junk)
+    for b, L in enumerate(d["seq_lens"]):
+        for j in range(O.num_pages(L)):
+            p = O.physical_page(d["page_indptr"], d["page_indices"], b, j)
+            assert np.array_equal(fb[p], ref[p])
+            if p in last:
+                assert np.array_equal(tb[p], ref[p])
+            else:
+                assert np.array_equal(tb[p], jb[p])
+
+
+def _oracle_scores(c, d, stride):
+    meta = O.build_page_meta(d["k_pool"], c.dtype, d["page_indptr"], d["page_indices"], d["seq_lens"])
+    head, group = O.score_pages(d["q"], c.dtype, meta, c.dtype, d["page_indptr"], d["page_indices"],
+                                d["seq_lens"], c.Hkv, stride=stride)
+    return meta, head, group
+
+
+@pytest.mark.parametrize("label,lens,Hq,Hkv,dtype,k", SMALL)
+def test_scores_and_selection(label, lens, Hq, Hkv, dtype, k):
+    c = _case(label, lens, Hq, Hkv, dtype, plant_pages=3)
+    d = case_np(c)
+    g, kv = _kv(c)
+    stride = kv.max_pages() + 3
+    meta = qsa.build_page_meta(kv)
+    gs, hs = qsa.score_pages(g.q, kv, meta, stride=stride, head_scores=True)
+    sel, cnt, phys = qsa.topk_pages(gs, kv, k, num_q_heads=Hq)
+    torch.cuda.synchronize()
+    ometa, ohead, ogroup = _oracle_scores(c, d, stride)
+    qv = O.values_f64(d["q"], dtype)
+    mv = O.values_f64(ometa, dtype)
+    hs_n, gs_n = hs.cpu().numpy(), gs.cpu().numpy()
+    G = Hq // Hkv
+    for b, L in enumerate(d["seq_lens"]):
+        n = O.num_pages(L)
+        assert np.all(np.isneginf(gs_n[b, :, n:])) and np.all(np.isneginf(hs_n[b, :, n:]))
+        for j in range(n):
+            p = O.physical_page(d["page_indptr"], d["page_indices"], b, j)
+            for hq in range(Hq):
+                h = hq // G
+                tol = score_tol(qv[b, hq], mv[p, h, 0], mv[p, h, 1])
+                assert abs(float(hs_n[b, hq, j]) - float(ohead[b, hq, j])) <= tol, (b, hq, j)
+            for h in range(Hkv):
+                assert gs_n[b, h, j] == hs_n[b, h * G:(h + 1) * G, j].max()
+    sel_n, cnt_n, phys_n = sel.cpu().numpy(), cnt.cpu().numpy(), phys.cpu().numpy()
+    for b, L in enumerate(d["seq_lens"]):
+        n = O.num_pages(L)
+        table = d["page_indices"][d["page_indptr"][b]:d["page_indptr"][b + 1]]
+        for h in range(Hkv):
+            check_selection_row(sel_n[b, h], cnt_n[b, h], phys_n[b, h], ogroup[b, h], n, k, table)
+
+
+@pytest.mark.parametrize("label,lens,Hq,Hkv,dtype,k", SMALL)
+def test_topk_exact_on_oracle_scores(label, lens, Hq, Hkv, dtype, k):
+    # Same fp32 scores in -> identical selection out (integer work: bit-exact).
+    c = _case(label, lens, Hq, Hkv, dtype)
+    d = case_np(c)
+    stride = max(O.num_pages(L) for L in d["seq_lens"])
+    _, _, ogroup = _oracle_scores(c, d, stride)
+    # plant exact ties (including -0 vs +0) in the oracle's scores
+    ogroup = ogroup.copy()
+    ogroup[:, :, 1::5] = ogroup[:, :, 0:1]
+    ogroup[0, 0, 2] = -0.0
+    ogroup[0, 0, 3] = 0.0
+    g, kv = _kv(c)
+    gs = torch.from_numpy(ogroup).to(DEV)
+    sel, cnt, phys = qsa.topk_pages(gs, kv, k, num_q_heads=Hq)
+    osel, ocnt = O.topk_pages(ogroup, d["seq_lens"], k)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), osel)
+    assert np.array_equal(cnt.cpu().numpy(), ocnt)
+
+
+@pytest.mark.parametrize("label,lens,Hq,Hkv,dtype,k", SMALL)
+def test_decode_dense_and_sparse(label, lens, Hq, Hkv, dtype, k):
+    c = _case(label, lens, Hq, Hkv, dtype)
+    d = case_np(c)
+    g, kv = _kv(c)
+    out, lse = qsa.paged_decode(g.q, kv, sm_scale=c.sm_scale)
+    torch.cuda.synchronize()
+    oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], dtype, d["page_indptr"], d["page_indices"],
+                            d["seq_lens"], c.sm_scale)
+    assert_close_out(out.cpu().numpy(), lse.cpu().numpy(), oo, ol)
+    # sparse, on the oracle's own selection (an oracle output fed to the GPU)
+    stride = max(O.num_pages(L) for L in d["seq_lens"])
+    _, _, ogroup = _oracle_scores(c, d, stride)
+    osel, ocnt = O.topk_pages(ogroup, d["seq_lens"], k)
+    out2, lse2 = qsa.paged_decode(g.q, kv, sel=torch.from_numpy(osel).to(DEV),
+                                  sel_count=torch.from_numpy(ocnt).to(DEV), sm_scale=c.sm_scale)
+    torch.cuda.synchronize()
+    so, sl = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], dtype, d["page_indptr"], d["page_indices"],
+                            d["seq_lens"], c.sm_scale, sel=osel, sel_count=ocnt)
+    assert_close_out(out2.cpu().numpy(), lse2.cpu().numpy(), so, sl)
+
+
+@pytest.mark.parametrize("label,lens,Hq,Hkv,dtype,k", SMALL[:4])
+def test_all_pages_selected_is_bitwise_dense(label, lens, Hq, Hkv, dtype, k):
+    c = _case(label, lens, Hq, Hkv, dtype)
+    g, kv = _kv(c)
+    ns = [-(-L // 16) for L in lens]
+    K = max(ns)
+    sel = torch.full((c.B, Hkv, K), -1, dtype=torch.int32)
+    for b, n in enumerate(ns):
+        sel[b, :, :n] = torch.arange(n, dtype=torch.int32)
+    cnt = torch.tensor([[n] * Hkv for n in ns], dtype=torch.int32)
+    dense = qsa.paged_decode(g.q, kv, sm_scale=c.sm_scale)
+    sparse = qsa.paged_decode(g.q, kv, sel=sel.to(DEV), sel_count=cnt.to(DEV), sm_scale=c.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dense[0], sparse[0]) and torch.equal(dense[1], sparse[1])
+    # and the GPU's own top-K with K >= n_b takes every page
+    meta = qsa.build_page_meta(kv)
+    gs, _ = qsa.score_pages(g.q, kv, meta)
+    s2, c2, _ = qsa.topk_pages(gs, kv, K, num_q_heads=Hq)
+    via = qsa.paged_decode(g.q, kv, sel=s2, sel_count=c2, sm_scale=c.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dense[0], via[0])
+
+
+def test_end_to_end_pipeline_tiny_config():
+    c = workloads.c1_tiny()
+    d = case_np(c)
+    g, kv = _kv(c)
+    meta = qsa.build_page_meta(kv)
+    gs, _ = qsa.score_pages(g.q, kv, meta)
+    sel, cnt, phys = qsa.topk_pages(gs, kv, c.k_pages, num_q_heads=c.Hq)
+    out, lse = qsa.paged_decode(g.q, kv, sel=sel, sel_count=cnt, sm_scale=c.sm_scale)
+    torch.cuda.synchronize()
+    _, _, ogroup = _oracle_scores(c, d, 64)
+    osel, ocnt = O.topk_pages(ogroup, d["seq_lens"], c.k_pages)
+    assert np.array_equal(sel.cpu().numpy(), osel)            # planted gap: exact
+    assert set(int(x) for x in c.planted[0]) <= set(int(x) for x in sel.cpu().numpy()[0, 0])
+    oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], "f32", d["page_indptr"], d["page_indices"],
+                            d["seq_lens"], c.sm_scale, sel=osel, sel_count=ocnt)
+    assert_close_out(out.cpu().numpy(), lse.cpu().numpy(), oo, ol)
+
+
+@pytest.mark.parametrize("prefix_len,suffix_len,B,Hq,Hkv,k", [
+    (256, 48, 5, 8, 2, None), (100, 70, 3, 16, 2, None), (1024 + 64, 160, 33, 8, 2, None),
+    (512, 200, 9, 8, 2, 4), (2048, 512, 20, 32, 8, 9),
+])
+def test_cascade(prefix_len, suffix_len, B, Hq, Hkv, k):
+    c = workloads.cascade_case("cas", B, Hq, Hkv, 128, prefix_len, suffix_len, "bf16", 21, n_sentinel=3)
+    d = case_np(c)
+    g, kv = _kv(c)
+    osel = ocnt = None
+    sel_t = cnt_t = None
+    if k is not None:
+        stride = O.num_pages(suffix_len)
+        _, _, ogroup = _oracle_scores(c, d, stride)
+        osel, ocnt = O.topk_pages(ogroup, d["seq_lens"], k)
+        sel_t, cnt_t = torch.from_numpy(osel).to(DEV), torch.from_numpy(ocnt).to(DEV)
+    out, lse = qsa.cascade_decode(g.q, g.prefix_pages, prefix_len, kv, sel=sel_t, sel_count=cnt_t,
+                                  sm_scale=c.sm_scale)
+    torch.cuda.synchronize()
+    oo, ol = O.cascade_decode(d["q"], d["k_pool"], d["v_pool"], "bf16", d["prefix_pages"], prefix_len,
+                              d["page_indptr"], d["page_indices"], d["seq_lens"], c.sm_scale,
+                              sel=osel, sel_count=ocnt)
+    assert_close_out(out.cpu().numpy(), lse.cpu().numpy(), oo, ol)
+
+
+def test_error_paths_raise():
+    c = _case("err", [64, 40], 8, 2)
+    g, kv = _kv(c)
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.score_pages(g.q, kv, qsa.build_page_meta(kv), stride=1)
+    assert e.value.status == qsa.QSA_ERR_INVALID_ARG
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.paged_decode(g.q, kv, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert e.value.status == qsa.QSA_ERR_WORKSPACE
+    q6 = torch.zeros(2, 6, 128, dtype=torch.bfloat16, device=DEV)   # 6 % 2 == 0 but g = 3
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.paged_decode(q6, kv)
+    assert e.value.status == qsa.QSA_ERR_UNSUPPORTED

@@ -51,7 +51,7 @@ class PagedCase:
     # shared-prefix cascade extras
     prefix_pages: Optional[torch.Tensor] = None   # int32 [n_prefix_pages]
     prefix_len: int = 0
-    planted: Optional[torch.Tensor] = None        # int64 [B, n_planted] logical pages
+    planted: Optional[list] = None                # per sequence: int64 logical pages planted
     seed: int = 0
 
     @property
@@ -154,13 +154,13 @@ def build_case(
         dirn = torch.sign(qf)
         rows = []
         for b in range(B):
-            sel = torch.randperm(nps[b], generator=g, device=device)[:plant_pages]
+            sel = torch.randperm(nps[b], generator=g, device=device)[:min(plant_pages, nps[b])]
             rows.append(torch.sort(sel).values)
             phys = page_indices[indptr[b].item() + sel.to(torch.int64)].to(torch.int64)
             kk = k_pool[phys].to(torch.float32)                              # [n,Hkv,16,D]
             kk = kk + plant_scale * dirn[b].view(1, Hkv, 1, D)
             k_pool[phys] = _cast(kk, dtype)
-        planted = torch.stack(rows).cpu()
+        planted = [r.cpu() for r in rows]
 
     if drift is not None:
         rho, sigma = drift
