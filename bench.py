@@ -112,7 +112,7 @@ def main():
         qsa.build_page_meta(kvs[r], meta=metas[r], tail_pages=1)
 
     def stage_score(r):
-        qsa.score_pages(case.q, kvs[r], metas[r], stride=stride, out=gs)
+        qsa.score_pages(case.q, kvs[r], metas[r], out=gs)
 
     def stage_topk(r):
         qsa.topk_pages(gs, kvs[r], k, num_q_heads=Hq, with_phys=False, out=(sel, cnt, None))

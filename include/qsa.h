@@ -81,16 +81,18 @@ typedef struct qsa_paged_kv {
 } qsa_paged_kv;
 
 /* Step 1 - per-page bounding-box metadata (TinyServe §2.1; refreshed every
- * decode step per §5.3). For each sequence b, logical page j and KV head h,
- * with p = the physical slot: meta[p][h][0][i] = min and meta[p][h][1][i] =
- * max over the page's valid tokens of K[p][h][t][i], under IEEE total order
- * (-0 < +0), so the values are exact copies of key elements (bit-exact).
- * meta: [num_phys_pages, Hkv, 2, D] in dims->dtype; only slots reachable
- * through the table are written. tail_pages = 0 rebuilds every page;
+ * decode step per §5.3). For each sequence b, logical page j < n_b and KV
+ * head h, read through the page table: meta[b][h][j][0][i] = min and
+ * meta[b][h][j][1][i] = max over the page's valid tokens of K[p][h][t][i]
+ * (p the physical slot), under IEEE total order (-0 < +0), so the values are
+ * exact copies of key elements (bit-exact). meta: [B, Hkv, stride, 2, D] in
+ * dims->dtype, stored in logical page order so that scoring streams each
+ * (b, h) row; stride >= max_b n_b. Entries j >= n_b, and pages whose physical
+ * slot is out of range, are not written. tail_pages = 0 rebuilds every page;
  * tail_pages = n > 0 rebuilds only the last n pages of each sequence (the
  * per-step update after a token is appended). Reads kv->k_pool only. */
 qsa_status qsa_build_page_meta(const qsa_dims* dims, const qsa_paged_kv* kv,
-                               int32_t tail_pages, void* meta,
+                               int32_t tail_pages, void* meta, int32_t stride,
                                hipStream_t stream);
 
 /* Step 2 - upper-bound page score (TinyServe §2.2):
@@ -99,9 +101,10 @@ qsa_status qsa_build_page_meta(const qsa_dims* dims, const qsa_paged_kv* kv,
  * hq / g, accumulated in fp32 (no softmax scale: the ranking does not
  * depend on it). group_scores[b][h][j] = max over the g query heads of KV
  * head h (this keeps the bound: it is >= every group head's largest q.k in
- * the page). Layouts: q [B, Hq, D] in dtype; group_scores [B, Hkv, stride]
- * fp32; head_scores [B, Hq, stride] fp32 or NULL. Entries n_b <= j < stride
- * are written as -inf. Requires stride >= max_b n_b. */
+ * the page). Layouts: q [B, Hq, D] in dtype; meta [B, Hkv, stride, 2, D] as
+ * written by qsa_build_page_meta with the same stride; group_scores
+ * [B, Hkv, stride] fp32; head_scores [B, Hq, stride] fp32 or NULL. Entries
+ * n_b <= j < stride are written as -inf. Requires stride >= max_b n_b. */
 qsa_status qsa_score_pages(const qsa_dims* dims, const void* q,
                            const qsa_paged_kv* kv, const void* meta,
                            float* group_scores, float* head_scores,
@@ -113,8 +116,9 @@ qsa_status qsa_score_pages(const qsa_dims* dims, const void* q,
  * (equal fp32 values, -0 == +0) broken towards the smaller page index.
  * Outputs: sel [B, Hkv, k] int32, ascending page order, padded with -1;
  * sel_count [B, Hkv] = K_eff; sel_phys [B, Hkv, k] (or NULL) = the physical
- * slots of sel, -1 padded. Workspace: qsa_topk_workspace_size bytes (may be
- * 0; ws may then be NULL). */
+ * slots of sel, -1 padded. Rows of up to 16384 pages (stride <= 16384, i.e.
+ * 256K tokens); longer rows return QSA_ERR_UNSUPPORTED. Workspace:
+ * qsa_topk_workspace_size bytes (may be 0; ws may then be NULL). */
 qsa_status qsa_topk_pages(const qsa_dims* dims, const qsa_paged_kv* kv,
                           const float* group_scores, int32_t stride, int32_t k,
                           int32_t* sel, int32_t* sel_count, int32_t* sel_phys,

@@ -186,15 +186,19 @@ int32_t qsa_budget_pages(int32_t budget_tokens, int32_t page_size) {
 }
 
 qsa_status qsa_build_page_meta(const qsa_dims* dims, const qsa_paged_kv* kv, int32_t tail_pages,
-                               void* meta, hipStream_t stream) {
+                               void* meta, int32_t stride, hipStream_t stream) {
   qsa_status s = check_dims(dims);
   if (s != QSA_OK) return s;
   int max_pages = 0;
   if ((s = check_kv(dims, kv, false, &max_pages)) != QSA_OK) return s;
   if (meta == nullptr) return fail(QSA_ERR_INVALID_ARG, "meta is NULL");
   if (tail_pages < 0) return fail(QSA_ERR_INVALID_ARG, "tail_pages %d < 0", tail_pages);
-  return device_status(qsa::launch_build_meta(common(dims, kv), max_pages, tail_pages, meta, stream),
-                       "build_page_meta launch");
+  if (stride < max_pages)
+    return fail(QSA_ERR_INVALID_ARG, "stride %d < longest sequence's page count %d", stride,
+                max_pages);
+  return device_status(
+      qsa::launch_build_meta(common(dims, kv), max_pages, tail_pages, meta, stride, stream),
+      "build_page_meta launch");
 }
 
 qsa_status qsa_score_pages(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv,
@@ -233,6 +237,8 @@ qsa_status qsa_topk_pages(const qsa_dims* dims, const qsa_paged_kv* kv, const fl
   if (group_scores == nullptr || sel == nullptr || sel_count == nullptr)
     return fail(QSA_ERR_INVALID_ARG, "group_scores/sel/sel_count is NULL");
   if (k < 1) return fail(QSA_ERR_INVALID_ARG, "k = %d (must be >= 1)", k);
+  if (stride > qsa::kTopkMaxPages)
+    return fail(QSA_ERR_UNSUPPORTED, "stride %d > %d pages per row", stride, qsa::kTopkMaxPages);
   if (stride < max_pages)
     return fail(QSA_ERR_INVALID_ARG, "stride %d < longest sequence's page count %d", stride,
                 max_pages);

@@ -76,6 +76,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   const int npw = (uend - ubeg > wave) ? (uend - ubeg - wave + 3) / 4 : 0;
 
   // This wave's pages: physical slot and valid-token count, one per lane.
+  // Two dependent loads (selection entry, then table entry).
   int my_p = 0, my_valid = 0;
   if (lane < npw) {
     const int idx = ubeg + wave + 4 * lane;
@@ -115,13 +116,13 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   const char* vbase = reinterpret_cast<const char*>(v_pool) + (size_t)h * kTileBytes;
   const size_t page_stride = (size_t)Hkv * kTileBytes;
 
-  for (int sp = 0; sp < npw; ++sp) {
+  // Issue the loads of page sp of this wave (K in the QK layout, V linear).
+  auto issue = [&](int sp, uint4 (&kA)[2][2], uint4 (&vB)[4]) {
     const int p = __builtin_amdgcn_readlane(my_p, sp);
     const int valid = __builtin_amdgcn_readlane(my_valid, sp);
-    if (valid == 0) continue;
+    if (valid == 0) return;
     const char* kt = kbase + (size_t)p * page_stride;
     const char* vt = vbase + (size_t)p * page_stride;
-    uint4 kA[2][2], vB[4];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       kA[s2][0] = ld16(kt + (gi + 8 * s2) * kRowBytes + qa * 16);
@@ -129,6 +130,12 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) vB[r] = ld16(vt + r * 1024 + lane * 16);
+  };
+
+  // Attention over page sp, whose tiles are in kA / vB.
+  auto process = [&](int sp, const uint4 (&kA)[2][2], const uint4 (&vB)[4]) {
+    const int valid = __builtin_amdgcn_readlane(my_valid, sp);
+    if (valid == 0) return;
 
     // ---- logits of rows gi, gi+8 for every head of the group
     float z[2][G];
@@ -211,6 +218,18 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
         for (int e = 0; e < EPC; ++e) o[hh][e] = __builtin_fmaf(pr[hh], vf[e], o[hh][e]);
     }
     wave_lds_sync();
+  };
+
+  // Software pipeline: the next page's loads are in flight while the current
+  // page is processed (two register buffers, unrolled so no copies).
+  uint4 kA0[2][2], vB0[4], kA1[2][2], vB1[4];
+  if (npw > 0) issue(0, kA0, vB0);
+  for (int sp = 0; sp < npw; sp += 2) {
+    if (sp + 1 < npw) issue(sp + 1, kA1, vB1);
+    process(sp, kA0, vB0);
+    if (sp + 1 >= npw) break;
+    if (sp + 2 < npw) issue(sp + 2, kA0, vB0);
+    process(sp + 1, kA1, vB1);
   }
 
   // ---- wave epilogue: sum l over the lanes of a head, o over the 4 row groups
@@ -263,7 +282,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
 }
 
 // One wave per (b, hq): log-sum-exp merge of the unit partials (and of the
-// shared-prefix partials for the cascade), then normalisation.
+// shared-prefix partials for the cascade), then normalisation. All partial
+// maxima are loaded at once (one per lane), so the merge costs two dependent
+// loads rather than one per unit.
 template <int D>
 __global__ void __launch_bounds__(256) merge_kernel(
     int B, int Hkv, int G, const int* __restrict__ seq_lens, const int* __restrict__ sel_count,
@@ -291,35 +312,62 @@ __global__ void __launch_bounds__(256) merge_kernel(
   }
   int units = count > 0 ? (count + chunk - 1) / chunk : 0;
   units = units < max_units ? units : max_units;  // never beyond the planned workspace
+  const int total = units + n_pre;
 
-  float M = -__builtin_inff(), lsum = 0.0f;
+  // partial i: decode unit i (i < units) or prefix split i - units
+  auto part = [&](int i, const float*& po, const float*& pml) {
+    if (i < units) {
+      const size_t unit = row * (size_t)max_units + i;
+      po = part_o + (unit * G + hh) * D;
+      pml = part_ml + (unit * G + hh) * 2;
+    } else {
+      const size_t pr = ((size_t)h * n_pre + (i - units)) * ((size_t)B * G) + (size_t)b * G + hh;
+      po = pre_o + pr * D;
+      pml = pre_ml + pr * 2;
+    }
+  };
+
+  float M = -__builtin_inff();
+  for (int base = 0; base < total; base += 64) {
+    const int i = base + lane;
+    if (i < total) {
+      const float* po;
+      const float* pml;
+      part(i, po, pml);
+      M = fmaxf(M, pml[0]);
+    }
+  }
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, xshfl(M, msk));
+
+  float lsum = 0.0f;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  auto absorb = [&](const float* po, const float* pml) {
-    const float m = pml[0];
-    const float l = pml[1];
-    if (m == -__builtin_inff()) return;
-    if (m > M) {
-      const float a = (M == -__builtin_inff()) ? 0.0f : fast_exp2(M - m);
-      lsum *= a;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] *= a;
-      M = m;
+  for (int base = 0; base < total; base += 64) {
+    const int i = base + lane;
+    float w = 0.0f;
+    if (i < total) {
+      const float* po;
+      const float* pml;
+      part(i, po, pml);
+      const float m = pml[0];
+      w = (m == -__builtin_inff()) ? 0.0f : fast_exp2(m - M);
+      lsum += w * pml[1];
     }
-    const float w = fast_exp2(m - M);
-    lsum += l * w;
+    const int cnt = min(64, total - base);
+    for (int t = 0; t < cnt; ++t) {
+      const float wt = readlane_f(w, t);
+      const float* po;
+      const float* pml;
+      part(base + t, po, pml);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += po[lane + 64 * e] * w;
-  };
-  for (int uu = 0; uu < units; ++uu) {
-    const size_t unit = row * (size_t)max_units + uu;
-    absorb(part_o + (unit * G + hh) * D, part_ml + (unit * G + hh) * 2);
+      for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(wt, po[lane + 64 * e], acc[e]);
+    }
   }
-  for (int s = 0; s < n_pre; ++s) {
-    const size_t pr = ((size_t)h * n_pre + s) * ((size_t)B * G) + (size_t)b * G + hh;
-    absorb(pre_o + pr * D, pre_ml + pr * 2);
-  }
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) lsum += xshfl(lsum, msk);
+
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) out[(size_t)gw * D + lane + 64 * e] = acc[e] * inv;

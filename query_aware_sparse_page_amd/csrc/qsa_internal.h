@@ -34,10 +34,13 @@ struct Partials {
 };
 
 hipError_t launch_build_meta(const LaunchCommon& c, int max_pages, int tail_pages, void* meta,
-                             hipStream_t stream);
+                             int stride, hipStream_t stream);
 
 hipError_t launch_score(const LaunchCommon& c, const void* q, const void* meta, float* group_scores,
                         float* head_scores, int stride, hipStream_t stream);
+
+// Longest row the top-K kernel handles (pages): 1024 threads x 16 keys.
+constexpr int kTopkMaxPages = 16384;
 
 hipError_t launch_topk(const LaunchCommon& c, const float* group_scores, int stride, int k,
                        int* sel, int* sel_count, int* sel_phys, hipStream_t stream);

@@ -6,11 +6,12 @@
 // 2D between the split query and the page's 512-byte [m | M] metadata row.
 // bf16 products are exact in fp32; they accumulate with v_dot2_f32_bf16.
 //
-// Layout: 16 lanes (one DPP row) per page; lane c of the row holds chunk c
-// of m and chunk c of M (16 bytes each), so each load instruction reads two
-// full 256-byte rows per page. A wave covers 4 pages per step, a workgroup
-// (4 waves) 64 pages of one (sequence, KV head). Lane partials are summed
-// over the row with DPP; the group max over the g query heads is in-lane.
+// Layout: the metadata is in logical page order, so a (sequence, KV head) row
+// is one contiguous stream of 512-byte [m | M] records. 16 lanes (one DPP
+// row) per page; lane c of the row holds chunk c of m and chunk c of M (16
+// bytes each). A wave covers 4 consecutive pages per step (2 KiB contiguous),
+// a workgroup (4 waves) 64 pages. Lane partials are summed over the row with
+// DPP; the group max over the g query heads is in-lane.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -21,8 +22,7 @@ constexpr int kScorePagesPerBlock = 64;
 
 template <typename T, int G>
 __global__ void __launch_bounds__(256) score_kernel(
-    const T* __restrict__ q, const T* __restrict__ meta, int num_phys, int Hkv,
-    const int* __restrict__ page_indptr, const int* __restrict__ page_indices,
+    const T* __restrict__ q, const T* __restrict__ meta, int Hkv,
     const int* __restrict__ seq_lens, float* __restrict__ group_scores,
     float* __restrict__ head_scores, int stride) {
   const int lane = threadIdx.x & 63;
@@ -32,10 +32,10 @@ __global__ void __launch_bounds__(256) score_kernel(
   const int c = lane & 15;      // chunk within a metadata row
   const int slot = lane >> 4;   // which of the wave's 4 pages
   const int L = seq_lens[b];
-  const int n = L > 0 ? (L + kPage - 1) / kPage : 0;
+  const int n = L > 0 ? min((L + kPage - 1) / kPage, stride) : 0;
   const int base_j = blockIdx.x * kScorePagesPerBlock;
   if (base_j >= stride) return;
-  const int* table = page_indices + page_indptr[b];
+  const char* mrow_base = reinterpret_cast<const char*>(meta) + ((size_t)b * Hkv + h) * stride * 512;
 
   // Query chunks of the group's heads, split by sign.
   uint4 qn[G], qp[G];
@@ -54,15 +54,11 @@ __global__ void __launch_bounds__(256) score_kernel(
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     jj[s] = base_j + s * 16 + wave * 4 + slot;
-    ok[s] = false;
-    if (jj[s] < n) {
-      int p = table[jj[s]];
-      if (p >= 0 && p < num_phys) {
-        const char* tile = reinterpret_cast<const char*>(meta) + ((size_t)p * Hkv + h) * 512;
-        mrow[s] = ld16(tile + c * 16);
-        Mrow[s] = ld16(tile + 256 + c * 16);
-        ok[s] = true;
-      }
+    ok[s] = jj[s] < n;
+    if (ok[s]) {
+      const char* rec = mrow_base + (size_t)jj[s] * 512;
+      mrow[s] = ld16(rec + c * 16);
+      Mrow[s] = ld16(rec + 256 + c * 16);
     }
   }
 #pragma unroll
@@ -100,8 +96,8 @@ hipError_t launch_score_t(const LaunchCommon& c, const void* q, const void* meta
   const T* mm = static_cast<const T*>(meta);
 #define QSA_SCORE_CASE(GG)                                                                       \
   case GG:                                                                                       \
-    hipLaunchKernelGGL((score_kernel<T, GG>), grid, dim3(256), 0, stream, qq, mm, c.num_phys, \
-                       c.Hkv, c.page_indptr, c.page_indices, c.seq_lens, gs, hs, stride);        \
+    hipLaunchKernelGGL((score_kernel<T, GG>), grid, dim3(256), 0, stream, qq, mm, c.Hkv,      \
+                       c.seq_lens, gs, hs, stride);                                              \
     break;
   switch (c.G) {
     QSA_SCORE_CASE(1)

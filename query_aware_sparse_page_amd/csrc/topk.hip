@@ -8,7 +8,9 @@
 // still needed (krem). A compaction pass in page order then keeps every page
 // with key > T and the first krem pages with key == T - so ties go to the
 // smaller page index and the output comes out in ascending page order, with
-// the position of a kept page given by two block-wide prefix counts.
+// the position of a kept page given by two block-wide prefix counts. Keys stay
+// in registers for the whole select (up to 16 per thread, so rows of up to
+// 16384 pages); each wave counts into its own LDS histogram.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -26,13 +28,14 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
-template <int kThreads>
+template <int kThreads, int kKeys>
 __global__ void __launch_bounds__(kThreads) topk_kernel(
     const float* __restrict__ group_scores, int stride, int Hkv, const int* __restrict__ seq_lens,
     const int* __restrict__ page_indptr, const int* __restrict__ page_indices, int k,
     int* __restrict__ sel, int* __restrict__ sel_count, int* __restrict__ sel_phys) {
   constexpr int kWaves = kThreads / 64;
-  __shared__ uint32_t hist[256];
+  constexpr int kBinsPad = 257;  // per-wave histogram; the pad spreads the waves over LDS banks
+  __shared__ uint32_t hist[kWaves * kBinsPad];
   __shared__ uint32_t wtot[kWaves];
   __shared__ uint32_t s_digit, s_krem;
 
@@ -48,6 +51,7 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
   const int L = seq_lens[b];
   int n = L > 0 ? (L + kPage - 1) / kPage : 0;
   n = n < stride ? n : stride;
+  n = n < kThreads * kKeys ? n : kThreads * kKeys;
   const int keff = k < n ? k : n;
   const int* table = page_indices + page_indptr[b];
 
@@ -61,21 +65,33 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
     return;
   }
 
+  // Keys stay in registers: slot i holds page j = tid + i * kThreads.
+  uint32_t keys[kKeys];
+#pragma unroll
+  for (int i = 0; i < kKeys; ++i) {
+    const int j = tid + i * kThreads;
+    keys[i] = j < n ? score_key(sc[j]) : 0u;
+  }
+
   uint32_t prefix = 0, mask = 0, krem = (uint32_t)keff;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kThreads) hist[i] = 0;
+    for (int i = tid; i < kWaves * kBinsPad; i += kThreads) hist[i] = 0;
     __syncthreads();
-    for (int j = tid; j < n; j += kThreads) {
-      uint32_t key = score_key(sc[j]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xFFu], 1u);
+#pragma unroll
+    for (int i = 0; i < kKeys; ++i) {
+      const int j = tid + i * kThreads;
+      if (j < n && (keys[i] & mask) == prefix)
+        atomicAdd(&hist[wave * kBinsPad + ((keys[i] >> shift) & 0xFFu)], 1u);
     }
     __syncthreads();
     // Thread t < 256 owns digit 255 - t, so an inclusive scan over t counts
     // the keys whose digit is >= that digit.
     uint32_t v = 0, incl = 0;
     if (tid < 256) {
-      v = hist[255 - tid];
+      const int d = 255 - tid;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += hist[w * kBinsPad + d];
       incl = wave_incl_scan(v);
       if (lane == 63) wtot[wave] = incl;
     }
@@ -96,11 +112,13 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
   }
   const uint32_t T = prefix;
 
-  // Compaction in page order, kThreads pages per round.
+  // Compaction in page order: round i covers pages i*kThreads .. +kThreads.
   uint32_t gt_base = 0, eq_base = 0;
-  for (int base = 0; base < n; base += kThreads) {
-    const int j = base + tid;
-    uint32_t key = j < n ? score_key(sc[j]) : 0u;
+#pragma unroll
+  for (int i = 0; i < kKeys; ++i) {
+    if (i * kThreads >= n) break;
+    const int j = tid + i * kThreads;
+    const uint32_t key = keys[i];
     const uint32_t gt = (j < n && key > T) ? 1u : 0u;
     const uint32_t eq = (j < n && key == T) ? 1u : 0u;
     const uint32_t packed = gt | (eq << 16);
@@ -139,12 +157,17 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
 hipError_t launch_topk(const LaunchCommon& c, const float* group_scores, int stride, int k,
                        int* sel, int* sel_count, int* sel_phys, hipStream_t stream) {
   dim3 grid(c.Hkv, c.B);
-  if (stride > 1024) {
-    hipLaunchKernelGGL(topk_kernel<1024>, grid, dim3(1024), 0, stream, group_scores, stride, c.Hkv,
-                       c.seq_lens, c.page_indptr, c.page_indices, k, sel, sel_count, sel_phys);
+  if (stride <= 256 * 4) {
+    hipLaunchKernelGGL((topk_kernel<256, 4>), grid, dim3(256), 0, stream, group_scores, stride,
+                       c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, k, sel, sel_count, sel_phys);
+  } else if (stride <= 1024 * 8) {
+    hipLaunchKernelGGL((topk_kernel<1024, 8>), grid, dim3(1024), 0, stream, group_scores, stride,
+                       c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, k, sel, sel_count, sel_phys);
+  } else if (stride <= kTopkMaxPages) {
+    hipLaunchKernelGGL((topk_kernel<1024, 16>), grid, dim3(1024), 0, stream, group_scores, stride,
+                       c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, k, sel, sel_count, sel_phys);
   } else {
-    hipLaunchKernelGGL(topk_kernel<256>, grid, dim3(256), 0, stream, group_scores, stride, c.Hkv,
-                       c.seq_lens, c.page_indptr, c.page_indices, k, sel, sel_count, sel_phys);
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -49,7 +49,7 @@ def lib():
         vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
         D, KV = ctypes.POINTER(Dims), ctypes.POINTER(PagedKVStruct)
         sig = {
-            "qsa_build_page_meta": (i32, [D, KV, i32, vp, vp]),
+            "qsa_build_page_meta": (i32, [D, KV, i32, vp, i32, vp]),
             "qsa_score_pages": (i32, [D, vp, KV, vp, vp, vp, i32, vp]),
             "qsa_topk_pages": (i32, [D, KV, vp, i32, i32, vp, vp, vp, vp, sz, vp]),
             "qsa_paged_decode": (i32, [D, vp, KV, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
@@ -138,19 +138,26 @@ class PagedKV:
 
 # ---------------------------------------------------------------- calls
 
-def build_page_meta(kv: PagedKV, meta: Optional[torch.Tensor] = None, tail_pages: int = 0):
+def build_page_meta(kv: PagedKV, meta: Optional[torch.Tensor] = None, tail_pages: int = 0,
+                    stride: Optional[int] = None):
+    """Metadata [B, Hkv, stride, 2, D] in logical page order (stride defaults
+    to the longest sequence's page count, or meta's own stride)."""
     if meta is None:
-        P, H, _, D = kv.k_pool.shape
-        meta = torch.zeros(P, H, 2, D, dtype=kv.k_pool.dtype, device=kv.k_pool.device)
+        stride = stride or kv.max_pages()
+        meta = torch.zeros(kv.num_seqs, kv.num_kv_heads, stride, 2, kv.head_dim,
+                           dtype=kv.k_pool.dtype, device=kv.k_pool.device)
+    stride = int(meta.shape[2])
     d, s = kv.dims(), kv.struct()
-    _check(lib().qsa_build_page_meta(ctypes.byref(d), ctypes.byref(s), tail_pages, _ptr(meta), _stream()))
+    _check(lib().qsa_build_page_meta(ctypes.byref(d), ctypes.byref(s), tail_pages, _ptr(meta), stride, _stream()))
     return meta
 
 
-def score_pages(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, stride: Optional[int] = None,
+def score_pages(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor,
                 head_scores: bool = False, out: Optional[torch.Tensor] = None):
+    """Scores [B, Hkv, stride] (and per-head [B, Hq, stride]) with the
+    metadata's stride."""
     B, Hq, _ = q.shape
-    stride = stride or kv.max_pages()
+    stride = int(meta.shape[2])
     gs = out if out is not None else torch.empty(B, kv.num_kv_heads, stride, dtype=torch.float32, device=q.device)
     hs = torch.empty(B, Hq, stride, dtype=torch.float32, device=q.device) if head_scores else None
     d, s = kv.dims(Hq), kv.struct()

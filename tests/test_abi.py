@@ -72,10 +72,15 @@ def test_validation_errors_return_before_any_device_work(L):
     # a zero-length sequence is rejected from the host copy of seq_lens
     lens = _lens([16, 0, 5, 5])
     kv = qsa.PagedKVStruct(1, 1, 10, 1, 1, 1, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)))
-    st = L.qsa_build_page_meta(ctypes.byref(d), ctypes.byref(kv), 0, 1, None)
+    st = L.qsa_build_page_meta(ctypes.byref(d), ctypes.byref(kv), 0, 1, 8, None)
     assert st == qsa.QSA_ERR_INVALID_ARG and b"seq_lens[1]" in L.qsa_last_error()
-    st = L.qsa_build_page_meta(ctypes.byref(d), ctypes.byref(kv), -1, 1, None)
-    assert st == qsa.QSA_ERR_INVALID_ARG
+    lens[1] = 40
+    st = L.qsa_build_page_meta(ctypes.byref(d), ctypes.byref(kv), -1, 1, 8, None)
+    assert st == qsa.QSA_ERR_INVALID_ARG and b"tail_pages" in L.qsa_last_error()
+    st = L.qsa_build_page_meta(ctypes.byref(d), ctypes.byref(kv), 0, 1, 2, None)   # 40 tokens = 3 pages
+    assert st == qsa.QSA_ERR_INVALID_ARG and b"stride" in L.qsa_last_error()
+    st = L.qsa_topk_pages(ctypes.byref(d), ctypes.byref(kv), 1, 20000, 5, 1, 1, None, None, 0, None)
+    assert st == qsa.QSA_ERR_UNSUPPORTED
     # cascade is bf16 / 128 only
     st = L.qsa_cascade_decode(ctypes.byref(_dims(D=64, dt=qsa.QSA_F32)), None, None, 1, None, None, None, 0,
                               ctypes.c_float(1.0), None, None, None, 0, None)

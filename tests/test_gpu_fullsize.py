@@ -1,0 +1,176 @@
+"""The five workloads at their full sizes, in the launch configuration the
+benchmark uses: the GPU runs the whole batch; the oracle checks sampled
+sequences one by one (their pages are gathered into a compact pool, which is
+input marshalling only - the oracle sees generated inputs, never GPU output)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import qsa_oracle as O
+from query_aware_sparse_page_amd import qsa
+from tests._util import np_store
+from tests.gpu_helpers import assert_close_out, check_selection_row, score_tol
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def subcase(case, seqs):
+    """Oracle inputs for the sequences `seqs` of a (device) case: their pages
+    gathered to a compact host pool with a remapped table."""
+    indptr = case.page_indptr.cpu().numpy()
+    table = case.page_indices.cpu().numpy()
+    lens = case.seq_lens.cpu().numpy()
+    phys, ptr = [], [0]
+    for b in seqs:
+        phys += list(table[indptr[b]:indptr[b + 1]])
+        ptr.append(len(phys))
+    extra = []
+    if case.prefix_pages is not None:
+        extra = list(case.prefix_pages.cpu().numpy())
+    allp = np.array(phys + extra, dtype=np.int64)
+    idx = torch.from_numpy(allp).to(case.k_pool.device)
+    d = dict(
+        q=np_store(case.q[list(seqs)]), k_pool=np_store(case.k_pool[idx]), v_pool=np_store(case.v_pool[idx]),
+        page_indptr=np.array(ptr, dtype=np.int32), page_indices=np.arange(len(phys), dtype=np.int32),
+        seq_lens=lens[list(seqs)].astype(np.int32), dtype=case.dtype,
+    )
+    if extra:
+        d["prefix_pages"] = np.arange(len(phys), len(phys) + len(extra), dtype=np.int32)
+    return d
+
+
+def run_sparse(case, kv):
+    meta = qsa.build_page_meta(kv)
+    gs, hs = qsa.score_pages(case.q, kv, meta, head_scores=True)
+    sel, cnt, phys = qsa.topk_pages(gs, kv, case.k_pages, num_q_heads=case.Hq)
+    out, lse = qsa.paged_decode(case.q, kv, sel=sel, sel_count=cnt, sm_scale=case.sm_scale)
+    torch.cuda.synchronize()
+    return meta, gs, hs, sel, cnt, phys, out, lse
+
+
+def check_sparse_rows(case, kv, seqs, heads_check=None):
+    meta, gs, hs, sel, cnt, phys, out, lse = run_sparse(case, kv)
+    d = subcase(case, seqs)
+    dt = case.dtype
+    ometa = O.build_page_meta(d["k_pool"], dt, d["page_indptr"], d["page_indices"], d["seq_lens"])
+    ohead, ogroup = O.score_pages(d["q"], dt, ometa, dt, d["page_indptr"], d["page_indices"], d["seq_lens"],
+                                  case.Hkv)
+    osel, ocnt = O.topk_pages(ogroup, d["seq_lens"], case.k_pages)
+    G = case.group
+    meta_n, hs_n, gs_n = np_store(meta), hs.cpu().numpy(), gs.cpu().numpy()
+    sel_n, cnt_n, phys_n = sel.cpu().numpy(), cnt.cpu().numpy(), phys.cpu().numpy()
+    qv = O.values_f64(d["q"], dt)
+    mv = O.values_f64(ometa, dt)
+    table_full = case.page_indices.cpu().numpy()
+    indptr_full = case.page_indptr.cpu().numpy()
+    heads = heads_check if heads_check is not None else range(case.Hkv)
+    for si, b in enumerate(seqs):
+        n = O.num_pages(int(d["seq_lens"][si]))
+        for j in range(n):
+            p = int(d["page_indices"][d["page_indptr"][si] + j])
+            assert np.array_equal(meta_n[b, :, j].view(np.uint8), ometa[p].view(np.uint8)), (b, j)
+        for h in heads:
+            for hq in range(h * G, (h + 1) * G):
+                for j in range(0, n, max(1, n // 64)):
+                    p = int(d["page_indices"][d["page_indptr"][si] + j])
+                    tol = score_tol(qv[si, hq], mv[p, h, 0], mv[p, h, 1])
+                    assert abs(float(hs_n[b, hq, j]) - float(ohead[si, hq, j])) <= tol, (b, hq, j)
+            check_selection_row(sel_n[b, h], cnt_n[b, h], phys_n[b, h], ogroup[si, h], n, case.k_pages,
+                                table_full[indptr_full[b]:indptr_full[b + 1]])
+    # Attention: the GPU decode on the oracle's selection for the sampled rows.
+    sel2 = sel.clone()
+    cnt2 = cnt.clone()
+    for si, b in enumerate(seqs):
+        sel2[b] = torch.from_numpy(osel[si]).to(DEV)
+        cnt2[b] = torch.from_numpy(ocnt[si]).to(DEV)
+    out2, lse2 = qsa.paged_decode(case.q, kv, sel=sel2, sel_count=cnt2, sm_scale=case.sm_scale)
+    torch.cuda.synchronize()
+    oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], dt, d["page_indptr"], d["page_indices"],
+                            d["seq_lens"], case.sm_scale, sel=osel, sel_count=ocnt)
+    o_n, l_n = out2.cpu().numpy(), lse2.cpu().numpy()
+    for si, b in enumerate(seqs):
+        assert_close_out(o_n[b], l_n[b], oo[si], ol[si])
+    assert np.all(np.isfinite(out.cpu().numpy()))
+
+
+def test_c2_sparse_full_size_sampled():
+    print("[case] c2 sparse full size: B=16 GQA 32/8 8192 tokens K=153", flush=True)
+    case = workloads.c2_sparse(device=DEV, n_sentinel=64)
+    kv = qsa.PagedKV.from_case(case)
+    check_sparse_rows(case, kv, [0, 9, 15])
+
+
+def test_c4_long_full_size_sampled():
+    print("[case] c4 long full size: B=8 GQA 32/8 131072 tokens K=128", flush=True)
+    case = workloads.c4_long(device=DEV)
+    kv = qsa.PagedKV.from_case(case)
+    check_sparse_rows(case, kv, [5], heads_check=[0, 7])
+
+
+def test_c3_dense_full_size_sampled():
+    print("[case] c3 dense full size: B=64 GQA 64/8 lengths 4096..32768", flush=True)
+    case = workloads.c3_dense(device=DEV, n_sentinel=32)
+    kv = qsa.PagedKV.from_case(case)
+    out, lse = qsa.paged_decode(case.q, kv, sm_scale=case.sm_scale)
+    torch.cuda.synchronize()
+    lens = case.seq_lens_list()
+    seqs = [int(np.argmax(lens)), int(np.argmin(lens)), 17]
+    d = subcase(case, seqs)
+    oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], "bf16", d["page_indptr"], d["page_indices"],
+                            d["seq_lens"], case.sm_scale)
+    o_n, l_n = out.cpu().numpy(), lse.cpu().numpy()
+    for si, b in enumerate(seqs):
+        assert_close_out(o_n[b], l_n[b], oo[si], ol[si])
+    assert np.all(np.isfinite(o_n))
+    # every page selected through the sparse entry: bit-identical
+    K = max(-(-L // 16) for L in lens)
+    sel = torch.full((case.B, case.Hkv, K), -1, dtype=torch.int32)
+    cnt = torch.zeros(case.B, case.Hkv, dtype=torch.int32)
+    for b, L in enumerate(lens):
+        n = -(-L // 16)
+        sel[b, :, :n] = torch.arange(n, dtype=torch.int32)
+        cnt[b] = n
+    o2, l2 = qsa.paged_decode(case.q, kv, sel=sel.to(DEV), sel_count=cnt.to(DEV), sm_scale=case.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, out) and torch.equal(l2, lse)
+
+
+@pytest.mark.parametrize("selective", [False, True])
+def test_c5_cascade_full_size_sampled(selective):
+    print(f"[case] c5 cascade full size: B=256 prefix 4096 suffix 512 selective={selective}", flush=True)
+    case = workloads.c5_cascade(device=DEV, selective=selective, n_sentinel=16)
+    kv = qsa.PagedKV.from_case(case)
+    seqs = [0, 101, 255]
+    d = subcase(case, seqs)
+    sel = cnt = None
+    osel = ocnt = None
+    if selective:
+        meta = qsa.build_page_meta(kv)
+        gs, _ = qsa.score_pages(case.q, kv, meta)
+        sel, cnt, _ = qsa.topk_pages(gs, kv, case.k_pages, num_q_heads=case.Hq)
+        torch.cuda.synchronize()
+        ometa = O.build_page_meta(d["k_pool"], "bf16", d["page_indptr"], d["page_indices"], d["seq_lens"])
+        _, ogroup = O.score_pages(d["q"], "bf16", ometa, "bf16", d["page_indptr"], d["page_indices"],
+                                  d["seq_lens"], case.Hkv)
+        osel, ocnt = O.topk_pages(ogroup, d["seq_lens"], case.k_pages)
+        sel_n, cnt_n = sel.cpu().numpy(), cnt.cpu().numpy()
+        table_full = case.page_indices.cpu().numpy()
+        for si, b in enumerate(seqs):
+            for h in range(case.Hkv):
+                check_selection_row(sel_n[b, h], cnt_n[b, h], None, ogroup[si, h], 32, case.k_pages,
+                                    table_full[b * 32:(b + 1) * 32])
+            sel[b] = torch.from_numpy(osel[si]).to(DEV)
+            cnt[b] = torch.from_numpy(ocnt[si]).to(DEV)
+    out, lse = qsa.cascade_decode(case.q, case.prefix_pages, case.prefix_len, kv, sel=sel, sel_count=cnt,
+                                  sm_scale=case.sm_scale)
+    torch.cuda.synchronize()
+    oo, ol = O.cascade_decode(d["q"], d["k_pool"], d["v_pool"], "bf16", d["prefix_pages"], case.prefix_len,
+                              d["page_indptr"], d["page_indices"], d["seq_lens"], case.sm_scale,
+                              sel=osel, sel_count=ocnt)
+    o_n, l_n = out.cpu().numpy(), lse.cpu().numpy()
+    for si, b in enumerate(seqs):
+        assert_close_out(o_n[b], l_n[b], oo[si], ol[si])
+    assert np.all(np.isfinite(o_n))

@@ -47,14 +47,14 @@ def test_meta_bit_exact(label, lens, Hq, Hkv, dtype, k):
     c = _case(label, lens, Hq, Hkv, dtype)
     d = case_np(c)
     g, kv = _kv(c)
-    meta = qsa.build_page_meta(kv)
+    meta = qsa.build_page_meta(kv, stride=kv.max_pages() + 2)
     torch.cuda.synchronize()
     ref = O.build_page_meta(d["k_pool"], dtype, d["page_indptr"], d["page_indices"], d["seq_lens"])
-    got = np_store(meta)
+    got = np_store(meta)                          # [B, Hkv, stride, 2, D], logical page order
     for b, L in enumerate(d["seq_lens"]):
         for j in range(O.num_pages(L)):
             p = O.physical_page(d["page_indptr"], d["page_indices"], b, j)
-            assert np.array_equal(got[p].view(np.uint8), ref[p].view(np.uint8)), (b, j, p)
+            assert np.array_equal(got[b, :, j].view(np.uint8), ref[p].view(np.uint8)), (b, j, p)
 
 
 def test_meta_tail_update_and_signed_zero():
@@ -72,18 +72,18 @@ def test_meta_tail_update_and_signed_zero():
     torch.cuda.synchronize()
     ref = O.build_page_meta(d["k_pool"], "bf16", d["page_indptr"], d["page_indices"], d["seq_lens"])
     fb, tb = np_store(full), np_store(tail)
-    assert int(fb[p0, 0, 0, 0]) == 0x8000 and int(fb[p0, 0, 1, 0]) == 0x0000
-    assert int(fb[p0, 0, 0, 1]) == 0x8000 and int(fb[p0, 0, 1, 1]) == 0x8000
-    last = {int(d["page_indices"][d["page_indptr"][b + 1] - 1]) for b in range(3)}
+    assert int(fb[0, 0, 0, 0, 0]) == 0x8000 and int(fb[0, 0, 0, 1, 0]) == 0x0000
+    assert int(fb[0, 0, 0, 0, 1]) == 0x8000 and int(fb[0, 0, 0, 1, 1]) == 0x8000
     jb = np_store(junk)
     for b, L in enumerate(d["seq_lens"]):
-        for j in range(O.num_pages(L)):
+        n = O.num_pages(L)
+        for j in range(n):
             p = O.physical_page(d["page_indptr"], d["page_indices"], b, j)
-            assert np.array_equal(fb[p], ref[p])
-            if p in last:
-                assert np.array_equal(tb[p], ref[p])
+            assert np.array_equal(fb[b, :, j], ref[p])
+            if j == n - 1:
+                assert np.array_equal(tb[b, :, j], ref[p])
             else:
-                assert np.array_equal(tb[p], jb[p])
+                assert np.array_equal(tb[b, :, j], jb[b, :, j])
 
 
 def _oracle_scores(c, d, stride):
@@ -99,8 +99,8 @@ def test_scores_and_selection(label, lens, Hq, Hkv, dtype, k):
     d = case_np(c)
     g, kv = _kv(c)
     stride = kv.max_pages() + 3
-    meta = qsa.build_page_meta(kv)
-    gs, hs = qsa.score_pages(g.q, kv, meta, stride=stride, head_scores=True)
+    meta = qsa.build_page_meta(kv, stride=stride)
+    gs, hs = qsa.score_pages(g.q, kv, meta, head_scores=True)
     sel, cnt, phys = qsa.topk_pages(gs, kv, k, num_q_heads=Hq)
     torch.cuda.synchronize()
     ometa, ohead, ogroup = _oracle_scores(c, d, stride)
@@ -239,7 +239,10 @@ def test_error_paths_raise():
     c = _case("err", [64, 40], 8, 2)
     g, kv = _kv(c)
     with pytest.raises(qsa.QsaError) as e:
-        qsa.score_pages(g.q, kv, qsa.build_page_meta(kv), stride=1)
+        qsa.build_page_meta(kv, stride=1)
+    assert e.value.status == qsa.QSA_ERR_INVALID_ARG
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.score_pages(g.q, kv, torch.zeros(2, 2, 1, 2, 128, dtype=torch.bfloat16, device=DEV))
     assert e.value.status == qsa.QSA_ERR_INVALID_ARG
     with pytest.raises(qsa.QsaError) as e:
         qsa.paged_decode(g.q, kv, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
