@@ -14,6 +14,7 @@
  *  - Ownership: the caller owns every buffer. The library never allocates or
  *    frees device memory and keeps no state between calls; scratch space is a
  *    caller-provided workspace of the size the *_workspace_size query returns.
+ *    Calls that share a workspace must not run concurrently.
  *  - Ordering: work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream) and the call returns without synchronising. Outputs are valid
  *    once the stream reaches that point.
@@ -104,11 +105,16 @@ qsa_status qsa_build_page_meta(const qsa_dims* dims, const qsa_paged_kv* kv,
  * the page). Layouts: q [B, Hq, D] in dtype; meta [B, Hkv, stride, 2, D] as
  * written by qsa_build_page_meta with the same stride; group_scores
  * [B, Hkv, stride] fp32; head_scores [B, Hq, stride] fp32 or NULL. Entries
- * n_b <= j < stride are written as -inf. Requires stride >= max_b n_b. */
+ * n_b <= j < stride are written as -inf. Requires stride >= max_b n_b.
+ * refresh_tail = 1 first rebuilds each sequence's last page's metadata from
+ * kv->k_pool exactly as qsa_build_page_meta(tail_pages = 1) would (writing
+ * meta) and scores with it - the per-decode-step update of §5.3 fused into
+ * this call; refresh_tail = 0 only reads meta. */
 qsa_status qsa_score_pages(const qsa_dims* dims, const void* q,
-                           const qsa_paged_kv* kv, const void* meta,
+                           const qsa_paged_kv* kv, void* meta,
                            float* group_scores, float* head_scores,
-                           int32_t stride, hipStream_t stream);
+                           int32_t stride, int32_t refresh_tail,
+                           hipStream_t stream);
 
 /* Step 3 - top-K page selection per (sequence, KV head) (TinyServe §2.3; the
  * radix select of the Vortex digest, optimisations). For each (b, h):

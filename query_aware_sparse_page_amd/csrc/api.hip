@@ -97,56 +97,73 @@ qsa::LaunchCommon common(const qsa_dims* d, const qsa_paged_kv* kv) {
   return c;
 }
 
-// Work units wanted per launch: enough to give every CU several workgroups.
-int target_units() {
-  static const int t = [] {
-    const char* e = std::getenv("QSA_DECODE_TARGET_UNITS");
-    int v = e ? std::atoi(e) : 0;
-    return v > 0 ? v : 2048;
-  }();
-  return t;
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
 }
 
-// Pages per unit: the largest chunk that still yields target_units() units;
-// counts per (b, h) row are min(k, n_b) (every page when k <= 0).
+// Work units wanted per launch: two 4-wave units per CU, i.e. two waves per
+// SIMD, so that every SIMD gets the same number of pages in one round.
+int target_units() {
+  static const int env = [] {
+    const char* e = std::getenv("QSA_DECODE_TARGET_UNITS");
+    return e ? std::atoi(e) : 0;
+  }();
+  return env > 0 ? env : 2 * device_cus();
+}
+
+// Pages per unit: a multiple of 4 (one quarter per wave) sized so that the
+// rows' pages fill about target_units() equal units; counts per (b, h) row are
+// min(k, n_b) (every page when k <= 0). Capped at 256 (64 pages per wave).
 qsa::DecodePlan make_plan(const qsa_dims* d, const int32_t* lens, int32_t k) {
-  static const int kChunks[] = {256, 128, 64, 32, 16, 8, 4};
   qsa::DecodePlan plan;
+  long long total = 0;
   int maxc = 0;
   for (int b = 0; b < d->num_seqs; ++b) {
     int c = pages_of(lens[b]);
     if (k > 0) c = std::min(c, (int)k);
     maxc = std::max(maxc, c);
+    total += (long long)d->num_kv_heads * c;
   }
-  plan.chunk = 4;
-  for (int ch : kChunks) {
-    long long units = 0;
-    for (int b = 0; b < d->num_seqs; ++b) {
-      int c = pages_of(lens[b]);
-      if (k > 0) c = std::min(c, (int)k);
-      units += (long long)d->num_kv_heads * ((c + ch - 1) / ch);
-    }
-    if (units >= target_units()) {
-      plan.chunk = ch;
-      break;
-    }
-  }
-  plan.max_units = (maxc + plan.chunk - 1) / plan.chunk;
+  const long long per = (total + target_units() - 1) / target_units();
+  int chunk = (int)std::min<long long>(256, std::max<long long>(4, (per + 3) / 4 * 4));
+  plan.chunk = chunk;
+  plan.max_units = (maxc + chunk - 1) / chunk;
   return plan;
 }
 
+// Decode workspace: [unit partial outputs][unit partial (max, sum)], each
+// region 256-byte aligned.
 struct DecodeWs {
   size_t o_bytes = 0, ml_bytes = 0;
   size_t total() const { return align_up(o_bytes) + align_up(ml_bytes); }
 };
 
 DecodeWs decode_ws(const qsa_dims* d, const qsa::DecodePlan& plan) {
-  const size_t units = (size_t)d->num_seqs * d->num_kv_heads * plan.max_units;
+  const size_t rows = (size_t)d->num_seqs * d->num_kv_heads;
+  const size_t units = rows * plan.max_units;
   const int g = d->num_q_heads / d->num_kv_heads;
   DecodeWs w;
   w.o_bytes = units * g * d->head_dim * sizeof(float);
   w.ml_bytes = units * g * 2 * sizeof(float);
   return w;
+}
+
+qsa::Partials carve(void* ws, const DecodeWs& w) {
+  char* base = static_cast<char*>(ws);
+  qsa::Partials p;
+  p.o = reinterpret_cast<float*>(base);
+  p.ml = reinterpret_cast<float*>(base + align_up(w.o_bytes));
+  return p;
 }
 
 constexpr int kPrefixSplitTokens = 1024;  // prefix tokens per cascade split
@@ -201,9 +218,9 @@ qsa_status qsa_build_page_meta(const qsa_dims* dims, const qsa_paged_kv* kv, int
       "build_page_meta launch");
 }
 
-qsa_status qsa_score_pages(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv,
-                           const void* meta, float* group_scores, float* head_scores,
-                           int32_t stride, hipStream_t stream) {
+qsa_status qsa_score_pages(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv, void* meta,
+                           float* group_scores, float* head_scores, int32_t stride,
+                           int32_t refresh_tail, hipStream_t stream) {
   qsa_status s = check_dims(dims);
   if (s != QSA_OK) return s;
   int max_pages = 0;
@@ -213,9 +230,11 @@ qsa_status qsa_score_pages(const qsa_dims* dims, const void* q, const qsa_paged_
   if (stride < max_pages)
     return fail(QSA_ERR_INVALID_ARG, "stride %d < longest sequence's page count %d", stride,
                 max_pages);
-  return device_status(
-      qsa::launch_score(common(dims, kv), q, meta, group_scores, head_scores, stride, stream),
-      "score_pages launch");
+  if (refresh_tail != 0 && refresh_tail != 1)
+    return fail(QSA_ERR_INVALID_ARG, "refresh_tail %d (0 or 1)", refresh_tail);
+  return device_status(qsa::launch_score(common(dims, kv), q, meta, refresh_tail, group_scores,
+                                         head_scores, stride, stream),
+                       "score_pages launch");
 }
 
 size_t qsa_topk_workspace_size(const qsa_dims* dims, int32_t max_pages, int32_t k) {
@@ -285,16 +304,12 @@ qsa_status qsa_paged_decode(const qsa_dims* dims, const void* q, const qsa_paged
   const DecodeWs w = decode_ws(dims, plan);
   if (ws_bytes < w.total() || (w.total() > 0 && ws == nullptr))
     return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, w.total());
-  qsa::Partials part;
-  part.o = static_cast<float*>(ws);
-  part.ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(w.o_bytes));
+  const qsa::Partials part = carve(ws, w);
   const qsa::LaunchCommon c = common(dims, kv);
   const float scale_log2 = sm_scale * 1.4426950408889634f;
-  hipError_t e = qsa::launch_decode_split(c, q, sel, sel_count, kk, scale_log2, plan, part, stream);
-  if (e != hipSuccess) return device_status(e, "paged_decode split launch");
-  e = qsa::launch_merge(c, sel != nullptr ? sel_count : nullptr, kk, plan, part, qsa::Partials{}, 0,
-                        out, lse, stream);
-  return device_status(e, "paged_decode merge launch");
+  return device_status(qsa::launch_decode(c, q, sel, sel_count, kk, scale_log2, plan, part,
+                                          qsa::Partials{}, 0, out, lse, stream),
+                       "paged_decode launch");
 }
 
 size_t qsa_cascade_workspace_size(const qsa_dims* dims, int32_t prefix_len,
@@ -329,9 +344,7 @@ qsa_status qsa_cascade_decode(const qsa_dims* dims, const void* q, const int32_t
   if (ws_bytes < need || ws == nullptr)
     return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
   char* base = static_cast<char*>(ws);
-  qsa::Partials part;
-  part.o = reinterpret_cast<float*>(base);
-  part.ml = reinterpret_cast<float*>(base + align_up(w.o_bytes));
+  const qsa::Partials part = carve(ws, w);
   const int nsplit = prefix_splits(prefix_len);
   const size_t rows = (size_t)dims->num_kv_heads * nsplit * (dims->num_q_heads / dims->num_kv_heads) *
                       dims->num_seqs;
@@ -343,11 +356,9 @@ qsa_status qsa_cascade_decode(const qsa_dims* dims, const void* q, const int32_t
   hipError_t e = qsa::launch_cascade_prefix(c, q, prefix_pages, prefix_len, nsplit, scale_log2, pre,
                                             stream);
   if (e != hipSuccess) return device_status(e, "cascade prefix launch");
-  e = qsa::launch_decode_split(c, q, sel, sel_count, kk, scale_log2, plan, part, stream);
-  if (e != hipSuccess) return device_status(e, "cascade suffix launch");
-  e = qsa::launch_merge(c, sel != nullptr ? sel_count : nullptr, kk, plan, part, pre, nsplit, out,
-                        lse, stream);
-  return device_status(e, "cascade merge launch");
+  e = qsa::launch_decode(c, q, sel, sel_count, kk, scale_log2, plan, part, pre, nsplit, out, lse,
+                         stream);
+  return device_status(e, "cascade suffix launch");
 }
 
 }  // extern "C"

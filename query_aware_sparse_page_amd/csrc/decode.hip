@@ -23,7 +23,9 @@
 //    {l/16, 4+l/16, 8+l/16, 12+l/16}; probabilities move from the QK layout
 //    through 512 B of LDS per page; o[g][chunk] accumulates in fp32.
 // Unit results (o unnormalised, max, sum) go to the workspace and are merged
-// per (b, hq) by merge_kernel.
+// per (b, hq) by merge_kernel. (Merging inside the last-arriving unit would
+// need device-scope release fences in every unit; on this chip those write
+// back the XCD's L2 and cost far more than the separate launch.)
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -41,7 +43,8 @@ struct DecodeShared {
 };
 
 template <typename T, int G>
-__global__ void __launch_bounds__(256) decode_split_kernel(
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ k_pool, const T* __restrict__ v_pool,
     int num_phys, int Hkv, const int* __restrict__ page_indptr,
     const int* __restrict__ page_indices, const int* __restrict__ seq_lens,
@@ -51,38 +54,45 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   constexpr int EPC = Elem<T>::kPerChunk;
   constexpr int D = 16 * EPC;
   constexpr int NP = (2 * G + 7) / 8;  // (row, head) pairs owned per lane
+  constexpr int kStages = G >= 8 ? 2 : 3;  // pages in flight per wave (register budget)
   __shared__ DecodeShared<T, G> sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int u = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int Hq = Hkv * G;
-  const int L = seq_lens[b];
-  if (L <= 0) return;
-  const int n = (L + kPage - 1) / kPage;
   const size_t row = (size_t)b * Hkv + h;
+  const int ubeg = u * chunk;
+  // First level of loads, all independent: row length, selection count,
+  // table base and (speculatively) this wave's selection entries.
+  const int L = seq_lens[b];
+  const int cnt_sel = sel != nullptr ? sel_count[row] : 0;
+  const int tbase = page_indptr[b];
+  const int idx = ubeg + wave + 4 * lane;
+  int jsel = idx;
+  if (sel != nullptr && lane < (chunk >> 2) && idx < k_stride) jsel = sel[row * k_stride + idx];
+  const int n = L > 0 ? (L + kPage - 1) / kPage : 0;
   int count = n;
   if (sel != nullptr) {
-    count = sel_count[row];
-    count = count < k_stride ? count : k_stride;
+    count = cnt_sel < k_stride ? cnt_sel : k_stride;
     count = count < n ? count : n;  // a row selects distinct pages of the sequence
+    count = count > 0 ? count : 0;
   }
-  const int ubeg = u * chunk;
-  if (ubeg >= count) return;  // whole workgroup: nothing in this unit
+  int units = (count + chunk - 1) / chunk;
+  units = units < 1 ? 1 : (units < max_units ? units : max_units);
+  if (u >= units) return;  // whole workgroup: nothing in this unit
   const int uend = min(ubeg + chunk, count);
   const int npw = (uend - ubeg > wave) ? (uend - ubeg - wave + 3) / 4 : 0;
 
   // This wave's pages: physical slot and valid-token count, one per lane.
-  // Two dependent loads (selection entry, then table entry).
   int my_p = 0, my_valid = 0;
   if (lane < npw) {
-    const int idx = ubeg + wave + 4 * lane;
-    const int j = sel != nullptr ? sel[row * k_stride + idx] : idx;
+    const int j = jsel;
     if (j >= 0 && j < n) {
-      const int p = page_indices[page_indptr[b] + j];
+      const int p = page_indices[tbase + j];
       if (p >= 0 && p < num_phys) {
         my_p = p;
         my_valid = min(kPage, L - kPage * j);
@@ -117,10 +127,11 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   const size_t page_stride = (size_t)Hkv * kTileBytes;
 
   // Issue the loads of page sp of this wave (K in the QK layout, V linear).
+  // Branch-free, so the compiler's wait counts stay exact and the next page's
+  // loads overlap the current page's math; a skipped page (no valid tokens)
+  // reads physical slot 0, which always exists.
   auto issue = [&](int sp, uint4 (&kA)[2][2], uint4 (&vB)[4]) {
     const int p = __builtin_amdgcn_readlane(my_p, sp);
-    const int valid = __builtin_amdgcn_readlane(my_valid, sp);
-    if (valid == 0) return;
     const char* kt = kbase + (size_t)p * page_stride;
     const char* vt = vbase + (size_t)p * page_stride;
 #pragma unroll
@@ -208,9 +219,12 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
       for (int hh = 0; hh < G; ++hh) pr[hh] = pb[t * G + hh];
       float vf[EPC];
       chunk_unpack(vB[r], vf, T{});
-      if (valid < kPage && t >= valid) {
+      if (__builtin_expect(valid < kPage, 0)) {
+        // rows past the end of a partial last page may hold anything
+        if (t >= valid) {
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) vf[e] = 0.0f;  // rows past the end may hold anything
+          for (int e = 0; e < EPC; ++e) vf[e] = 0.0f;
+        }
       }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh)
@@ -220,16 +234,39 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
     wave_lds_sync();
   };
 
-  // Software pipeline: the next page's loads are in flight while the current
-  // page is processed (two register buffers, unrolled so no copies).
-  uint4 kA0[2][2], vB0[4], kA1[2][2], vB1[4];
-  if (npw > 0) issue(0, kA0, vB0);
-  for (int sp = 0; sp < npw; sp += 2) {
-    if (sp + 1 < npw) issue(sp + 1, kA1, vB1);
-    process(sp, kA0, vB0);
-    if (sp + 1 >= npw) break;
-    if (sp + 2 < npw) issue(sp + 2, kA0, vB0);
-    process(sp + 1, kA1, vB1);
+  // Software pipeline: the loads of the next kStages-1 pages are in flight
+  // while the current page is processed (HBM latency is several times the
+  // math of one page). kStages register buffers, rotated by an unrolled loop
+  // so no data is copied; past the wave's last page the prefetch re-reads
+  // that page (an L2 hit, no extra HBM traffic).
+  if (npw > 0) {
+    uint4 kA0[2][2], vB0[4], kA1[2][2], vB1[4];
+    issue(0, kA0, vB0);
+    int sp = 0;
+    if constexpr (kStages == 2) {
+      while (true) {
+        issue(min(sp + 1, npw - 1), kA1, vB1);
+        process(sp, kA0, vB0);
+        if (++sp >= npw) break;
+        issue(min(sp + 1, npw - 1), kA0, vB0);
+        process(sp, kA1, vB1);
+        if (++sp >= npw) break;
+      }
+    } else {
+      uint4 kA2[2][2], vB2[4];
+      issue(min(1, npw - 1), kA1, vB1);
+      while (true) {
+        issue(min(sp + 2, npw - 1), kA2, vB2);
+        process(sp, kA0, vB0);
+        if (++sp >= npw) break;
+        issue(min(sp + 2, npw - 1), kA0, vB0);
+        process(sp, kA1, vB1);
+        if (++sp >= npw) break;
+        issue(min(sp + 2, npw - 1), kA1, vB1);
+        process(sp, kA2, vB2);
+        if (++sp >= npw) break;
+      }
+    }
   }
 
   // ---- wave epilogue: sum l over the lanes of a head, o over the 4 row groups
@@ -259,9 +296,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
 
   // ---- workgroup combine of the 4 waves -> one partial per (unit, head)
   const size_t unit = row * (size_t)max_units + u;
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int hh = idx / D;
-    const int d = idx - hh * D;
+  for (int idx2 = tid; idx2 < G * D; idx2 += 256) {
+    const int hh = idx2 / D;
+    const int d = idx2 - hh * D;
     float M = -__builtin_inff();
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, sh.ml[w][hh][0]);
@@ -279,12 +316,13 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
       part_ml[(unit * G + hh) * 2 + 1] = lsum;
     }
   }
+
 }
 
 // One wave per (b, hq): log-sum-exp merge of the unit partials (and of the
-// shared-prefix partials for the cascade), then normalisation. All partial
-// maxima are loaded at once (one per lane), so the merge costs two dependent
-// loads rather than one per unit.
+// shared-prefix partials for the cascade), then normalisation. The partials
+// are loaded without waiting for the row's unit count (every slot the row can
+// own is in bounds), so the merge costs one round of dependent loads.
 template <int D>
 __global__ void __launch_bounds__(256) merge_kernel(
     int B, int Hkv, int G, const int* __restrict__ seq_lens, const int* __restrict__ sel_count,
@@ -293,8 +331,9 @@ __global__ void __launch_bounds__(256) merge_kernel(
     const float* __restrict__ pre_ml, int n_pre, float* __restrict__ out,
     float* __restrict__ lse) {
   constexpr int PER = D / 64;
+  constexpr int kBatch = 8;
   const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Hq = Hkv * G;
   if (gw >= B * Hq) return;
   const int b = gw / Hq;
@@ -302,72 +341,67 @@ __global__ void __launch_bounds__(256) merge_kernel(
   const int h = hq / G;
   const int hh = hq - h * G;
   const size_t row = (size_t)b * Hkv + h;
+  const size_t pre_row = (size_t)b * G + hh;
   const int L = seq_lens[b];
-  const int n = L > 0 ? (L + kPage - 1) / kPage : 0;
-  int count = n;
-  if (sel_count != nullptr) {
-    count = sel_count[row];
-    count = count < k_stride ? count : k_stride;
-    count = count < n ? count : n;
-  }
-  int units = count > 0 ? (count + chunk - 1) / chunk : 0;
-  units = units < max_units ? units : max_units;  // never beyond the planned workspace
-  const int total = units + n_pre;
+  const int cnt_sel = sel_count != nullptr ? sel_count[row] : 0;
+  const int slots = max_units + n_pre;
 
-  // partial i: decode unit i (i < units) or prefix split i - units
-  auto part = [&](int i, const float*& po, const float*& pml) {
-    if (i < units) {
-      const size_t unit = row * (size_t)max_units + i;
-      po = part_o + (unit * G + hh) * D;
-      pml = part_ml + (unit * G + hh) * 2;
-    } else {
-      const size_t pr = ((size_t)h * n_pre + (i - units)) * ((size_t)B * G) + (size_t)b * G + hh;
-      po = pre_o + pr * D;
-      pml = pre_ml + pr * 2;
-    }
-  };
-
-  float M = -__builtin_inff();
-  for (int base = 0; base < total; base += 64) {
-    const int i = base + lane;
-    if (i < total) {
-      const float* po;
-      const float* pml;
-      part(i, po, pml);
-      M = fmaxf(M, pml[0]);
-    }
-  }
-#pragma unroll
-  for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, xshfl(M, msk));
-
-  float lsum = 0.0f;
+  float M = -__builtin_inff(), lsum = 0.0f;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  for (int base = 0; base < total; base += 64) {
-    const int i = base + lane;
-    float w = 0.0f;
-    if (i < total) {
-      const float* po;
-      const float* pml;
-      part(i, po, pml);
-      const float m = pml[0];
-      w = (m == -__builtin_inff()) ? 0.0f : fast_exp2(m - M);
-      lsum += w * pml[1];
-    }
-    const int cnt = min(64, total - base);
-    for (int t = 0; t < cnt; ++t) {
-      const float wt = readlane_f(w, t);
-      const float* po;
-      const float* pml;
-      part(base + t, po, pml);
+  int units = -1;
+  for (int base = 0; base < slots; base += kBatch) {
+    float m[kBatch], l[kBatch], v[kBatch][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(wt, po[lane + 64 * e], acc[e]);
+    for (int t = 0; t < kBatch; ++t) {
+      const int i = min(base + t, slots - 1);
+      const float* po;
+      const float* pml;
+      if (i < max_units) {
+        const size_t un = row * max_units + i;
+        po = part_o + (un * G + hh) * D;
+        pml = part_ml + (un * G + hh) * 2;
+      } else {
+        const size_t pr = ((size_t)h * n_pre + (i - max_units)) * ((size_t)B * G) + pre_row;
+        po = pre_o + pr * D;
+        pml = pre_ml + pr * 2;
+      }
+      m[t] = pml[0];
+      l[t] = pml[1];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[t][e] = po[lane + 64 * e];
+    }
+    if (units < 0) {
+      const int n = L > 0 ? (L + kPage - 1) / kPage : 0;
+      int count = n;
+      if (sel_count != nullptr) {
+        count = cnt_sel < k_stride ? cnt_sel : k_stride;
+        count = count < n ? count : n;
+        count = count > 0 ? count : 0;
+      }
+      units = (count + chunk - 1) / chunk;
+      units = units < max_units ? units : max_units;
+    }
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int i = base + t;
+      // slots past the row's units (and past the list) hold stale values
+      const bool use = i < slots && (i < units || i >= max_units);
+      if (!use || m[t] == -__builtin_inff()) continue;
+      if (m[t] > M) {
+        const float a = (M == -__builtin_inff()) ? 0.0f : fast_exp2(M - m[t]);
+        lsum *= a;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] *= a;
+        M = m[t];
+      }
+      const float w = fast_exp2(m[t] - M);
+      lsum = __builtin_fmaf(w, l[t], lsum);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(w, v[t][e], acc[e]);
     }
   }
-#pragma unroll
-  for (int msk = 1; msk < 64; msk <<= 1) lsum += xshfl(lsum, msk);
-
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) out[(size_t)gw * D + lane + 64 * e] = acc[e] * inv;
@@ -379,7 +413,8 @@ __global__ void __launch_bounds__(256) merge_kernel(
 template <typename T>
 hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
                            const int* sel_count, int k, float scale_log2, const DecodePlan& plan,
-                           Partials part, hipStream_t stream) {
+                           Partials part, Partials prefix, int n_prefix, float* out, float* lse,
+                           hipStream_t stream) {
   dim3 grid(plan.max_units, c.Hkv, c.B);
   const T* qq = static_cast<const T*>(q);
   const T* kk = static_cast<const T*>(c.k_pool);
@@ -399,34 +434,33 @@ hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
       return hipErrorInvalidValue;
   }
 #undef QSA_DECODE_CASE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 mgrid((c.B * c.Hq + 3) / 4);
+  const int* sc = sel != nullptr ? sel_count : nullptr;
+  if (c.D == 128) {
+    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, stream, c.B, c.Hkv, c.G, c.seq_lens,
+                       sc, k, plan.chunk, plan.max_units, part.o, part.ml, prefix.o, prefix.ml,
+                       n_prefix, out, lse);
+  } else {
+    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(256), 0, stream, c.B, c.Hkv, c.G, c.seq_lens,
+                       sc, k, plan.chunk, plan.max_units, part.o, part.ml, prefix.o, prefix.ml,
+                       n_prefix, out, lse);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_split(const LaunchCommon& c, const void* q, const int* sel,
-                               const int* sel_count, int k, float scale_log2,
-                               const DecodePlan& plan, Partials part, hipStream_t stream) {
+hipError_t launch_decode(const LaunchCommon& c, const void* q, const int* sel, const int* sel_count,
+                         int k, float scale_log2, const DecodePlan& plan, Partials part,
+                         Partials prefix, int n_prefix, float* out, float* lse,
+                         hipStream_t stream) {
   if (plan.max_units <= 0) return hipSuccess;
-  return c.bf16 ? launch_decode_t<bf16s>(c, q, sel, sel_count, k, scale_log2, plan, part, stream)
-                : launch_decode_t<float>(c, q, sel, sel_count, k, scale_log2, plan, part, stream);
-}
-
-hipError_t launch_merge(const LaunchCommon& c, const int* sel_count, int k, const DecodePlan& plan,
-                        Partials part, Partials prefix, int n_prefix_splits, float* out,
-                        float* lse, hipStream_t stream) {
-  const int waves = c.B * c.Hq;
-  dim3 grid((waves + 3) / 4);
-  if (c.D == 128) {
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, stream, c.B, c.Hkv, c.G, c.seq_lens,
-                       sel_count, k, plan.chunk, plan.max_units, part.o, part.ml, prefix.o,
-                       prefix.ml, n_prefix_splits, out, lse);
-  } else {
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, stream, c.B, c.Hkv, c.G, c.seq_lens,
-                       sel_count, k, plan.chunk, plan.max_units, part.o, part.ml, prefix.o,
-                       prefix.ml, n_prefix_splits, out, lse);
-  }
-  return hipGetLastError();
+  return c.bf16 ? launch_decode_t<bf16s>(c, q, sel, sel_count, k, scale_log2, plan, part, prefix,
+                                         n_prefix, out, lse, stream)
+                : launch_decode_t<float>(c, q, sel, sel_count, k, scale_log2, plan, part, prefix,
+                                         n_prefix, out, lse, stream);
 }
 
 }  // namespace qsa

@@ -173,6 +173,63 @@ __device__ __forceinline__ uint32_t xshfl_u(uint32_t v, int mask) {
   return (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, (int)v);
 }
 
+__device__ __forceinline__ float readlane_f_(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// ---- wave64 scans / reductions on DPP (no LDS crossbar) ----------------
+template <int kCtrl, int kRowMask = 0xF, int kBankMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  // lanes whose source is outside the row (or not enabled) read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, kBankMask, true);
+}
+
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each 16-lane
+// row (row_shr 1, 2, 4, 8), then row_bcast:15 / row_bcast:31 carry the row
+// totals into the following rows.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
+  v += dpp_u<0x111>(v);  // row_shr:1
+  v += dpp_u<0x112>(v);  // row_shr:2
+  v += dpp_u<0x114>(v);  // row_shr:4
+  v += dpp_u<0x118>(v);  // row_shr:8
+  v += dpp_u<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_u<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_full_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xF, 0xF, true);
+}
+// Minimum / maximum over the 64 lanes, returned in every lane (uniform).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_full_u<kDppQuadXor1>(v));
+  v = min(v, dpp_full_u<kDppQuadXor2>(v));
+  v = min(v, dpp_full_u<kDppRowHalfMirror>(v));
+  v = min(v, dpp_full_u<kDppRowMirror>(v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return min(min(a, b), min(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_full_u<kDppQuadXor1>(v));
+  v = max(v, dpp_full_u<kDppQuadXor2>(v));
+  v = max(v, dpp_full_u<kDppRowHalfMirror>(v));
+  v = max(v, dpp_full_u<kDppRowMirror>(v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+// Sum / max of floats over the 64 lanes, returned in every lane.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v = sum16(v);
+  return readlane_f_(v, 0) + readlane_f_(v, 16) + readlane_f_(v, 32) + readlane_f_(v, 48);
+}
+
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }

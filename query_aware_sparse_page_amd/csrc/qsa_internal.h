@@ -36,8 +36,8 @@ struct Partials {
 hipError_t launch_build_meta(const LaunchCommon& c, int max_pages, int tail_pages, void* meta,
                              int stride, hipStream_t stream);
 
-hipError_t launch_score(const LaunchCommon& c, const void* q, const void* meta, float* group_scores,
-                        float* head_scores, int stride, hipStream_t stream);
+hipError_t launch_score(const LaunchCommon& c, const void* q, void* meta, int refresh_tail,
+                        float* group_scores, float* head_scores, int stride, hipStream_t stream);
 
 // Longest row the top-K kernel handles (pages): 1024 threads x 16 keys.
 constexpr int kTopkMaxPages = 16384;
@@ -45,16 +45,13 @@ constexpr int kTopkMaxPages = 16384;
 hipError_t launch_topk(const LaunchCommon& c, const float* group_scores, int stride, int k,
                        int* sel, int* sel_count, int* sel_phys, hipStream_t stream);
 
-hipError_t launch_decode_split(const LaunchCommon& c, const void* q, const int* sel,
-                               const int* sel_count, int k, float scale_log2,
-                               const DecodePlan& plan, Partials part, hipStream_t stream);
-
-// Merge the decode partials of every (b, hq) (and, if prefix != nullptr, the
-// per-query prefix partials: n_prefix_splits of them per query row
-// r = b*G + (hq % G) of KV head h, laid out [Hkv][n_prefix_splits][B*G]).
-hipError_t launch_merge(const LaunchCommon& c, const int* sel_count, int k, const DecodePlan& plan,
-                        Partials part, Partials prefix, int n_prefix_splits, float* out,
-                        float* lse, hipStream_t stream);
+// Split-K decode (partials into `part`) followed by the log-sum-exp merge of
+// each (b, hq) into out / lse, which also folds in n_prefix shared-prefix
+// partials per query row laid out [Hkv][n_prefix][B*G] (cascade).
+hipError_t launch_decode(const LaunchCommon& c, const void* q, const int* sel, const int* sel_count,
+                         int k, float scale_log2, const DecodePlan& plan, Partials part,
+                         Partials prefix, int n_prefix, float* out, float* lse,
+                         hipStream_t stream);
 
 // Cascade prefix on the matrix cores (bf16, D = 128): partials per
 // (KV head, split, query row).

@@ -6,6 +6,11 @@
 // 2D between the split query and the page's 512-byte [m | M] metadata row.
 // bf16 products are exact in fp32; they accumulate with v_dot2_f32_bf16.
 //
+// With refresh_tail set, the wave that holds a row's last page first rebuilds
+// that page's min/max from the keys (the per-step update after a token is
+// appended) and writes it back, so a decode step needs no separate metadata
+// launch.
+//
 // Layout: the metadata is in logical page order, so a (sequence, KV head) row
 // is one contiguous stream of 512-byte [m | M] records. 16 lanes (one DPP
 // row) per page; lane c of the row holds chunk c of m and chunk c of M (16
@@ -20,23 +25,52 @@ namespace {
 
 constexpr int kScorePagesPerBlock = 64;
 
+template <typename T>
+struct KeyOps;
+template <>
+struct KeyOps<bf16s> {
+  static __device__ __forceinline__ uint32_t key(uint32_t x) { return bf2_to_key(x); }
+  static __device__ __forceinline__ uint32_t unkey(uint32_t k) { return key_to_bf2(k); }
+  static __device__ __forceinline__ uint32_t vmin(uint32_t a, uint32_t b) { return umin2x16(a, b); }
+  static __device__ __forceinline__ uint32_t vmax(uint32_t a, uint32_t b) { return umax2x16(a, b); }
+};
+template <>
+struct KeyOps<float> {
+  static __device__ __forceinline__ uint32_t key(uint32_t x) { return f32_to_key(x); }
+  static __device__ __forceinline__ uint32_t unkey(uint32_t k) { return key_to_f32(k); }
+  static __device__ __forceinline__ uint32_t vmin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+  static __device__ __forceinline__ uint32_t vmax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+};
+
 template <typename T, int G>
 __global__ void __launch_bounds__(256) score_kernel(
-    const T* __restrict__ q, const T* __restrict__ meta, int Hkv,
-    const int* __restrict__ seq_lens, float* __restrict__ group_scores,
-    float* __restrict__ head_scores, int stride) {
+    const T* __restrict__ q, T* __restrict__ meta, int Hkv, const int* __restrict__ seq_lens,
+    const int* __restrict__ page_indptr, const int* __restrict__ page_indices,
+    const T* __restrict__ k_pool, int num_phys, int refresh_tail,
+    float* __restrict__ group_scores, float* __restrict__ head_scores, int stride) {
+  using Ops = KeyOps<T>;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int c = lane & 15;      // chunk within a metadata row
   const int slot = lane >> 4;   // which of the wave's 4 pages
-  const int L = seq_lens[b];
-  const int n = L > 0 ? min((L + kPage - 1) / kPage, stride) : 0;
   const int base_j = blockIdx.x * kScorePagesPerBlock;
-  if (base_j >= stride) return;
-  const char* mrow_base = reinterpret_cast<const char*>(meta) + ((size_t)b * Hkv + h) * stride * 512;
+  char* mrow_base = reinterpret_cast<char*>(meta) + ((size_t)b * Hkv + h) * stride * 512;
 
+  // Metadata loads first (any j < stride is in bounds), then the row length.
+  constexpr int kSteps = kScorePagesPerBlock / 16;
+  uint4 mrow[kSteps], Mrow[kSteps];
+  int jj[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    jj[s] = base_j + s * 16 + wave * 4 + slot;
+    if (jj[s] < stride) {
+      const char* rec = mrow_base + (size_t)jj[s] * 512;
+      mrow[s] = ld16(rec + c * 16);
+      Mrow[s] = ld16(rec + 256 + c * 16);
+    }
+  }
   // Query chunks of the group's heads, split by sign.
   uint4 qn[G], qp[G];
   const int Hq = Hkv * G;
@@ -46,36 +80,77 @@ __global__ void __launch_bounds__(256) score_kernel(
     uint4 qc = ld16(qrow + c * 16);
     chunk_sign_split(qc, qn[hh], qp[hh], T{});
   }
+  const int L = seq_lens[b];
+  const int n = L > 0 ? min((L + kPage - 1) / kPage, stride) : 0;
 
-  constexpr int kSteps = kScorePagesPerBlock / 16;
-  uint4 mrow[kSteps], Mrow[kSteps];
-  int jj[kSteps];
-  bool ok[kSteps];
+  // Optional refresh of the tail page's metadata (the page a decode step
+  // appends to), by the wave whose slots hold it: min/max of its valid keys,
+  // written back and used for this score.
+  if (refresh_tail && n > 0) {
+    const int jt = n - 1;
+    const int off = jt - base_j;
+    if (off >= 0 && off < kScorePagesPerBlock && ((off & 15) >> 2) == wave) {
+      const int p = page_indices[page_indptr[b] + jt];
+      if (p >= 0 && p < num_phys) {
+        const int valid = min(kPage, L - kPage * jt);
+        const char* src = reinterpret_cast<const char*>(k_pool) + ((size_t)p * Hkv + h) * kTileBytes;
+        uint4 rows[4];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    jj[s] = base_j + s * 16 + wave * 4 + slot;
-    ok[s] = jj[s] < n;
-    if (ok[s]) {
-      const char* rec = mrow_base + (size_t)jj[s] * 512;
-      mrow[s] = ld16(rec + c * 16);
-      Mrow[s] = ld16(rec + 256 + c * 16);
+        for (int r = 0; r < 4; ++r) rows[r] = ld16(src + r * 1024 + lane * 16);
+        uint32_t mn[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+        uint32_t mx[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (4 * r + (lane >> 4) < valid) {
+            const uint32_t* w = reinterpret_cast<const uint32_t*>(&rows[r]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t kk = Ops::key(w[e]);
+              mn[e] = Ops::vmin(mn[e], kk);
+              mx[e] = Ops::vmax(mx[e], kk);
+            }
+          }
+        }
+        // after this every lane holds the page's min/max of chunk lane % 16
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mn[e] = Ops::vmin(mn[e], xshfl_u(mn[e], 16));
+          mx[e] = Ops::vmax(mx[e], xshfl_u(mx[e], 16));
+          mn[e] = Ops::vmin(mn[e], xshfl_u(mn[e], 32));
+          mx[e] = Ops::vmax(mx[e], xshfl_u(mx[e], 32));
+        }
+        const uint4 vmn = make_uint4(Ops::unkey(mn[0]), Ops::unkey(mn[1]), Ops::unkey(mn[2]), Ops::unkey(mn[3]));
+        const uint4 vmx = make_uint4(Ops::unkey(mx[0]), Ops::unkey(mx[1]), Ops::unkey(mx[2]), Ops::unkey(mx[3]));
+        if (lane < 32) st16(mrow_base + (size_t)jt * 512 + (lane >> 4) * 256 + c * 16, lane < 16 ? vmn : vmx);
+        const int st = off >> 4;
+        if (slot == (off & 3)) {
+#pragma unroll
+          for (int s = 0; s < kSteps; ++s)
+            if (s == st) {
+              mrow[s] = vmn;
+              Mrow[s] = vmx;
+            }
+        }
+      }
     }
   }
+
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     const int j = jj[s];
     if (j >= stride) continue;
+    const bool ok = j < n;
     float hs[G];
     float gmax = -__builtin_inff();
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       float acc = 0.0f;
-      if (ok[s]) {
+      if (ok) {
         acc = chunk_dot(qn[hh], mrow[s], acc, T{});
         acc = chunk_dot(qp[hh], Mrow[s], acc, T{});
       }
       acc = sum16(acc);
-      hs[hh] = ok[s] ? acc : -__builtin_inff();
+      hs[hh] = ok ? acc : -__builtin_inff();
       gmax = fmaxf(gmax, hs[hh]);
     }
     if (c == 0) group_scores[((size_t)b * Hkv + h) * stride + j] = gmax;
@@ -89,15 +164,17 @@ __global__ void __launch_bounds__(256) score_kernel(
 }
 
 template <typename T>
-hipError_t launch_score_t(const LaunchCommon& c, const void* q, const void* meta, float* gs,
-                          float* hs, int stride, hipStream_t stream) {
+hipError_t launch_score_t(const LaunchCommon& c, const void* q, void* meta, int refresh_tail,
+                          float* gs, float* hs, int stride, hipStream_t stream) {
   dim3 grid((stride + kScorePagesPerBlock - 1) / kScorePagesPerBlock, c.Hkv, c.B);
   const T* qq = static_cast<const T*>(q);
-  const T* mm = static_cast<const T*>(meta);
+  T* mm = static_cast<T*>(meta);
+  const T* kp = static_cast<const T*>(c.k_pool);
 #define QSA_SCORE_CASE(GG)                                                                       \
   case GG:                                                                                       \
     hipLaunchKernelGGL((score_kernel<T, GG>), grid, dim3(256), 0, stream, qq, mm, c.Hkv,      \
-                       c.seq_lens, gs, hs, stride);                                              \
+                       c.seq_lens, c.page_indptr, c.page_indices, kp, c.num_phys, refresh_tail,  \
+                       gs, hs, stride);                                                          \
     break;
   switch (c.G) {
     QSA_SCORE_CASE(1)
@@ -113,10 +190,12 @@ hipError_t launch_score_t(const LaunchCommon& c, const void* q, const void* meta
 
 }  // namespace
 
-hipError_t launch_score(const LaunchCommon& c, const void* q, const void* meta, float* group_scores,
-                        float* head_scores, int stride, hipStream_t stream) {
-  return c.bf16 ? launch_score_t<bf16s>(c, q, meta, group_scores, head_scores, stride, stream)
-                : launch_score_t<float>(c, q, meta, group_scores, head_scores, stride, stream);
+hipError_t launch_score(const LaunchCommon& c, const void* q, void* meta, int refresh_tail,
+                        float* group_scores, float* head_scores, int stride, hipStream_t stream) {
+  return c.bf16 ? launch_score_t<bf16s>(c, q, meta, refresh_tail, group_scores, head_scores, stride,
+                                        stream)
+                : launch_score_t<float>(c, q, meta, refresh_tail, group_scores, head_scores, stride,
+                                        stream);
 }
 
 }  // namespace qsa

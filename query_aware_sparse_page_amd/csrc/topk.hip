@@ -3,29 +3,184 @@
 // indexer's bottleneck).
 //
 // One workgroup per row. Scores map to order-preserving uint32 keys (-0 folded
-// onto +0). An MSB-first radix select (4 passes of 8 bits, histograms in LDS)
-// finds the K_eff-th largest key T exactly, and how many keys equal to T are
-// still needed (krem). A compaction pass in page order then keeps every page
-// with key > T and the first krem pages with key == T - so ties go to the
-// smaller page index and the output comes out in ascending page order, with
-// the position of a kept page given by two block-wide prefix counts. Keys stay
-// in registers for the whole select (up to 16 per thread, so rows of up to
-// 16384 pages); each wave counts into its own LDS histogram.
+// onto +0), held in registers (each thread a contiguous run of pages; rows of
+// up to 16384 pages). An MSB-first radix select finds the K_eff-th largest
+// key T exactly, and how many keys equal to T are still needed (krem): it
+// starts below the bits that every key shares (from the block min and max)
+// and takes 13 bits per pass with an 8192-bin LDS histogram, so typical fp32
+// scores resolve in two passes. A compaction in page order then keeps every
+// page with key > T and the first krem pages with key == T - ties go to the
+// smaller page index and the output is in ascending page order; each kept
+// page's position comes from one block-wide scan of (greater, equal) counts.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
 
-// Inclusive prefix sum over a wave (ds_bpermute steps of 1..32 lanes).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = __lane_id();
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) { return wave_scan_incl(v); }
+
+// Exclusive prefix sum over the workgroup (thread order); *total gets the
+// sum. Contains barriers: every thread must call it.
+template <int kWaves>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t t = (uint32_t)__builtin_amdgcn_ds_bpermute((lane - d) << 2, (int)v);
-    if (lane >= d) v += t;
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t t = wsum[w];
+    before += (w < wave) ? t : 0u;
+    tot += t;
   }
-  return v;
+  __syncthreads();
+  *total = tot;
+  return before + incl - v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) { return wave_min_u32(v); }
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) { return wave_max_u32(v); }
+
+// Rows of up to 1024 pages: one wave per row (4 rows per workgroup), no
+// workgroup barriers. Lane l owns pages l*kKeys .. l*kKeys + kKeys - 1; the
+// radix select uses 8-bit digits with a per-wave LDS histogram.
+template <int kKeys>
+__global__ void __launch_bounds__(256) topk_wave_kernel(
+    const float* __restrict__ group_scores, int stride, int Hkv, int rows,
+    const int* __restrict__ seq_lens, const int* __restrict__ page_indptr,
+    const int* __restrict__ page_indices, int k, int* __restrict__ sel,
+    int* __restrict__ sel_count, int* __restrict__ sel_phys) {
+  __shared__ uint32_t hist[4][256];
+  __shared__ uint32_t pick[4][2];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row_i = blockIdx.x * 4 + wave;
+  if (row_i >= rows) return;
+  const size_t row = (size_t)row_i;
+  const int b = row_i / Hkv;
+  const float* sc = group_scores + row * stride;
+  int* out = sel + row * k;
+  int* outp = sel_phys ? sel_phys + row * k : nullptr;
+  // scores first (every j < stride is in bounds), then the row length
+  const int j0 = lane * kKeys;
+  float raw[kKeys];
+#pragma unroll
+  for (int i = 0; i < kKeys; ++i) raw[i] = (j0 + i < stride) ? sc[j0 + i] : 0.0f;
+  const int L = seq_lens[b];
+  int n = L > 0 ? (L + kPage - 1) / kPage : 0;
+  n = n < stride ? n : stride;
+  n = n < 64 * kKeys ? n : 64 * kKeys;
+  const int keff = k < n ? k : n;
+  const int* table = page_indices + page_indptr[b];
+  uint32_t* h = hist[wave];
+
+  if (keff == n) {
+    for (int i = lane; i < k; i += 64) {
+      out[i] = i < n ? i : -1;
+      if (outp) outp[i] = i < n ? table[i] : -1;
+    }
+    if (lane == 0) sel_count[row] = keff;
+    return;
+  }
+
+  uint32_t keys[kKeys];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < kKeys; ++i) {
+    const int j = j0 + i;
+    keys[i] = j < n ? score_key(raw[i]) : 0u;
+    if (j < n) {
+      kmin = min(kmin, keys[i]);
+      kmax = max(kmax, keys[i]);
+    }
+  }
+  kmin = wave_min_u(kmin);
+  kmax = wave_max_u(kmax);
+
+  uint32_t krem = (uint32_t)keff;
+  uint32_t T = kmin;
+  const uint32_t diff = kmin ^ kmax;
+  if (diff != 0u) {
+    int shift = 32 - __builtin_clz(diff);
+    uint32_t prefix = (uint32_t)((uint64_t)kmin >> shift);
+    while (shift > 0) {
+      const int nb = shift < 8 ? shift : 8;
+      const int lo = shift - nb;
+      const uint32_t nbins = 1u << nb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[lane * 4 + i] = 0u;
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < kKeys; ++i) {
+        if (j0 + i < n && (uint32_t)((uint64_t)keys[i] >> shift) == prefix)
+          atomicAdd(&h[(keys[i] >> lo) & (nbins - 1u)], 1u);
+      }
+      wave_lds_sync();
+      // lane l scans digits nbins-1 - (4l .. 4l+3), i.e. descending
+      uint32_t cnt[4];
+      uint32_t local = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = lane * 4 + i;
+        cnt[i] = pos < (int)nbins ? h[nbins - 1 - pos] : 0u;
+        local += cnt[i];
+      }
+      uint32_t above = wave_incl_scan(local) - local;
+      if (above < krem && above + local >= krem) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (above < krem && above + cnt[i] >= krem) {
+            pick[wave][0] = nbins - 1u - (uint32_t)(lane * 4 + i);
+            pick[wave][1] = krem - above;
+          }
+          above += cnt[i];
+        }
+      }
+      wave_lds_sync();
+      prefix = (prefix << nb) | pick[wave][0];
+      krem = pick[wave][1];
+      shift = lo;
+      wave_lds_sync();
+    }
+    T = prefix;
+  }
+
+  uint32_t gt_n = 0, eq_n = 0;
+#pragma unroll
+  for (int i = 0; i < kKeys; ++i) {
+    if (j0 + i < n) {
+      gt_n += keys[i] > T ? 1u : 0u;
+      eq_n += keys[i] == T ? 1u : 0u;
+    }
+  }
+  const uint32_t packed = gt_n | (eq_n << 16);
+  const uint32_t excl = wave_incl_scan(packed) - packed;
+  uint32_t gt_before = excl & 0xFFFFu;
+  uint32_t eq_before = excl >> 16;
+#pragma unroll
+  for (int i = 0; i < kKeys; ++i) {
+    const int j = j0 + i;
+    if (j >= n) break;
+    const bool gt = keys[i] > T;
+    const bool eq = keys[i] == T;
+    if (gt || (eq && eq_before < krem)) {
+      const uint32_t pos = gt_before + (eq_before < krem ? eq_before : krem);
+      if (pos < (uint32_t)keff) {
+        out[pos] = j;
+        if (outp) outp[pos] = table[j];
+      }
+    }
+    gt_before += gt ? 1u : 0u;
+    eq_before += eq ? 1u : 0u;
+  }
+  for (int i = keff + lane; i < k; i += 64) {
+    out[i] = -1;
+    if (outp) outp[i] = -1;
+  }
+  if (lane == 0) sel_count[row] = keff;
 }
 
 template <int kThreads, int kKeys>
@@ -34,9 +189,12 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
     const int* __restrict__ page_indptr, const int* __restrict__ page_indices, int k,
     int* __restrict__ sel, int* __restrict__ sel_count, int* __restrict__ sel_phys) {
   constexpr int kWaves = kThreads / 64;
-  constexpr int kBinsPad = 257;  // per-wave histogram; the pad spreads the waves over LDS banks
-  __shared__ uint32_t hist[kWaves * kBinsPad];
-  __shared__ uint32_t wtot[kWaves];
+  constexpr int kRadixBits = 13;
+  constexpr int kBins = 1 << kRadixBits;
+  constexpr int kBinsPerThread = kBins / kThreads;
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t wsum[kWaves];
+  __shared__ uint32_t wmin[kWaves], wmax[kWaves];
   __shared__ uint32_t s_digit, s_krem;
 
   const int tid = threadIdx.x;
@@ -48,6 +206,10 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
   const float* sc = group_scores + row * stride;
   int* out = sel + row * k;
   int* outp = sel_phys ? sel_phys + row * k : nullptr;
+  const int j0 = tid * kKeys;
+  float raw[kKeys];
+#pragma unroll
+  for (int i = 0; i < kKeys; ++i) raw[i] = (j0 + i < stride) ? sc[j0 + i] : 0.0f;
   const int L = seq_lens[b];
   int n = L > 0 ? (L + kPage - 1) / kPage : 0;
   n = n < stride ? n : stride;
@@ -65,75 +227,103 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
     return;
   }
 
-  // Keys stay in registers: slot i holds page j = tid + i * kThreads.
+  // Keys stay in registers; thread t owns the contiguous pages t*kKeys + i.
   uint32_t keys[kKeys];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int i = 0; i < kKeys; ++i) {
-    const int j = tid + i * kThreads;
-    keys[i] = j < n ? score_key(sc[j]) : 0u;
+    const int j = j0 + i;
+    keys[i] = j < n ? score_key(raw[i]) : 0u;
+    if (j < n) {
+      kmin = min(kmin, keys[i]);
+      kmax = max(kmax, keys[i]);
+    }
+  }
+  kmin = wave_min_u(kmin);
+  kmax = wave_max_u(kmax);
+  if (lane == 0) {
+    wmin[wave] = kmin;
+    wmax[wave] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    kmin = min(kmin, wmin[w]);
+    kmax = max(kmax, wmax[w]);
   }
 
-  uint32_t prefix = 0, mask = 0, krem = (uint32_t)keff;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < kWaves * kBinsPad; i += kThreads) hist[i] = 0;
-    __syncthreads();
+  // Radix select of the keff-th largest key T, MSB first, starting below the
+  // bits every key shares; krem = how many keys equal to T are taken.
+  uint32_t krem = (uint32_t)keff;
+  uint32_t T = kmin;
+  const uint32_t diff = kmin ^ kmax;
+  // digit width: about log2(n) + 2 bits, so the histogram stays small for
+  // short rows and a pass splits a long row finely
+  const int width = min(kRadixBits, max(4, 34 - __builtin_clz((uint32_t)n)));
+  if (diff != 0u) {
+    int shift = 32 - __builtin_clz(diff);          // bits below `shift` still open
+    uint32_t prefix = (uint32_t)((uint64_t)kmin >> shift);
+    while (shift > 0) {
+      const int nb = shift < width ? shift : width;
+      const int lo = shift - nb;
+      const uint32_t nbins = 1u << nb;
+      for (int i = tid; i < (int)nbins; i += kThreads) hist[i] = 0u;
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kKeys; ++i) {
-      const int j = tid + i * kThreads;
-      if (j < n && (keys[i] & mask) == prefix)
-        atomicAdd(&hist[wave * kBinsPad + ((keys[i] >> shift) & 0xFFu)], 1u);
-    }
-    __syncthreads();
-    // Thread t < 256 owns digit 255 - t, so an inclusive scan over t counts
-    // the keys whose digit is >= that digit.
-    uint32_t v = 0, incl = 0;
-    if (tid < 256) {
-      const int d = 255 - tid;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += hist[w * kBinsPad + d];
-      incl = wave_incl_scan(v);
-      if (lane == 63) wtot[wave] = incl;
-    }
-    __syncthreads();
-    if (tid < 256) {
-      for (int w = 0; w < wave; ++w) incl += wtot[w];
-      const uint32_t above = incl - v;  // keys with a larger digit
-      if (above < krem && incl >= krem) {
-        s_digit = 255u - (uint32_t)tid;
-        s_krem = krem - above;
+      for (int i = 0; i < kKeys; ++i) {
+        if (j0 + i < n && (uint32_t)((uint64_t)keys[i] >> shift) == prefix)
+          atomicAdd(&hist[(keys[i] >> lo) & (nbins - 1u)], 1u);
       }
+      __syncthreads();
+      // thread t scans digits nbins-1 - (t*B .. t*B+B-1), i.e. descending
+      uint32_t cnt[kBinsPerThread];
+      uint32_t local = 0;
+#pragma unroll
+      for (int i = 0; i < kBinsPerThread; ++i) {
+        const int pos = tid * kBinsPerThread + i;
+        cnt[i] = pos < (int)nbins ? hist[nbins - 1 - pos] : 0u;
+        local += cnt[i];
+      }
+      uint32_t total;
+      uint32_t above = block_excl_scan<kWaves>(local, wsum, &total);
+      if (above < krem && above + local >= krem) {
+#pragma unroll
+        for (int i = 0; i < kBinsPerThread; ++i) {
+          if (above < krem && above + cnt[i] >= krem) {
+            s_digit = nbins - 1u - (uint32_t)(tid * kBinsPerThread + i);
+            s_krem = krem - above;
+          }
+          above += cnt[i];
+        }
+      }
+      __syncthreads();
+      prefix = (prefix << nb) | s_digit;
+      krem = s_krem;
+      shift = lo;
+      __syncthreads();
     }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    mask |= 0xFFu << shift;
-    krem = s_krem;
-    __syncthreads();
+    T = prefix;
   }
-  const uint32_t T = prefix;
 
-  // Compaction in page order: round i covers pages i*kThreads .. +kThreads.
-  uint32_t gt_base = 0, eq_base = 0;
+  // Compaction in page order: one block scan of (greater, equal) counts.
+  uint32_t gt_n = 0, eq_n = 0;
 #pragma unroll
   for (int i = 0; i < kKeys; ++i) {
-    if (i * kThreads >= n) break;
-    const int j = tid + i * kThreads;
-    const uint32_t key = keys[i];
-    const uint32_t gt = (j < n && key > T) ? 1u : 0u;
-    const uint32_t eq = (j < n && key == T) ? 1u : 0u;
-    const uint32_t packed = gt | (eq << 16);
-    uint32_t incl = wave_incl_scan(packed);
-    if (lane == 63) wtot[wave] = incl;
-    __syncthreads();
-    uint32_t before = 0, total = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      const uint32_t t = wtot[w];
-      if (w < wave) before += t;
-      total += t;
+    if (j0 + i < n) {
+      gt_n += keys[i] > T ? 1u : 0u;
+      eq_n += keys[i] == T ? 1u : 0u;
     }
-    const uint32_t excl = before + incl - packed;
-    const uint32_t gt_before = gt_base + (excl & 0xFFFFu);
-    const uint32_t eq_before = eq_base + (excl >> 16);
+  }
+  uint32_t total;
+  const uint32_t excl = block_excl_scan<kWaves>(gt_n | (eq_n << 16), wsum, &total);
+  uint32_t gt_before = excl & 0xFFFFu;
+  uint32_t eq_before = excl >> 16;
+#pragma unroll
+  for (int i = 0; i < kKeys; ++i) {
+    const int j = j0 + i;
+    if (j >= n) break;
+    const bool gt = keys[i] > T;
+    const bool eq = keys[i] == T;
     if (gt || (eq && eq_before < krem)) {
       const uint32_t pos = gt_before + (eq_before < krem ? eq_before : krem);
       if (pos < (uint32_t)keff) {
@@ -141,9 +331,8 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
         if (outp) outp[pos] = table[j];
       }
     }
-    gt_base += total & 0xFFFFu;
-    eq_base += total >> 16;
-    __syncthreads();
+    gt_before += gt ? 1u : 0u;
+    eq_before += eq ? 1u : 0u;
   }
   for (int i = keff + tid; i < k; i += kThreads) {
     out[i] = -1;
@@ -157,9 +346,15 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
 hipError_t launch_topk(const LaunchCommon& c, const float* group_scores, int stride, int k,
                        int* sel, int* sel_count, int* sel_phys, hipStream_t stream) {
   dim3 grid(c.Hkv, c.B);
-  if (stride <= 256 * 4) {
-    hipLaunchKernelGGL((topk_kernel<256, 4>), grid, dim3(256), 0, stream, group_scores, stride,
-                       c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, k, sel, sel_count, sel_phys);
+  const int rows = c.B * c.Hkv;
+  if (stride <= 64 * 4) {
+    hipLaunchKernelGGL((topk_wave_kernel<4>), dim3((rows + 3) / 4), dim3(256), 0, stream,
+                       group_scores, stride, c.Hkv, rows, c.seq_lens, c.page_indptr, c.page_indices,
+                       k, sel, sel_count, sel_phys);
+  } else if (stride <= 64 * 16) {
+    hipLaunchKernelGGL((topk_wave_kernel<16>), dim3((rows + 3) / 4), dim3(256), 0, stream,
+                       group_scores, stride, c.Hkv, rows, c.seq_lens, c.page_indptr, c.page_indices,
+                       k, sel, sel_count, sel_phys);
   } else if (stride <= 1024 * 8) {
     hipLaunchKernelGGL((topk_kernel<1024, 8>), grid, dim3(1024), 0, stream, group_scores, stride,
                        c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, k, sel, sel_count, sel_phys);

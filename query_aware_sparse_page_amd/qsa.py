@@ -50,7 +50,7 @@ def lib():
         D, KV = ctypes.POINTER(Dims), ctypes.POINTER(PagedKVStruct)
         sig = {
             "qsa_build_page_meta": (i32, [D, KV, i32, vp, i32, vp]),
-            "qsa_score_pages": (i32, [D, vp, KV, vp, vp, vp, i32, vp]),
+            "qsa_score_pages": (i32, [D, vp, KV, vp, vp, vp, i32, i32, vp]),
             "qsa_topk_pages": (i32, [D, KV, vp, i32, i32, vp, vp, vp, vp, sz, vp]),
             "qsa_paged_decode": (i32, [D, vp, KV, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
             "qsa_cascade_decode": (i32, [D, vp, vp, i32, KV, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
@@ -153,16 +153,18 @@ def build_page_meta(kv: PagedKV, meta: Optional[torch.Tensor] = None, tail_pages
 
 
 def score_pages(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor,
-                head_scores: bool = False, out: Optional[torch.Tensor] = None):
+                head_scores: bool = False, out: Optional[torch.Tensor] = None,
+                refresh_tail: bool = False):
     """Scores [B, Hkv, stride] (and per-head [B, Hq, stride]) with the
-    metadata's stride."""
+    metadata's stride; refresh_tail also rebuilds (and writes) each
+    sequence's last-page metadata first."""
     B, Hq, _ = q.shape
     stride = int(meta.shape[2])
     gs = out if out is not None else torch.empty(B, kv.num_kv_heads, stride, dtype=torch.float32, device=q.device)
     hs = torch.empty(B, Hq, stride, dtype=torch.float32, device=q.device) if head_scores else None
     d, s = kv.dims(Hq), kv.struct()
     _check(lib().qsa_score_pages(ctypes.byref(d), _ptr(q), ctypes.byref(s), _ptr(meta), _ptr(gs), _ptr(hs),
-                                 stride, _stream()))
+                                 stride, int(refresh_tail), _stream()))
     return gs, hs
 
 
@@ -208,7 +210,7 @@ def paged_decode(q: torch.Tensor, kv: PagedKV, sel: Optional[torch.Tensor] = Non
     lse = (out[1] if out is not None else torch.empty(B, Hq, dtype=torch.float32, device=q.device)) if with_lse else None
     need = decode_workspace_size(kv, Hq, k)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     d, s = kv.dims(Hq), kv.struct()
     _check(lib().qsa_paged_decode(ctypes.byref(d), _ptr(q), ctypes.byref(s), _ptr(sel), _ptr(sel_count), k,
                                   ctypes.c_float(sm_scale), _ptr(o), _ptr(lse), _ptr(workspace),
@@ -232,7 +234,7 @@ def cascade_decode(q: torch.Tensor, prefix_pages: torch.Tensor, prefix_len: int,
     lse = (out[1] if out is not None else torch.empty(B, Hq, dtype=torch.float32, device=q.device)) if with_lse else None
     need = cascade_workspace_size(kv, Hq, prefix_len, k)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     d, s = kv.dims(Hq), kv.struct()
     _check(lib().qsa_cascade_decode(ctypes.byref(d), _ptr(q), _ptr(prefix_pages), prefix_len, ctypes.byref(s),
                                     _ptr(sel), _ptr(sel_count), k, ctypes.c_float(sm_scale), _ptr(o), _ptr(lse),

@@ -59,13 +59,13 @@ def test_validation_errors_return_before_any_device_work(L):
     st = L.qsa_paged_decode(None, None, None, None, None, 0, ctypes.c_float(1.0), None, None, None, 0, None)
     assert st == qsa.QSA_ERR_INVALID_ARG and b"dims" in L.qsa_last_error()
     bad = _dims(Hq=30)
-    st = L.qsa_score_pages(ctypes.byref(bad), None, None, None, None, None, 1, None)
+    st = L.qsa_score_pages(ctypes.byref(bad), None, None, None, None, None, 1, 0, None)
     assert st == qsa.QSA_ERR_INVALID_ARG and b"multiple" in L.qsa_last_error()
-    st = L.qsa_score_pages(ctypes.byref(_dims(D=96)), None, None, None, None, None, 1, None)
+    st = L.qsa_score_pages(ctypes.byref(_dims(D=96)), None, None, None, None, None, 1, 0, None)
     assert st == qsa.QSA_ERR_UNSUPPORTED
-    st = L.qsa_score_pages(ctypes.byref(_dims(ps=32)), None, None, None, None, None, 1, None)
+    st = L.qsa_score_pages(ctypes.byref(_dims(ps=32)), None, None, None, None, None, 1, 0, None)
     assert st == qsa.QSA_ERR_UNSUPPORTED
-    st = L.qsa_score_pages(ctypes.byref(_dims(Hq=48, Hkv=4)), None, None, None, None, None, 1, None)
+    st = L.qsa_score_pages(ctypes.byref(_dims(Hq=48, Hkv=4)), None, None, None, None, None, 1, 0, None)
     assert st == qsa.QSA_ERR_UNSUPPORTED                  # group size 12
     st = L.qsa_topk_pages(ctypes.byref(d), None, None, 1, 1, None, None, None, None, 0, None)
     assert st == qsa.QSA_ERR_INVALID_ARG

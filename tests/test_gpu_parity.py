@@ -86,6 +86,46 @@ def test_meta_tail_update_and_signed_zero():
                 assert np.array_equal(tb[b, :, j], jb[b, :, j])
 
 
+def test_score_refresh_tail_fused():
+    # Stale tail metadata is rebuilt inside the score launch (bit-exact) and
+    # the scores use it.
+    c = _case("refresh", [1000, 1537, 700, 16, 17, 1], 8, 2, plant_pages=2)
+    d = case_np(c)
+    g, kv = _kv(c)
+    stride = kv.max_pages() + 1
+    meta = qsa.build_page_meta(kv, stride=stride)
+    ns = [-(-L // 16) for L in c.seq_lens_list()]
+    for b, n in enumerate(ns):
+        meta[b, :, n - 1] = 3.0                      # stale tail record
+    gs, hs = qsa.score_pages(g.q, kv, meta, head_scores=True, refresh_tail=True)
+    torch.cuda.synchronize()
+    ometa, ohead, ogroup = _oracle_scores(c, d, stride)
+    got = np_store(meta)
+    qv = O.values_f64(d["q"], "bf16")
+    mv = O.values_f64(ometa, "bf16")
+    hs_n = hs.cpu().numpy()
+    for b, n in enumerate(ns):
+        for j in range(n):
+            p = O.physical_page(d["page_indptr"], d["page_indices"], b, j)
+            assert np.array_equal(got[b, :, j], ometa[p]), (b, j)
+            for hq in range(8):
+                tol = score_tol(qv[b, hq], mv[p, hq // 4, 0], mv[p, hq // 4, 1])
+                assert abs(float(hs_n[b, hq, j]) - float(ohead[b, hq, j])) <= tol
+
+
+def test_decode_workspace_garbage_is_harmless_and_repeatable():
+    # The merge must ignore workspace slots a row does not own (stale or NaN).
+    c = _case("ws", [1000, 1537, 700, 16], 8, 2)
+    g, kv = _kv(c)
+    need = qsa.decode_workspace_size(kv, 8, 0)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=DEV).view(torch.uint8)
+    o1, l1 = qsa.paged_decode(g.q, kv, sm_scale=c.sm_scale, workspace=ws)
+    o2, l2 = qsa.paged_decode(g.q, kv, sm_scale=c.sm_scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1).all() and torch.isfinite(l1).all()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def _oracle_scores(c, d, stride):
     meta = O.build_page_meta(d["k_pool"], c.dtype, d["page_indptr"], d["page_indices"], d["seq_lens"])
     head, group = O.score_pages(d["q"], c.dtype, meta, c.dtype, d["page_indptr"], d["page_indices"],
