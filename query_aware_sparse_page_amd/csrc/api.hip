@@ -7,7 +7,7 @@
 #include <cstdlib>
 #include <string>
 
-#include "../../include/qsa.h"
+#include "qsa.h"
 #include "qsa_internal.h"
 
 namespace {
