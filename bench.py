@@ -2,9 +2,12 @@
 """Benchmark: sparse paged decode with query-aware page selection on one GPU.
 
 A step is one pass of the whole hot path over one batch of decode queries:
-  tail-page metadata refresh + upper-bound page scores (one launch) -> top-K
-  pages -> split-K flash-decode over the selected pages with the log-sum-exp
-  merge fused in (dense configurations: the decode alone).
+  tail-page metadata refresh + upper-bound page scores -> top-K pages ->
+  flash-decode over the selected pages with the log-sum-exp merge (dense
+  configurations: the decode alone). Sparse steps go through one
+  qsa_sparse_decode call, whose fused path runs all of it in one launch (one
+  workgroup per (sequence, KV head) row) and whose split path runs the
+  separate score, top-K, split-K decode and merge kernels.
 The default workload is the sparse-decode configuration (batch 16, GQA 32/8,
 head_dim 128, 8192-token contexts, 153-page budget, bf16). Inputs are seeded
 synthetic data resident in HBM before timing starts. Steps rotate over
@@ -14,7 +17,7 @@ last-level cache.
 Prints one JSON line (see --help). Timed region 1 (the reported value)
 replays the steps as a HIP graph; timed region 2 launches the same calls
 eagerly with HIP events between the stages, giving the per-stage times and
-the decode kernel's roofline. The CPU oracle is timed on a bounded sample.
+the dominant kernel's roofline. The CPU oracle is timed on a bounded sample.
 """
 import argparse
 import json
@@ -30,6 +33,32 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse paged decode: queries/s and effective KV HBM GB/s vs MI355X peak"
 PEAK_HBM_GBPS = 8000.0
 
+# HBM bytes per launch of the dominant kernel, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs scaled by a plain 256 MiB copy (FETCH_SIZE x 2.0,
+# WRITE_SIZE x 1.0; see the profiles/ summary named). A figure only holds for
+# the kernel sources it was taken on: their SHA-256 is recorded with it and
+# "traffic" is null when the sources differ.
+MEASURED_TRAFFIC = {
+    ("c2_sparse", "fused"): {
+        "bytes": 195656294,
+        "sources": ["sparse_row.hip", "decode_wave.h", "qsa_device.h", "qsa_internal.h"],
+        "sha256_16": "0e6f530c830703ff",
+        "profile": "profiles/sparse_row_kernel_c2_sparse.md",
+    },
+}
+
+
+def measured_traffic(config, path):
+    import hashlib
+    rec = MEASURED_TRAFFIC.get((config, path))
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, "query_aware_sparse_page_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return rec["bytes"] if h.hexdigest()[:16] == rec["sha256_16"] else None
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -39,6 +68,8 @@ def parse():
     ap.add_argument("--config", default="c2_sparse",
                     choices=["c2_sparse", "c3_dense", "c4_long", "c5_cascade"])
     ap.add_argument("--replicas", type=int, default=4, help="KV pool copies rotated over steps")
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "split"],
+                    help="kernels of a sparse step (auto: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
@@ -121,6 +152,8 @@ def main():
         ws_bytes = qsa.decode_workspace_size(kvs[0], Hq, k or 0)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
+    path = qsa.sparse_decode_path(kvs[0], Hq, stride, k, args.path) if (k and not cascade) else None
+
     def stage_score(r):
         # scores with the tail page's metadata refreshed in the same launch
         qsa.score_pages(case.q, kvs[r], metas[r], out=gs, refresh_tail=True)
@@ -137,10 +170,16 @@ def main():
             qsa.paged_decode(case.q, kvs[r], sel=s, sel_count=c, sm_scale=case.sm_scale, workspace=ws,
                              out=(out, lse))
 
-    stages = []
-    if k:
-        stages += [("score+meta_tail", stage_score), ("topk", stage_topk)]
-    stages += [("decode", stage_decode)]
+    def stage_fused(r):
+        qsa.sparse_decode(case.q, kvs[r], metas[r], k, sm_scale=case.sm_scale, refresh_tail=True, path="fused",
+                          out=(out, lse))
+
+    if path == "fused":
+        stages = [("sparse_decode_fused", stage_fused)]
+    elif k:
+        stages = [("score+meta_tail", stage_score), ("topk", stage_topk), ("decode", stage_decode)]
+    else:
+        stages = [("decode", stage_decode)]
 
     def step(i):
         r = i % R
@@ -218,20 +257,27 @@ def main():
     eager_step_ms = sum(v["mean"] for v in stage_ms.values())
 
     # ---- byte accounting (algorithmic)
+    dec = accounting.decode_bytes(lens, Hq, Hkv, D, elem, k=k)
     if cascade:
-        dec = accounting.decode_bytes(lens, Hq, Hkv, D, elem, k=k)
         pre_kv = case.prefix_len * Hkv * D * 2 * elem
         dec["kv"] += pre_kv
         dec["total"] += pre_kv
+    if path == "fused":
+        fz = accounting.fused_step_bytes(lens, Hq, Hkv, D, elem, k)
+        step_bytes = fz["total"]
+        dom_name, dom_bytes = "sparse_decode_fused", fz["total"]
+        dom_kernel = "sparse_row_kernel (fused scores, top-K, decode and merge; one workgroup per row)"
     else:
-        dec = accounting.decode_bytes(lens, Hq, Hkv, D, elem, k=k)
-    sc = accounting.score_bytes(lens, Hq, Hkv, D, elem) if k else {"total": 0}
-    tk = accounting.topk_bytes(lens, Hkv, k) if k else {"total": 0}
-    mt = accounting.meta_bytes(lens, Hkv, D, elem, tail_pages=1) if k else {"total": 0}
-    step_bytes = dec["total"] + sc["total"] + tk["total"] + mt["total"]
+        sc = accounting.score_bytes(lens, Hq, Hkv, D, elem) if k else {"total": 0}
+        tk = accounting.topk_bytes(lens, Hkv, k) if k else {"total": 0}
+        mt = accounting.meta_bytes(lens, Hkv, D, elem, tail_pages=1) if k else {"total": 0}
+        step_bytes = dec["total"] + sc["total"] + tk["total"] + mt["total"]
+        dom_name, dom_bytes = "decode", dec["total"]
+        dom_kernel = ("cascade prefix (MFMA) + split-K suffix decode + LSE merge" if cascade
+                      else "decode_split_kernel + merge_kernel (split-K paged decode, LSE merge)")
     qps = B / (ms_step / 1e3)
-    dec_ms = stage_ms["decode"]["mean"]
-    achieved = dec["total"] / (dec_ms / 1e3) / 1e9
+    dom_ms = stage_ms[dom_name]["mean"]
+    achieved = dom_bytes / (dom_ms / 1e3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -253,6 +299,7 @@ def main():
                         + (f", shared prefix {case.prefix_len}" if cascade else ""),
             "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": 16,
             "budget_pages": k, "kv_pool_replicas": R, "timing": "hip graph replay" if graph else "eager",
+            "path": path or ("cascade" if cascade else "dense"),
         },
         "effective_kv_gbps": round(dec["kv"] / (ms_step / 1e3) / 1e9, 1),
         "step_algorithmic_gbps": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
@@ -262,15 +309,15 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "graph_replay_matches_eager": graph_matches,
         "roofline": {
-            "kernel": "decode_split_kernel (split-K paged decode, LSE merge fused)",
+            "kernel": dom_kernel,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": None,
-            "algorithmic_bytes_per_launch": dec["total"],
-            "avg_launch_ms": round(dec_ms, 5),
+            "traffic": measured_traffic(args.config, path),
+            "algorithmic_bytes_per_launch": dom_bytes,
+            "avg_launch_ms": round(dom_ms, 5),
         },
     }
 

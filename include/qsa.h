@@ -165,11 +165,53 @@ qsa_status qsa_cascade_decode(const qsa_dims* dims, const void* q,
                               float sm_scale, float* out, float* lse, void* ws,
                               size_t ws_bytes, hipStream_t stream);
 
+/* Steps 2-4 as one call: one decode step of the sparse path (TinyServe §3.2
+ * fuses page scoring, top-K selection and the sparse attention into one
+ * kernel, with the scores kept on chip). Computes exactly what
+ * qsa_score_pages(refresh_tail) -> qsa_topk_pages(k) -> qsa_paged_decode(sel)
+ * compute: the same group scores (equal values; a -0 score may be returned
+ * as +0), the same selection, and
+ * out / lse within fp32 rounding of qsa_paged_decode on that selection.
+ * meta / stride / refresh_tail as in qsa_score_pages (meta is written only
+ * when refresh_tail = 1); k, out, lse as in qsa_topk_pages / qsa_paged_decode.
+ * Optional outputs (each may be NULL): group_scores [B, Hkv, stride] fp32,
+ * sel [B, Hkv, k] int32 (ascending, -1 padded), sel_count [B, Hkv] int32.
+ * path selects the kernels:
+ *   QSA_PATH_FUSED - one workgroup per (b, h) row scores, selects, attends
+ *     and merges in LDS (one launch, no workspace); rows of at most 4096
+ *     pages (max_b n_b <= 4096) with min(k, max_b n_b) <= 512, else
+ *     QSA_ERR_UNSUPPORTED;
+ *   QSA_PATH_SPLIT - the separate score, top-K and split-K decode kernels,
+ *     which spread one row over many workgroups (long rows, few rows);
+ *   QSA_PATH_AUTO - FUSED when supported and B * Hkv >= 64, else SPLIT.
+ * Workspace: qsa_sparse_decode_workspace_size(...) with the same path (0 for
+ * the fused path; ws may then be NULL). */
+typedef enum qsa_path {
+  QSA_PATH_AUTO = 0,
+  QSA_PATH_FUSED = 1,
+  QSA_PATH_SPLIT = 2
+} qsa_path;
+
+qsa_status qsa_sparse_decode(const qsa_dims* dims, const void* q,
+                             const qsa_paged_kv* kv, void* meta, int32_t stride,
+                             int32_t refresh_tail, int32_t k, float sm_scale,
+                             float* out, float* lse, float* group_scores,
+                             int32_t* sel, int32_t* sel_count, qsa_path path,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The kernels qsa_sparse_decode will run for these arguments (QSA_PATH_FUSED
+ * or QSA_PATH_SPLIT), in *chosen. */
+qsa_status qsa_sparse_decode_path(const qsa_dims* dims, const int32_t* seq_lens_host,
+                                  int32_t stride, int32_t k, qsa_path path,
+                                  qsa_path* chosen);
+
 /* Workspace sizes in bytes (0 on invalid arguments). k <= 0 means dense. */
 size_t qsa_topk_workspace_size(const qsa_dims* dims, int32_t max_pages, int32_t k);
 size_t qsa_decode_workspace_size(const qsa_dims* dims, const int32_t* seq_lens_host, int32_t k);
 size_t qsa_cascade_workspace_size(const qsa_dims* dims, int32_t prefix_len,
                                   const int32_t* suffix_lens_host, int32_t k);
+size_t qsa_sparse_decode_workspace_size(const qsa_dims* dims, const int32_t* seq_lens_host,
+                                        int32_t stride, int32_t k, qsa_path path);
 
 /* The decode work split the library will use: pages per work unit and the
  * largest number of units of one (b, h). Returns QSA_ERR_INVALID_ARG on bad

@@ -178,6 +178,40 @@ size_t prefix_ws_bytes(const qsa_dims* d, int prefix_len) {
   return align_up(rows * d->head_dim * sizeof(float)) + align_up(rows * 2 * sizeof(float));
 }
 
+// Rows the fused path wants before it is chosen automatically: with one
+// 8-wave workgroup per row, 64 rows already keep HBM busy at ~5.4 TB/s in a
+// plain tile-streaming test and 128 reach ~6.9 TB/s, while the split path
+// pays three more launches.
+constexpr int kFusedMinRows = 64;
+
+bool fused_supported(int max_pages, int k) {
+  return max_pages <= qsa::kRowMaxPages && std::min(k, max_pages) <= qsa::kRowMaxSelect;
+}
+
+qsa_path choose_path(const qsa_dims* d, int max_pages, int k, qsa_path path) {
+  if (path != QSA_PATH_AUTO) return path;
+  const long long rows = (long long)d->num_seqs * d->num_kv_heads;
+  return (fused_supported(max_pages, k) && rows >= kFusedMinRows) ? QSA_PATH_FUSED : QSA_PATH_SPLIT;
+}
+
+// Split-path workspace of qsa_sparse_decode: [group scores][sel][sel_count]
+// [decode partials], each region 256-byte aligned.
+struct SparseWs {
+  size_t gs = 0, sel = 0, cnt = 0;
+  DecodeWs dec;
+  size_t total() const { return align_up(gs) + align_up(sel) + align_up(cnt) + dec.total(); }
+};
+
+SparseWs sparse_ws(const qsa_dims* d, const int32_t* lens, int stride, int k) {
+  const size_t rows = (size_t)d->num_seqs * d->num_kv_heads;
+  SparseWs w;
+  w.gs = rows * stride * sizeof(float);
+  w.sel = rows * k * sizeof(int32_t);
+  w.cnt = rows * sizeof(int32_t);
+  w.dec = decode_ws(d, make_plan(d, lens, k));
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -359,6 +393,89 @@ qsa_status qsa_cascade_decode(const qsa_dims* dims, const void* q, const int32_t
   e = qsa::launch_decode(c, q, sel, sel_count, kk, scale_log2, plan, part, pre, nsplit, out, lse,
                          stream);
   return device_status(e, "cascade suffix launch");
+}
+
+qsa_status qsa_sparse_decode_path(const qsa_dims* dims, const int32_t* seq_lens_host,
+                                  int32_t stride, int32_t k, qsa_path path, qsa_path* chosen) {
+  qsa_status s = check_dims(dims);
+  if (s != QSA_OK) return s;
+  if (seq_lens_host == nullptr || chosen == nullptr) return fail(QSA_ERR_INVALID_ARG, "NULL argument");
+  if (path != QSA_PATH_AUTO && path != QSA_PATH_FUSED && path != QSA_PATH_SPLIT)
+    return fail(QSA_ERR_INVALID_ARG, "unknown path %d", (int)path);
+  if (k < 1) return fail(QSA_ERR_INVALID_ARG, "k = %d (must be >= 1)", k);
+  int max_pages = 0;
+  for (int b = 0; b < dims->num_seqs; ++b) {
+    if (seq_lens_host[b] < 1) return fail(QSA_ERR_INVALID_ARG, "seq_lens[%d] < 1", b);
+    max_pages = std::max(max_pages, pages_of(seq_lens_host[b]));
+  }
+  if (stride < max_pages)
+    return fail(QSA_ERR_INVALID_ARG, "stride %d < longest sequence's page count %d", stride,
+                max_pages);
+  const qsa_path p = choose_path(dims, max_pages, k, path);
+  if (p == QSA_PATH_FUSED && !fused_supported(max_pages, k))
+    return fail(QSA_ERR_UNSUPPORTED,
+                "fused path: %d pages per row (max %d) and %d selected (max %d)", max_pages,
+                qsa::kRowMaxPages, std::min(k, max_pages), qsa::kRowMaxSelect);
+  if (p == QSA_PATH_SPLIT && stride > qsa::kTopkMaxPages)
+    return fail(QSA_ERR_UNSUPPORTED, "stride %d > %d pages per row", stride, qsa::kTopkMaxPages);
+  *chosen = p;
+  return ok();
+}
+
+size_t qsa_sparse_decode_workspace_size(const qsa_dims* dims, const int32_t* seq_lens_host,
+                                        int32_t stride, int32_t k, qsa_path path) {
+  qsa_path chosen;
+  if (qsa_sparse_decode_path(dims, seq_lens_host, stride, k, path, &chosen) != QSA_OK) return 0;
+  if (chosen == QSA_PATH_FUSED) return 0;
+  return sparse_ws(dims, seq_lens_host, stride, k).total();
+}
+
+qsa_status qsa_sparse_decode(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv, void* meta,
+                             int32_t stride, int32_t refresh_tail, int32_t k, float sm_scale,
+                             float* out, float* lse, float* group_scores, int32_t* sel,
+                             int32_t* sel_count, qsa_path path, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  qsa_status s = check_dims(dims);
+  if (s != QSA_OK) return s;
+  int max_pages = 0;
+  if ((s = check_kv(dims, kv, true, &max_pages)) != QSA_OK) return s;
+  if (q == nullptr || meta == nullptr || out == nullptr)
+    return fail(QSA_ERR_INVALID_ARG, "q/meta/out is NULL");
+  if (refresh_tail != 0 && refresh_tail != 1)
+    return fail(QSA_ERR_INVALID_ARG, "refresh_tail %d (0 or 1)", refresh_tail);
+  if (!std::isfinite(sm_scale)) return fail(QSA_ERR_INVALID_ARG, "sm_scale is not finite");
+  qsa_path chosen;
+  if ((s = qsa_sparse_decode_path(dims, kv->seq_lens_host, stride, k, path, &chosen)) != QSA_OK)
+    return s;
+  const qsa::LaunchCommon c = common(dims, kv);
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  if (chosen == QSA_PATH_FUSED) {
+    return device_status(qsa::launch_sparse_row(c, q, meta, stride, refresh_tail, k, scale_log2, out,
+                                                 lse, group_scores, sel, sel_count, stream),
+                         "sparse_decode (fused) launch");
+  }
+  const SparseWs w = sparse_ws(dims, kv->seq_lens_host, stride, k);
+  if (ws_bytes < w.total() || ws == nullptr)
+    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, w.total());
+  char* base = static_cast<char*>(ws);
+  float* gs = reinterpret_cast<float*>(base);
+  base += align_up(w.gs);
+  int32_t* sl = reinterpret_cast<int32_t*>(base);
+  base += align_up(w.sel);
+  int32_t* cn = reinterpret_cast<int32_t*>(base);
+  base += align_up(w.cnt);
+  if (group_scores != nullptr) gs = group_scores;
+  if (sel != nullptr) sl = sel;
+  if (sel_count != nullptr) cn = sel_count;
+  hipError_t e = qsa::launch_score(c, q, meta, refresh_tail, gs, nullptr, stride, stream);
+  if (e != hipSuccess) return device_status(e, "sparse_decode score launch");
+  e = qsa::launch_topk(c, gs, stride, k, sl, cn, nullptr, stream);
+  if (e != hipSuccess) return device_status(e, "sparse_decode top-K launch");
+  const qsa::DecodePlan plan = make_plan(dims, kv->seq_lens_host, k);
+  const qsa::Partials part = carve(base, w.dec);
+  return device_status(qsa::launch_decode(c, q, sl, cn, k, scale_log2, plan, part, qsa::Partials{},
+                                          0, out, lse, stream),
+                       "sparse_decode decode launch");
 }
 
 }  // extern "C"

@@ -129,6 +129,25 @@ __device__ __forceinline__ uint32_t umax2x16(uint32_t a, uint32_t b) {
                                                                  __builtin_bit_cast(u16x2_t, b)));
 }
 
+// Order-key operations on one dword of storage (a bf16 pair or one fp32):
+// to key, back, and element-wise min / max of keys.
+template <typename T>
+struct KeyOps;
+template <>
+struct KeyOps<bf16s> {
+  static __device__ __forceinline__ uint32_t key(uint32_t x) { return bf2_to_key(x); }
+  static __device__ __forceinline__ uint32_t unkey(uint32_t k) { return key_to_bf2(k); }
+  static __device__ __forceinline__ uint32_t vmin(uint32_t a, uint32_t b) { return umin2x16(a, b); }
+  static __device__ __forceinline__ uint32_t vmax(uint32_t a, uint32_t b) { return umax2x16(a, b); }
+};
+template <>
+struct KeyOps<float> {
+  static __device__ __forceinline__ uint32_t key(uint32_t x) { return f32_to_key(x); }
+  static __device__ __forceinline__ uint32_t unkey(uint32_t k) { return key_to_f32(k); }
+  static __device__ __forceinline__ uint32_t vmin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+  static __device__ __forceinline__ uint32_t vmax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+};
+
 // Score -> ascending uint32 key; -0 is folded onto +0 so equal values tie.
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = (s == 0.0f) ? 0u : __float_as_uint(s);
@@ -197,6 +216,27 @@ __device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
   return v;
 }
 
+// Exclusive prefix sum over the workgroup (thread order); *total gets the
+// sum. Contains barriers: every thread must call it.
+template <int kWaves>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_scan_incl(v);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t t = wsum[w];
+    before += (w < wave) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + incl - v;
+}
+
 template <int kCtrl>
 __device__ __forceinline__ uint32_t dpp_full_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xF, 0xF, true);
@@ -232,6 +272,43 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Element-wise min and max of the first `valid` key rows of one (page, KV
+// head) tile (16 rows x 256 B), exact (order keys, -0 < +0). Each load reads
+// 1 KiB contiguous: lane l holds chunk l%16 of rows {l/16, 4 + l/16, 8 + l/16,
+// 12 + l/16}; after the in-lane reduction lanes l, l^16, l^32, l^48 combine,
+// so on return every lane holds the tile's min / max of chunk l%16.
+template <typename T>
+__device__ __forceinline__ void tile_minmax(const char* tile, int valid, int lane, uint4& vmn,
+                                            uint4& vmx) {
+  using Ops = KeyOps<T>;
+  uint4 rows[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) rows[r] = ld16(tile + r * 1024 + lane * 16);
+  uint32_t mn[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  uint32_t mx[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (4 * r + (lane >> 4) < valid) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(&rows[r]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kk = Ops::key(w[e]);
+        mn[e] = Ops::vmin(mn[e], kk);
+        mx[e] = Ops::vmax(mx[e], kk);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    mn[e] = Ops::vmin(mn[e], xshfl_u(mn[e], 16));
+    mx[e] = Ops::vmax(mx[e], xshfl_u(mx[e], 16));
+    mn[e] = Ops::vmin(mn[e], xshfl_u(mn[e], 32));
+    mx[e] = Ops::vmax(mx[e], xshfl_u(mx[e], 32));
+  }
+  vmn = make_uint4(Ops::unkey(mn[0]), Ops::unkey(mn[1]), Ops::unkey(mn[2]), Ops::unkey(mn[3]));
+  vmx = make_uint4(Ops::unkey(mx[0]), Ops::unkey(mx[1]), Ops::unkey(mx[2]), Ops::unkey(mx[3]));
 }
 
 // Orders this wave's LDS accesses before and after the call point (all lanes

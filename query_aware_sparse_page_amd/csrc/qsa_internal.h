@@ -53,6 +53,16 @@ hipError_t launch_decode(const LaunchCommon& c, const void* q, const int* sel, c
                          Partials prefix, int n_prefix, float* out, float* lse,
                          hipStream_t stream);
 
+// Fused per-row sparse decode step (score -> top-K -> attention -> merge in
+// one workgroup per (b, h) row). Rows of at most kRowMaxPages pages, at most
+// kRowMaxSelect selected pages.
+constexpr int kRowMaxPages = 4096;
+constexpr int kRowMaxSelect = 512;
+
+hipError_t launch_sparse_row(const LaunchCommon& c, const void* q, void* meta, int stride,
+                             int refresh_tail, int k, float scale_log2, float* out, float* lse,
+                             float* group_scores, int* sel, int* sel_count, hipStream_t stream);
+
 // Cascade prefix on the matrix cores (bf16, D = 128): partials per
 // (KV head, split, query row).
 hipError_t launch_cascade_prefix(const LaunchCommon& c, const void* q, const int* prefix_pages,

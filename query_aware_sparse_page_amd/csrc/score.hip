@@ -25,30 +25,12 @@ namespace {
 
 constexpr int kScorePagesPerBlock = 64;
 
-template <typename T>
-struct KeyOps;
-template <>
-struct KeyOps<bf16s> {
-  static __device__ __forceinline__ uint32_t key(uint32_t x) { return bf2_to_key(x); }
-  static __device__ __forceinline__ uint32_t unkey(uint32_t k) { return key_to_bf2(k); }
-  static __device__ __forceinline__ uint32_t vmin(uint32_t a, uint32_t b) { return umin2x16(a, b); }
-  static __device__ __forceinline__ uint32_t vmax(uint32_t a, uint32_t b) { return umax2x16(a, b); }
-};
-template <>
-struct KeyOps<float> {
-  static __device__ __forceinline__ uint32_t key(uint32_t x) { return f32_to_key(x); }
-  static __device__ __forceinline__ uint32_t unkey(uint32_t k) { return key_to_f32(k); }
-  static __device__ __forceinline__ uint32_t vmin(uint32_t a, uint32_t b) { return a < b ? a : b; }
-  static __device__ __forceinline__ uint32_t vmax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-};
-
 template <typename T, int G>
 __global__ void __launch_bounds__(256) score_kernel(
     const T* __restrict__ q, T* __restrict__ meta, int Hkv, const int* __restrict__ seq_lens,
     const int* __restrict__ page_indptr, const int* __restrict__ page_indices,
     const T* __restrict__ k_pool, int num_phys, int refresh_tail,
     float* __restrict__ group_scores, float* __restrict__ head_scores, int stride) {
-  using Ops = KeyOps<T>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.y;
@@ -94,33 +76,8 @@ __global__ void __launch_bounds__(256) score_kernel(
       if (p >= 0 && p < num_phys) {
         const int valid = min(kPage, L - kPage * jt);
         const char* src = reinterpret_cast<const char*>(k_pool) + ((size_t)p * Hkv + h) * kTileBytes;
-        uint4 rows[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rows[r] = ld16(src + r * 1024 + lane * 16);
-        uint32_t mn[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-        uint32_t mx[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (4 * r + (lane >> 4) < valid) {
-            const uint32_t* w = reinterpret_cast<const uint32_t*>(&rows[r]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t kk = Ops::key(w[e]);
-              mn[e] = Ops::vmin(mn[e], kk);
-              mx[e] = Ops::vmax(mx[e], kk);
-            }
-          }
-        }
-        // after this every lane holds the page's min/max of chunk lane % 16
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          mn[e] = Ops::vmin(mn[e], xshfl_u(mn[e], 16));
-          mx[e] = Ops::vmax(mx[e], xshfl_u(mx[e], 16));
-          mn[e] = Ops::vmin(mn[e], xshfl_u(mn[e], 32));
-          mx[e] = Ops::vmax(mx[e], xshfl_u(mx[e], 32));
-        }
-        const uint4 vmn = make_uint4(Ops::unkey(mn[0]), Ops::unkey(mn[1]), Ops::unkey(mn[2]), Ops::unkey(mn[3]));
-        const uint4 vmx = make_uint4(Ops::unkey(mx[0]), Ops::unkey(mx[1]), Ops::unkey(mx[2]), Ops::unkey(mx[3]));
+        uint4 vmn, vmx;
+        tile_minmax<T>(src, valid, lane, vmn, vmx);
         if (lane < 32) st16(mrow_base + (size_t)jt * 512 + (lane >> 4) * 256 + c * 16, lane < 16 ? vmn : vmx);
         const int st = off >> 4;
         if (slot == (off & 3)) {

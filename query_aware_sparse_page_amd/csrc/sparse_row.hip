@@ -1,0 +1,418 @@
+// Steps 2-4 of one decode step fused into one workgroup per (sequence, KV
+// head) row: bound scores, top-K and attention over the selected pages, with
+// the scores, the selection and the partial results kept in LDS (TinyServe
+// page, §3.2: one kernel per decode step that scores pages, picks the top-K and
+// attends over them, with the scores held on chip; the score is §2.2, the
+// selection §2.3, the per-page attention decode_wave.h).
+//
+// Workgroup = 8 waves. Phases, separated by workgroup barriers:
+//  1. Score: the row's metadata is one contiguous stream of 512-byte [m | M]
+//     records (logical page order). 16 lanes per page, 4 pages per wave-step,
+//     32 pages per workgroup-step; records are loaded four steps ahead
+//     (double-buffered batches). The score arithmetic is the same as
+//     score_kernel's (q split by sign, v_dot2 / fma, DPP sum, group max), so
+//     both paths produce bit-identical group scores. With refresh_tail set the
+//     wave owning the tail page rebuilds its min/max from the keys first and
+//     writes it back. The row's page table is copied to LDS on the way.
+//  2. Select: MSB-first radix select on the order-preserving keys of the
+//     scores in LDS (8-bit digits, starting below the bits shared by the row's
+//     min and max key; it stops as soon as the boundary digit's bin is taken
+//     whole), then a compaction in page order: pages with key above the
+//     threshold, plus the first ones equal to it (ties go to the smaller
+//     logical page). The list is in ascending page order.
+//  3. Attend: wave w takes list entries w, w+8, ... through the per-wave
+//     paged attention of decode_wave.h.
+//  4. Merge: the 8 waves' (max, sum, o) are combined by log-sum-exp in LDS and
+//     the normalised output and LSE are written; no partials leave the chip.
+#include "decode_wave.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kRowWaves = 8;
+constexpr int kRowThreads = kRowWaves * kWave;
+constexpr int kKeysPerThread = kRowMaxPages / kRowThreads;
+constexpr int kBatch = 4;  // score steps per load batch
+
+template <typename T, int G>
+struct RowShared {
+  using WA = WaveAttn<T, G>;
+  static constexpr int D = WA::D;
+  union {
+    struct {
+      uint32_t key[kRowMaxPages];  // order keys of the group scores
+      int phys[kRowMaxPages];      // the row's page table
+    } s;
+    struct {
+      float o[kRowWaves][G][D];
+      float ml[kRowWaves][G][2];
+    } c;
+  } u;
+  int list[kRowMaxSelect];  // selected logical pages, ascending
+  uint4 q[WA::kQInLds ? G * kRowBytes / 16 : 1];  // the group's query rows
+  float p[kRowWaves][WA::kPBufFloats];
+  uint32_t hist[2][256];
+  uint32_t red[2][kRowWaves];
+  uint32_t wsum[kRowWaves];
+  uint32_t pick[3];
+};
+
+template <typename T, int G>
+__global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
+    const T* __restrict__ q, T* __restrict__ meta, int stride, const T* __restrict__ k_pool,
+    const T* __restrict__ v_pool, int num_phys, int Hkv, const int* __restrict__ page_indptr,
+    const int* __restrict__ page_indices, const int* __restrict__ seq_lens, int refresh_tail,
+    int k, float scale_log2, float* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ group_scores, int* __restrict__ sel, int* __restrict__ sel_count) {
+  using WA = typename RowShared<T, G>::WA;
+  constexpr int EPC = WA::EPC;
+  constexpr int D = WA::D;
+  __shared__ RowShared<T, G> sh;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row_i = blockIdx.x;
+  const int b = row_i / Hkv;
+  const int h = row_i - b * Hkv;
+  const int Hq = Hkv * G;
+  const size_t row = (size_t)row_i;
+  const int c = lane & 15;     // chunk within a metadata record
+  const int slot = lane >> 4;  // which of the wave's 4 pages of a step
+
+  // ---- phase 1: scores ---------------------------------------------------
+  const int L = seq_lens[b];
+  const int tbase = page_indptr[b];
+  const char* mrow = reinterpret_cast<const char*>(meta) + row * stride * 512;
+  // Records of steps s0 .. s0+kBatch-1 (pages past the row read the last slot of
+  // the row's stride, which is in bounds; their scores are masked).
+  auto issue = [&](int s0, uint4 (&bm)[kBatch], uint4 (&bM)[kBatch]) {
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int j = min((s0 + t) * 32 + wave * 4 + slot, stride - 1);
+      bm[t] = ld16(mrow + (size_t)j * 512 + c * 16);
+      bM[t] = ld16(mrow + (size_t)j * 512 + 256 + c * 16);
+    }
+  };
+  uint4 bm0[kBatch], bM0[kBatch], bm1[kBatch], bM1[kBatch];
+  issue(0, bm0, bM0);
+
+  uint4 qn[G], qp[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const char* qrow = reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G + hh) * kRowBytes;
+    chunk_sign_split(ld16(qrow + c * 16), qn[hh], qp[hh], T{});
+  }
+  // (the host keeps rows within kRowMaxPages; the clamp guards the LDS arrays)
+  const int n = L > 0 ? min(min((L + kPage - 1) / kPage, stride), kRowMaxPages) : 0;
+  if constexpr (WA::kQInLds) {
+    if (tid < G * kRowBytes / 16)
+      sh.q[tid] = ld16(reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G) * kRowBytes + tid * 16);
+  }
+  const int nsteps = (n + 31) >> 5;
+  const int last_batch = nsteps > 0 ? (nsteps - 1) / kBatch * kBatch : 0;
+
+  // the row's page table (to LDS for the attention phase)
+  int ph[kKeysPerThread];
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread; ++i) {
+    const int j = tid + i * kRowThreads;
+    ph[i] = j < n ? page_indices[tbase + j] : 0;
+  }
+  // Records are double-buffered: batch b+1 is in flight while batch b is
+  // scored. Past the last batch the prefetch re-reads it (cache hits), which
+  // keeps the issue branch-free; the scheduling barriers keep the loads in
+  // issue order for the in-order memory counter.
+  __builtin_amdgcn_sched_barrier(0);
+  issue(min(kBatch, last_batch), bm1, bM1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread; ++i) {
+    const int j = tid + i * kRowThreads;
+    if (j < n) sh.u.s.phys[j] = ph[i];
+  }
+
+  // tail-page refresh by the wave that scores it
+  const int jt = n - 1;
+  const bool own_tail = refresh_tail && n > 0 && ((jt >> 2) & (kRowWaves - 1)) == wave;
+  uint4 tmn = make_uint4(0, 0, 0, 0), tmx = tmn;
+  bool tail_ok = false;  // wave-uniform
+  if (own_tail) {
+    const int p = page_indices[tbase + jt];
+    if (p >= 0 && p < num_phys) {  // else the stored record is scored unchanged
+      const int valid = min(kPage, L - kPage * jt);
+      tile_minmax<T>(reinterpret_cast<const char*>(k_pool) + ((size_t)p * Hkv + h) * kTileBytes,
+                     valid, lane, tmn, tmx);
+      if (lane < 32)
+        st16(reinterpret_cast<char*>(meta) + (row * stride + jt) * 512 + (lane >> 4) * 256 + c * 16,
+             lane < 16 ? tmn : tmx);
+      tail_ok = true;
+    }
+  }
+
+  auto score = [&](int s0, uint4 (&bm)[kBatch], uint4 (&bM)[kBatch]) {
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int j = (s0 + t) * 32 + wave * 4 + slot;
+      uint4 m = bm[t], M = bM[t];
+      if (tail_ok && j == jt) {
+        m = tmn;
+        M = tmx;
+      }
+      const bool ok = j < n;
+      float gmax = -__builtin_inff();
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float acc = 0.0f;
+        if (ok) {
+          acc = chunk_dot(qn[hh], m, acc, T{});
+          acc = chunk_dot(qp[hh], M, acc, T{});
+        }
+        acc = sum16(acc);
+        gmax = fmaxf(gmax, ok ? acc : -__builtin_inff());
+      }
+      if (c == 0 && ok) sh.u.s.key[j] = score_key(gmax);
+    }
+  };
+
+  for (int s = 0;;) {
+    score(s, bm0, bM0);
+    s += kBatch;
+    if (s >= nsteps) break;
+    issue(min(s + kBatch, last_batch), bm0, bM0);
+    __builtin_amdgcn_sched_barrier(0);
+    score(s, bm1, bM1);
+    s += kBatch;
+    if (s >= nsteps) break;
+    issue(min(s + kBatch, last_batch), bm1, bM1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (tid < 256) sh.hist[0][tid] = 0u;
+
+  // ---- phase 2: top-K ----------------------------------------------------
+  const int keff = min(min(k, n), kRowMaxSelect);  // the host keeps min(k, n) within the list
+  const int kpt = (n + kRowThreads - 1) / kRowThreads;  // keys per thread, contiguous
+  const int j0 = tid * kpt;
+  uint32_t keys[kKeysPerThread];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread; ++i) {
+    keys[i] = 0u;
+    if (i < kpt && j0 + i < n) {
+      keys[i] = sh.u.s.key[j0 + i];
+      kmin = min(kmin, keys[i]);
+      kmax = max(kmax, keys[i]);
+    }
+  }
+  if (group_scores != nullptr) {
+    // the key is invertible (only -0 comes back as +0)
+    for (int j = tid; j < stride; j += kRowThreads)
+      group_scores[row * stride + j] =
+          j < n ? __uint_as_float(key_to_f32(sh.u.s.key[j])) : -__builtin_inff();
+  }
+  uint32_t krem = (uint32_t)keff;
+  uint32_t thr = 0u;  // threshold prefix at granularity `shift`
+  int shift = 0;
+  if (keff < n) {
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    if (lane == 0) {
+      sh.red[0][wave] = kmin;
+      sh.red[1][wave] = kmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      kmin = min(kmin, sh.red[0][w]);
+      kmax = max(kmax, sh.red[1][w]);
+    }
+    const uint32_t diff = kmin ^ kmax;
+    thr = kmin;
+    if (diff != 0u) {
+      shift = 32 - __builtin_clz(diff);
+      thr = (uint32_t)((uint64_t)kmin >> shift);
+      int pass = 0;
+      while (shift > 0) {
+        const int nb = shift < 8 ? shift : 8;
+        const int lo = shift - nb;
+        const uint32_t nbins = 1u << nb;
+        uint32_t* hcur = sh.hist[pass & 1];
+#pragma unroll
+        for (int i = 0; i < kKeysPerThread; ++i) {
+          if (i < kpt && j0 + i < n && (uint32_t)((uint64_t)keys[i] >> shift) == thr)
+            atomicAdd(&hcur[(keys[i] >> lo) & (nbins - 1u)], 1u);
+        }
+        if (tid >= kRowThreads - 256) sh.hist[(pass + 1) & 1][tid - (kRowThreads - 256)] = 0u;
+        __syncthreads();
+        if (wave == 0) {
+          // lane l scans digits nbins-1 - (4l .. 4l+3), i.e. descending
+          uint32_t cnt[4];
+          uint32_t local = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int pos = lane * 4 + i;
+            cnt[i] = pos < (int)nbins ? hcur[nbins - 1 - pos] : 0u;
+            local += cnt[i];
+          }
+          uint32_t above = wave_scan_incl(local) - local;
+          if (above < krem && above + local >= krem) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (above < krem && above + cnt[i] >= krem) {
+                sh.pick[0] = nbins - 1u - (uint32_t)(lane * 4 + i);
+                sh.pick[1] = krem - above;
+                sh.pick[2] = cnt[i];
+              }
+              above += cnt[i];
+            }
+          }
+        }
+        __syncthreads();
+        thr = (thr << nb) | sh.pick[0];
+        krem = sh.pick[1];
+        shift = lo;
+        if (krem == sh.pick[2]) break;  // the boundary bin is taken whole
+        ++pass;
+      }
+    }
+  }
+
+  // compaction in page order: above the threshold, then the first krem equal
+  uint32_t gt_n = 0, eq_n = 0;
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread; ++i) {
+    if (i < kpt && j0 + i < n) {
+      const uint32_t kk = (uint32_t)((uint64_t)keys[i] >> shift);
+      gt_n += kk > thr ? 1u : 0u;
+      eq_n += kk == thr ? 1u : 0u;
+    }
+  }
+  if (keff == n) {  // every page: nothing to compare
+    gt_n = (uint32_t)max(0, min(kpt, n - j0));
+    eq_n = 0;
+  }
+  uint32_t total;
+  const uint32_t excl = block_excl_scan<kRowWaves>(gt_n | (eq_n << 16), sh.wsum, &total);
+  uint32_t gt_before = excl & 0xFFFFu;
+  uint32_t eq_before = excl >> 16;
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread; ++i) {
+    const int j = j0 + i;
+    if (i < kpt && j < n) {
+      const uint32_t kk = (uint32_t)((uint64_t)keys[i] >> shift);
+      const bool gt = keff == n || kk > thr;
+      const bool eq = keff < n && kk == thr;
+      if (gt || (eq && eq_before < krem)) {  // keff <= kRowMaxSelect bounds pos
+        const uint32_t pos = gt_before + (eq_before < krem ? eq_before : krem);
+        if (pos < (uint32_t)keff) {
+          sh.list[pos] = j;
+          if (sel != nullptr) sel[row * k + pos] = j;
+        }
+      }
+      gt_before += gt ? 1u : 0u;
+      eq_before += eq ? 1u : 0u;
+    }
+  }
+  if (sel != nullptr)
+    for (int i = keff + tid; i < k; i += kRowThreads) sel[row * k + i] = -1;
+  if (sel_count != nullptr && tid == 0) sel_count[row] = keff;
+  __syncthreads();
+
+  // ---- phase 3: attention over the selected pages --------------------------
+  const int npw = keff > wave ? (keff - wave + kRowWaves - 1) / kRowWaves : 0;
+  int my_p = 0, my_valid = 0;
+  if (lane < npw) {
+    const int j = sh.list[wave + kRowWaves * lane];
+    const int p = sh.u.s.phys[j];
+    if (p >= 0 && p < num_phys) {
+      my_p = p;
+      my_valid = min(kPage, L - kPage * j);
+    }
+  }
+  __syncthreads();  // the key / table area is reused by the merge below
+
+  WA wa;
+  wa.init(WA::kQInLds ? reinterpret_cast<const char*>(sh.q)
+                      : reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G) * kRowBytes,
+          lane);
+  wa.run(npw, my_p, my_valid, reinterpret_cast<const char*>(k_pool) + (size_t)h * kTileBytes,
+         reinterpret_cast<const char*>(v_pool) + (size_t)h * kTileBytes,
+         (size_t)Hkv * kTileBytes, scale_log2, sh.p[wave], lane);
+
+  // ---- phase 4: merge of the 8 waves ----------------------------------------
+  float mw, lw;
+  wa.reduce(&mw, &lw);
+  if (lane < 16) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) sh.u.c.o[wave][hh][lane * EPC + e] = wa.o[hh][e];
+  }
+  if (lane < G) {
+    sh.u.c.ml[wave][lane][0] = mw;
+    sh.u.c.ml[wave][lane][1] = lw;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += kRowThreads) {
+    const int hh = idx / D;
+    const int d = idx - hh * D;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) M = fmaxf(M, sh.u.c.ml[w][hh][0]);
+    float acc = 0.0f, lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      const float m2 = sh.u.c.ml[w][hh][0];
+      const float sc = (m2 == -__builtin_inff()) ? 0.0f : fast_exp2(m2 - M);
+      acc += sh.u.c.o[w][hh][d] * sc;
+      lsum += sh.u.c.ml[w][hh][1] * sc;
+    }
+    const size_t qrow = (size_t)b * Hq + h * G + hh;
+    out[qrow * D + d] = lsum > 0.0f ? acc / lsum : 0.0f;
+    if (lse != nullptr && d == 0)
+      lse[qrow] = lsum > 0.0f ? (M + __log2f(lsum)) * 0.69314718055994530942f : -__builtin_inff();
+  }
+}
+
+template <typename T>
+hipError_t launch_sparse_row_t(const LaunchCommon& c, const void* q, void* meta, int stride,
+                               int refresh_tail, int k, float scale_log2, float* out, float* lse,
+                               float* group_scores, int* sel, int* sel_count, hipStream_t stream) {
+  const dim3 grid(c.B * c.Hkv);
+  const T* qq = static_cast<const T*>(q);
+  T* mm = static_cast<T*>(meta);
+  const T* kk = static_cast<const T*>(c.k_pool);
+  const T* vv = static_cast<const T*>(c.v_pool);
+#define QSA_ROW_CASE(GG)                                                                          \
+  case GG:                                                                                        \
+    hipLaunchKernelGGL((sparse_row_kernel<T, GG>), grid, dim3(kRowThreads), 0, stream, qq, mm,    \
+                       stride, kk, vv, c.num_phys, c.Hkv, c.page_indptr, c.page_indices,          \
+                       c.seq_lens, refresh_tail, k, scale_log2, out, lse, group_scores, sel,      \
+                       sel_count);                                                                \
+    break;
+  switch (c.G) {
+    QSA_ROW_CASE(1)
+    QSA_ROW_CASE(2)
+    QSA_ROW_CASE(4)
+    QSA_ROW_CASE(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef QSA_ROW_CASE
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_row(const LaunchCommon& c, const void* q, void* meta, int stride,
+                             int refresh_tail, int k, float scale_log2, float* out, float* lse,
+                             float* group_scores, int* sel, int* sel_count, hipStream_t stream) {
+  return c.bf16 ? launch_sparse_row_t<bf16s>(c, q, meta, stride, refresh_tail, k, scale_log2, out,
+                                             lse, group_scores, sel, sel_count, stream)
+                : launch_sparse_row_t<float>(c, q, meta, stride, refresh_tail, k, scale_log2, out,
+                                             lse, group_scores, sel, sel_count, stream);
+}
+
+}  // namespace qsa

@@ -18,29 +18,6 @@
 namespace qsa {
 namespace {
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) { return wave_scan_incl(v); }
-
-// Exclusive prefix sum over the workgroup (thread order); *total gets the
-// sum. Contains barriers: every thread must call it.
-template <int kWaves>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan(v);
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t t = wsum[w];
-    before += (w < wave) ? t : 0u;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + incl - v;
-}
-
 __device__ __forceinline__ uint32_t wave_min_u(uint32_t v) { return wave_min_u32(v); }
 __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) { return wave_max_u32(v); }
 
@@ -128,7 +105,7 @@ __global__ void __launch_bounds__(256) topk_wave_kernel(
         cnt[i] = pos < (int)nbins ? h[nbins - 1 - pos] : 0u;
         local += cnt[i];
       }
-      uint32_t above = wave_incl_scan(local) - local;
+      uint32_t above = wave_scan_incl(local) - local;
       if (above < krem && above + local >= krem) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -157,7 +134,7 @@ __global__ void __launch_bounds__(256) topk_wave_kernel(
     }
   }
   const uint32_t packed = gt_n | (eq_n << 16);
-  const uint32_t excl = wave_incl_scan(packed) - packed;
+  const uint32_t excl = wave_scan_incl(packed) - packed;
   uint32_t gt_before = excl & 0xFFFFu;
   uint32_t eq_before = excl >> 16;
 #pragma unroll

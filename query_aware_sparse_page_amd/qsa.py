@@ -16,6 +16,7 @@ _lib = None
 
 QSA_OK, QSA_ERR_INVALID_ARG, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_DEVICE = range(5)
 QSA_F32, QSA_BF16 = 0, 1
+PATHS = {"auto": 0, "fused": 1, "split": 2}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -54,6 +55,10 @@ def lib():
             "qsa_topk_pages": (i32, [D, KV, vp, i32, i32, vp, vp, vp, vp, sz, vp]),
             "qsa_paged_decode": (i32, [D, vp, KV, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
             "qsa_cascade_decode": (i32, [D, vp, vp, i32, KV, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
+            "qsa_sparse_decode": (i32, [D, vp, KV, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, i32, vp,
+                                        sz, vp]),
+            "qsa_sparse_decode_path": (i32, [D, _i32p, i32, i32, i32, _i32p]),
+            "qsa_sparse_decode_workspace_size": (sz, [D, _i32p, i32, i32, i32]),
             "qsa_topk_workspace_size": (sz, [D, i32, i32]),
             "qsa_decode_workspace_size": (sz, [D, _i32p, i32]),
             "qsa_cascade_workspace_size": (sz, [D, i32, _i32p, i32]),
@@ -239,6 +244,45 @@ def cascade_decode(q: torch.Tensor, prefix_pages: torch.Tensor, prefix_len: int,
     _check(lib().qsa_cascade_decode(ctypes.byref(d), _ptr(q), _ptr(prefix_pages), prefix_len, ctypes.byref(s),
                                     _ptr(sel), _ptr(sel_count), k, ctypes.c_float(sm_scale), _ptr(o), _ptr(lse),
                                     _ptr(workspace), workspace.numel(), _stream()))
+    return o, lse
+
+
+def sparse_decode_path(kv: PagedKV, num_q_heads: int, stride: int, k: int, path: str = "auto") -> str:
+    """The kernels sparse_decode runs for this shape: "fused" or "split"."""
+    d = kv.dims(num_q_heads)
+    chosen = ctypes.c_int32()
+    _check(lib().qsa_sparse_decode_path(ctypes.byref(d), ctypes.cast(kv._host_arr, _i32p), stride, k,
+                                        PATHS[path], ctypes.byref(chosen)))
+    return {v: n for n, v in PATHS.items()}[chosen.value]
+
+
+def sparse_decode_workspace_size(kv: PagedKV, num_q_heads: int, stride: int, k: int, path: str = "auto") -> int:
+    d = kv.dims(num_q_heads)
+    return int(lib().qsa_sparse_decode_workspace_size(ctypes.byref(d), ctypes.cast(kv._host_arr, _i32p), stride,
+                                                      k, PATHS[path]))
+
+
+def sparse_decode(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, k: int, sm_scale: Optional[float] = None,
+                  refresh_tail: bool = True, path: str = "auto", with_lse: bool = True,
+                  group_scores: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None,
+                  sel_count: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  out=None):
+    """One sparse decode step (scores -> top-k pages -> attention) in one
+    call; group_scores / sel / sel_count are optional extra outputs (pass
+    tensors of shape [B, Hkv, stride] / [B, Hkv, k] / [B, Hkv] to get them)."""
+    B, Hq, D = q.shape
+    stride = int(meta.shape[2])
+    sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
+    o = out[0] if out is not None else torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    lse = (out[1] if out is not None else torch.empty(B, Hq, dtype=torch.float32, device=q.device)) if with_lse else None
+    need = sparse_decode_workspace_size(kv, Hq, stride, k, path)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    d, s = kv.dims(Hq), kv.struct()
+    _check(lib().qsa_sparse_decode(ctypes.byref(d), _ptr(q), ctypes.byref(s), _ptr(meta), stride, int(refresh_tail),
+                                   k, ctypes.c_float(sm_scale), _ptr(o), _ptr(lse), _ptr(group_scores), _ptr(sel),
+                                   _ptr(sel_count), PATHS[path], _ptr(workspace),
+                                   0 if workspace is None else workspace.numel(), _stream()))
     return o, lse
 
 

@@ -107,3 +107,62 @@ def test_decode_plan_and_workspace(L):
 
 def test_topk_workspace_query(L):
     assert L.qsa_topk_workspace_size(ctypes.byref(_dims()), 8192, 128) >= 0
+
+
+def _path(L, d, lens, stride, k, path):
+    chosen = ctypes.c_int32(-1)
+    st = L.qsa_sparse_decode_path(ctypes.byref(d), lens, stride, k, path, ctypes.byref(chosen))
+    return st, chosen.value
+
+
+def test_sparse_decode_path_choice(L):
+    AUTO, FUSED, SPLIT = qsa.PATHS["auto"], qsa.PATHS["fused"], qsa.PATHS["split"]
+    # 16 x 8 rows of 512 pages, 153 selected: fused by default, no workspace
+    d = _dims(B=16)
+    lens = _lens([8192] * 16)
+    assert _path(L, d, lens, 512, 153, AUTO) == (0, FUSED)
+    assert L.qsa_sparse_decode_workspace_size(ctypes.byref(d), lens, 512, 153, AUTO) == 0
+    # the split path needs scores + selection + decode partials
+    assert _path(L, d, lens, 512, 153, SPLIT) == (0, SPLIT)
+    ws = L.qsa_sparse_decode_workspace_size(ctypes.byref(d), lens, 512, 153, SPLIT)
+    assert ws >= 128 * 512 * 4 + 128 * 153 * 4 + 128 * 4 + L.qsa_decode_workspace_size(ctypes.byref(d), lens, 153)
+    # 8 x 8 rows of 8192 pages: too long for one workgroup per row
+    d8 = _dims(B=8)
+    long_lens = _lens([131072] * 8)
+    assert _path(L, d8, long_lens, 8192, 128, AUTO) == (0, SPLIT)
+    st, _ = _path(L, d8, long_lens, 8192, 128, FUSED)
+    assert st == qsa.QSA_ERR_UNSUPPORTED and b"fused path" in L.qsa_last_error()
+    # few rows: split even when the rows would fit
+    d1 = _dims(B=1)
+    assert _path(L, d1, _lens([8192]), 512, 153, AUTO) == (0, SPLIT)
+    assert _path(L, d1, _lens([8192]), 512, 153, FUSED) == (0, FUSED)
+    # more than 512 selected pages do not fit the fused list; k >= n_b with n_b <= 512 does
+    assert _path(L, d, _lens([16384] * 16), 1024, 600, FUSED)[0] == qsa.QSA_ERR_UNSUPPORTED
+    assert _path(L, d, lens, 512, 100000, FUSED) == (0, FUSED)
+    # argument errors
+    assert _path(L, d, lens, 100, 153, AUTO)[0] == qsa.QSA_ERR_INVALID_ARG      # stride < 512 pages
+    assert _path(L, d, lens, 512, 0, AUTO)[0] == qsa.QSA_ERR_INVALID_ARG        # k < 1
+    assert _path(L, d, lens, 512, 153, 7)[0] == qsa.QSA_ERR_INVALID_ARG         # unknown path
+    assert L.qsa_sparse_decode_workspace_size(ctypes.byref(d), lens, 512, 0, AUTO) == 0
+
+
+def test_sparse_decode_validation(L):
+    d = _dims(B=4)
+    lens = _lens([64, 40, 16, 1])
+    kv = qsa.PagedKVStruct(1, 1, 10, 1, 1, 1, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)))
+    args = lambda **kw: dict(dict(q=1, meta=1, stride=4, refresh=1, k=2, scale=1.0, out=1, path=0, ws=None, wsb=0), **kw)
+
+    def call(a):
+        return L.qsa_sparse_decode(ctypes.byref(d), a["q"], ctypes.byref(kv), a["meta"], a["stride"], a["refresh"],
+                                   a["k"], ctypes.c_float(a["scale"]), a["out"], None, None, None, None, a["path"],
+                                   a["ws"], a["wsb"], None)
+
+    assert call(args(q=None)) == qsa.QSA_ERR_INVALID_ARG
+    assert call(args(meta=None)) == qsa.QSA_ERR_INVALID_ARG
+    assert call(args(refresh=2)) == qsa.QSA_ERR_INVALID_ARG
+    assert call(args(scale=float("nan"))) == qsa.QSA_ERR_INVALID_ARG
+    assert call(args(stride=3)) == qsa.QSA_ERR_INVALID_ARG              # 64 tokens = 4 pages
+    assert call(args(k=0)) == qsa.QSA_ERR_INVALID_ARG
+    # the split path checks its workspace before launching anything
+    st = call(args(path=qsa.PATHS["split"]))
+    assert st == qsa.QSA_ERR_WORKSPACE and b"workspace" in L.qsa_last_error()
