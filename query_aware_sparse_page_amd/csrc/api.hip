@@ -450,8 +450,13 @@ qsa_status qsa_sparse_decode(const qsa_dims* dims, const void* q, const qsa_page
   const qsa::LaunchCommon c = common(dims, kv);
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   if (chosen == QSA_PATH_FUSED) {
-    return device_status(qsa::launch_sparse_row(c, q, meta, stride, refresh_tail, k, scale_log2, out,
-                                                 lse, group_scores, sel, sel_count, stream),
+    // fewer rows than CUs: two workgroups per row, each attending for half
+    // of the group's query heads
+    const int rows = dims->num_seqs * dims->num_kv_heads;
+    const int head_split = (c.G >= 2 && rows < device_cus()) ? 2 : 1;
+    return device_status(qsa::launch_sparse_row(c, q, meta, stride, refresh_tail, k, scale_log2,
+                                                 head_split, out, lse, group_scores, sel, sel_count,
+                                                 stream),
                          "sparse_decode (fused) launch");
   }
   const SparseWs w = sparse_ws(dims, kv->seq_lens_host, stride, k);

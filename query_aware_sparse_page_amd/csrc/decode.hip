@@ -91,7 +91,8 @@ decode_split_kernel(
   }
   WA wa;
   wa.init(qrows, lane);
-  wa.run(npw, my_p, my_valid, reinterpret_cast<const char*>(k_pool) + (size_t)h * kTileBytes,
+  LanePages src{my_p, my_valid, npw};
+  wa.run(src, reinterpret_cast<const char*>(k_pool) + (size_t)h * kTileBytes,
          reinterpret_cast<const char*>(v_pool) + (size_t)h * kTileBytes,
          (size_t)Hkv * kTileBytes, scale_log2, sh.p[wave], lane);
 

@@ -28,16 +28,17 @@ namespace qsa {
 
 constexpr float kLazyTau = 8.0f;  // log2 headroom before the reference max moves
 
-// Page buffers per wave: three pages in flight at g <= 4, two at g = 8,
-// which is what the register file holds at two waves per SIMD. At g = 8 the
-// query rows (8 VGPRs per head) are read from LDS for every page instead of
-// being held in registers (the caller stages them in LDS).
-template <typename T, int G>
+// kStagesArg page buffers per wave (kStagesArg - 1 pages in flight while
+// one is computed); the default is what the register file holds at two
+// waves per SIMD: three at g <= 4, two at g = 8. At g = 8 the query rows
+// (8 VGPRs per head) are read from LDS for every page instead of being held
+// in registers (the caller stages them in LDS).
+template <typename T, int G, int kStagesArg = 2>
 struct WaveAttn {
   static constexpr int EPC = Elem<T>::kPerChunk;
   static constexpr int D = 16 * EPC;
   static constexpr int NP = (2 * G + 7) / 8;         // (row, head) pairs owned per lane
-  static constexpr int kStages = G >= 8 ? 2 : 3;     // page buffers per wave (register budget)
+  static constexpr int kStages = kStagesArg;         // page buffers per wave
   static constexpr bool kQInLds = G >= 8;            // query rows read from LDS
   static constexpr int kPBufFloats = 2 * kPage * G;  // LDS per wave: double-buffered probabilities
   // s_waitcnt immediate (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt
@@ -74,25 +75,30 @@ struct WaveAttn {
     l_lane = 0.0f;
   }
 
-  // Attention over the wave's npw pages: lane i (< npw) holds page i's
-  // physical slot (my_p) and valid-token count (my_valid, 0 = skip). kbase /
-  // vbase point at the KV head's tile of physical page 0; tiles of
-  // consecutive physical pages are page_stride bytes apart. pbuf: this wave's
-  // kPBufFloats of LDS.
-  __device__ __forceinline__ void run(int npw, int my_p, int my_valid, const char* kbase,
-                                      const char* vbase, size_t page_stride, float scale_log2,
-                                      float* pbuf, int lane) {
+  // Attention over the pages a page source hands this wave, one at a time:
+  // src.empty() says whether the wave gets any page; src.next(&p, &v) gives
+  // the next page's physical slot p and valid-token count v (0: skip the
+  // page; -1: no more pages, p then naming a page the wave has read).
+  // kbase / vbase point at the KV head's tile of physical page 0; tiles of
+  // consecutive physical pages are page_stride bytes apart. pbuf: this
+  // wave's kPBufFloats of LDS.
+  template <class Src>
+  __device__ __forceinline__ void run(Src& src, const char* kbase, const char* vbase,
+                                      size_t page_stride, float scale_log2, float* pbuf,
+                                      int lane) {
     const int gi = lane >> 3;      // K layout: row pair (gi, gi + 8)
     const int qa = lane & 7;       // K layout: chunks qa, qa + 8
     const int hl = qa & (G - 1);   // the head whose logits this lane owns
     const int vr = lane >> 4;      // V layout: rows vr + 4r
 
-    // Issue the loads of page sp (K in the QK layout, V linear). Branch-free,
-    // so the compiler's wait counts stay exact and the next pages' loads
-    // overlap the current page's math; a skipped page (no valid tokens)
-    // reads physical slot 0, which always exists.
-    auto issue = [&](int sp, uint4 (&kA)[2][2], uint4 (&vB)[4]) {
-      const int p = __builtin_amdgcn_readlane(my_p, sp);
+    // Issue the loads of the next page of the source (K in the QK layout, V
+    // linear) and return its valid-token count. Branch-free, so the
+    // compiler's wait counts stay exact and the next pages' loads overlap the
+    // current page's math; past the wave's last page it re-reads a page it
+    // has read (an L2 hit, no extra HBM traffic).
+    auto issue = [&](uint4 (&kA)[2][2], uint4 (&vB)[4]) -> int {
+      int p, valid;
+      src.next(&p, &valid);
       const char* kt = kbase + (size_t)p * page_stride;
       const char* vt = vbase + (size_t)p * page_stride;
 #pragma unroll
@@ -102,17 +108,17 @@ struct WaveAttn {
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) vB[r] = ld16(vt + r * 1024 + lane * 16);
+      return valid;
     };
 
-    // Attention over page sp, whose tiles are in kA / vB.
-    auto process = [&](int sp, const uint4 (&kA)[2][2], const uint4 (&vB)[4]) {
-      // A skipped page (valid == 0, or a pad slot past the wave's last page)
-      // only retires its loads: the wait leaves the kStages-1 newer pages'
-      // loads in flight, as the compute path would, so every path through
-      // the loop carries the same loads and the loop head never drains the
-      // memory queue.
-      const int valid = sp < npw ? __builtin_amdgcn_readlane(my_valid, sp) : 0;
-      if (valid == 0) {
+    // Attention over the page whose tiles are in kA / vB (`valid` rows).
+    auto process = [&](int sp, int valid, const uint4 (&kA)[2][2], const uint4 (&vB)[4]) {
+      // A skipped page (valid <= 0: skipped, or a slot past the wave's last
+      // page) only retires its loads: the wait leaves the kStages-1 newer
+      // pages' loads in flight, as the compute path would, so every path
+      // through the loop carries the same loads and the loop head never
+      // drains the memory queue.
+      if (valid <= 0) {
         __builtin_amdgcn_s_waitcnt(kSkipWait);
         return;
       }
@@ -214,29 +220,31 @@ struct WaveAttn {
     // Software pipeline: the loads of the next kStages-1 pages are in flight
     // while the current page is processed (HBM latency is several times the
     // math of one page). kStages register buffers, rotated by an unrolled
-    // loop so no data is copied; past the wave's last page the prefetch
-    // re-reads that page (an L2 hit, no extra HBM traffic).
-    if (npw <= 0) return;
+    // loop so no data is copied. The loop runs whole rotations and leaves at
+    // the bottom once no buffer holds a page (a single exit).
+    if (src.empty()) return;
     uint4 kA[kStages][2][2], vB[kStages][4];
+    int vld[kStages];
     // (the scheduling barriers keep the pages' loads in issue order, which
     // the in-order memory counter needs for the waits below to be partial)
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s) {
-      issue(min(s, npw - 1), kA[s], vB[s]);
+      vld[s] = issue(kA[s], vB[s]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // The trip count is rounded up to whole rotations (pad slots are
-    // masked), so the loop has a single exit at the bottom.
-    const int rotations = (npw + kStages - 1) / kStages;
     int sp = 0;
-    for (int it = 0; it < rotations; ++it) {
+    while (true) {
 #pragma unroll
       for (int r = 0; r < kStages; ++r) {
-        issue(min(sp + kStages - 1, npw - 1), kA[(r + kStages - 1) % kStages],
-              vB[(r + kStages - 1) % kStages]);
-        process(sp, kA[r], vB[r]);
+        vld[(r + kStages - 1) % kStages] =
+            issue(kA[(r + kStages - 1) % kStages], vB[(r + kStages - 1) % kStages]);
+        process(sp, vld[r], kA[r], vB[r]);
         ++sp;
       }
+      bool more = false;
+#pragma unroll
+      for (int s = 0; s < kStages - 1; ++s) more |= vld[s] >= 0;
+      if (!more) break;
     }
   }
 
@@ -258,6 +266,19 @@ struct WaveAttn {
       }
     *m_out = m_lane;
     *l_out = lr;
+  }
+};
+
+// Page source: the wave's pages held one per lane (lane i: physical slot
+// and valid-token count of the wave's i-th page), npw <= 64 of them.
+struct LanePages {
+  int my_p, my_valid, npw;
+  int i = 0;
+  __device__ __forceinline__ bool empty() const { return npw <= 0; }
+  __device__ __forceinline__ void next(int* p, int* v) {
+    *p = __builtin_amdgcn_readlane(my_p, min(i, npw - 1));
+    *v = i < npw ? __builtin_amdgcn_readlane(my_valid, min(i, 63)) : -1;
+    ++i;
   }
 };
 

@@ -54,14 +54,16 @@ hipError_t launch_decode(const LaunchCommon& c, const void* q, const int* sel, c
                          hipStream_t stream);
 
 // Fused per-row sparse decode step (score -> top-K -> attention -> merge in
-// one workgroup per (b, h) row). Rows of at most kRowMaxPages pages, at most
-// kRowMaxSelect selected pages.
+// one workgroup per (b, h) row, or head_split = 2 workgroups per row that
+// each attend for half of the group's query heads). Rows of at most
+// kRowMaxPages pages, at most kRowMaxSelect selected pages.
 constexpr int kRowMaxPages = 4096;
 constexpr int kRowMaxSelect = 512;
 
 hipError_t launch_sparse_row(const LaunchCommon& c, const void* q, void* meta, int stride,
-                             int refresh_tail, int k, float scale_log2, float* out, float* lse,
-                             float* group_scores, int* sel, int* sel_count, hipStream_t stream);
+                             int refresh_tail, int k, float scale_log2, int head_split, float* out,
+                             float* lse, float* group_scores, int* sel, int* sel_count,
+                             hipStream_t stream);
 
 // Cascade prefix on the matrix cores (bf16, D = 128): partials per
 // (KV head, split, query row).

@@ -32,12 +32,17 @@ namespace {
 
 constexpr int kRowWaves = 8;
 constexpr int kRowThreads = kRowWaves * kWave;
-constexpr int kKeysPerThread = kRowMaxPages / kRowThreads;
+constexpr int kStepPages = kRowWaves * 4;  // pages scored per workgroup step
+static_assert(kRowThreads >= 256, "the radix histogram is cleared by 256 threads");
+constexpr int kKeysPerThread = (kRowMaxPages + kRowThreads - 1) / kRowThreads;
 constexpr int kBatch = 4;  // score steps per load batch
 
-template <typename T, int G>
+// Page buffers of the per-wave attention (see WaveAttn).
+constexpr int row_stages(int gw) { return 2; }
+
+template <typename T, int GW>
 struct RowShared {
-  using WA = WaveAttn<T, G>;
+  using WA = WaveAttn<T, GW, row_stages(GW)>;
   static constexpr int D = WA::D;
   union {
     struct {
@@ -45,12 +50,13 @@ struct RowShared {
       int phys[kRowMaxPages];      // the row's page table
     } s;
     struct {
-      float o[kRowWaves][G][D];
-      float ml[kRowWaves][G][2];
+      float o[kRowWaves][GW][D];
+      float ml[kRowWaves][GW][2];
     } c;
   } u;
-  int list[kRowMaxSelect];  // selected logical pages, ascending
-  uint4 q[WA::kQInLds ? G * kRowBytes / 16 : 1];  // the group's query rows
+  int list[kRowMaxSelect];   // selected logical pages, ascending
+  int plist[kRowMaxSelect];  // their physical slots (-1: out of range)
+  uint4 q[WA::kQInLds ? GW * kRowBytes / 16 : 1];  // the attended query rows
   float p[kRowWaves][WA::kPBufFloats];
   uint32_t hist[2][256];
   uint32_t red[2][kRowWaves];
@@ -58,22 +64,41 @@ struct RowShared {
   uint32_t pick[3];
 };
 
-template <typename T, int G>
+// S workgroups share one row when there are too few rows to fill the chip:
+// each scores and selects the whole row (the group score needs every head of
+// the group) and attends for G/S of its query heads. Workgroup w serves part
+// (w / 8) % S of row (w % 8) + 8 * (w / (8 S)), so the S workgroups of a row
+// are dispatched to the same XCD (workgroups go round-robin over the 8 XCDs)
+// and share its L2 for the row's records and K/V tiles, which they stream in
+// the same order at the same time.
+template <typename T, int G, int S>
 __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     const T* __restrict__ q, T* __restrict__ meta, int stride, const T* __restrict__ k_pool,
-    const T* __restrict__ v_pool, int num_phys, int Hkv, const int* __restrict__ page_indptr,
-    const int* __restrict__ page_indices, const int* __restrict__ seq_lens, int refresh_tail,
-    int k, float scale_log2, float* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ group_scores, int* __restrict__ sel, int* __restrict__ sel_count) {
-  using WA = typename RowShared<T, G>::WA;
+    const T* __restrict__ v_pool, int num_phys, int Hkv, int rows,
+    const int* __restrict__ page_indptr, const int* __restrict__ page_indices,
+    const int* __restrict__ seq_lens, int refresh_tail, int k, float scale_log2,
+    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ group_scores,
+    int* __restrict__ sel, int* __restrict__ sel_count) {
+  constexpr int GW = G / S;  // query heads attended by this workgroup
+  using WA = typename RowShared<T, GW>::WA;
   constexpr int EPC = WA::EPC;
   constexpr int D = WA::D;
-  __shared__ RowShared<T, G> sh;
+  __shared__ RowShared<T, GW> sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row_i = blockIdx.x;
+  const int wg = blockIdx.x;
+  const int part = (wg >> 3) % S;
+  const int row_i = (wg & 7) + 8 * (wg / (8 * S));
+  if (row_i >= rows) return;  // padding of the last group of 8 rows (whole workgroup)
+  const bool writer = part == 0;  // one workgroup of the row writes the shared outputs
+  if (!writer) {
+    group_scores = nullptr;
+    sel = nullptr;
+    sel_count = nullptr;
+  }
+  const int hq0 = part * GW;  // first attended head within the group
   const int b = row_i / Hkv;
   const int h = row_i - b * Hkv;
   const int Hq = Hkv * G;
@@ -90,7 +115,7 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   auto issue = [&](int s0, uint4 (&bm)[kBatch], uint4 (&bM)[kBatch]) {
 #pragma unroll
     for (int t = 0; t < kBatch; ++t) {
-      const int j = min((s0 + t) * 32 + wave * 4 + slot, stride - 1);
+      const int j = min((s0 + t) * kStepPages + wave * 4 + slot, stride - 1);
       bm[t] = ld16(mrow + (size_t)j * 512 + c * 16);
       bM[t] = ld16(mrow + (size_t)j * 512 + 256 + c * 16);
     }
@@ -107,10 +132,11 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   // (the host keeps rows within kRowMaxPages; the clamp guards the LDS arrays)
   const int n = L > 0 ? min(min((L + kPage - 1) / kPage, stride), kRowMaxPages) : 0;
   if constexpr (WA::kQInLds) {
-    if (tid < G * kRowBytes / 16)
-      sh.q[tid] = ld16(reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G) * kRowBytes + tid * 16);
+    if (tid < GW * kRowBytes / 16)
+      sh.q[tid] = ld16(reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G + hq0) * kRowBytes +
+                       tid * 16);
   }
-  const int nsteps = (n + 31) >> 5;
+  const int nsteps = (n + kStepPages - 1) / kStepPages;
   const int last_batch = nsteps > 0 ? (nsteps - 1) / kBatch * kBatch : 0;
 
   // the row's page table (to LDS for the attention phase)
@@ -135,7 +161,7 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
 
   // tail-page refresh by the wave that scores it
   const int jt = n - 1;
-  const bool own_tail = refresh_tail && n > 0 && ((jt >> 2) & (kRowWaves - 1)) == wave;
+  const bool own_tail = refresh_tail && n > 0 && (jt >> 2) % kRowWaves == wave;
   uint4 tmn = make_uint4(0, 0, 0, 0), tmx = tmn;
   bool tail_ok = false;  // wave-uniform
   if (own_tail) {
@@ -144,7 +170,7 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
       const int valid = min(kPage, L - kPage * jt);
       tile_minmax<T>(reinterpret_cast<const char*>(k_pool) + ((size_t)p * Hkv + h) * kTileBytes,
                      valid, lane, tmn, tmx);
-      if (lane < 32)
+      if (writer && lane < 32)
         st16(reinterpret_cast<char*>(meta) + (row * stride + jt) * 512 + (lane >> 4) * 256 + c * 16,
              lane < 16 ? tmn : tmx);
       tail_ok = true;
@@ -154,7 +180,7 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   auto score = [&](int s0, uint4 (&bm)[kBatch], uint4 (&bM)[kBatch]) {
 #pragma unroll
     for (int t = 0; t < kBatch; ++t) {
-      const int j = (s0 + t) * 32 + wave * 4 + slot;
+      const int j = (s0 + t) * kStepPages + wave * 4 + slot;
       uint4 m = bm[t], M = bM[t];
       if (tail_ok && j == jt) {
         m = tmn;
@@ -307,7 +333,9 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
       if (gt || (eq && eq_before < krem)) {  // keff <= kRowMaxSelect bounds pos
         const uint32_t pos = gt_before + (eq_before < krem ? eq_before : krem);
         if (pos < (uint32_t)keff) {
+          const int pp = sh.u.s.phys[j];
           sh.list[pos] = j;
+          sh.plist[pos] = (pp >= 0 && pp < num_phys) ? pp : -1;
           if (sel != nullptr) sel[row * k + pos] = j;
         }
       }
@@ -321,23 +349,25 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   __syncthreads();
 
   // ---- phase 3: attention over the selected pages --------------------------
+  // Wave w takes list entries w, w + 8, ... (a fixed split keeps the
+  // summation order, and so the result, the same from run to run).
   const int npw = keff > wave ? (keff - wave + kRowWaves - 1) / kRowWaves : 0;
   int my_p = 0, my_valid = 0;
   if (lane < npw) {
-    const int j = sh.list[wave + kRowWaves * lane];
-    const int p = sh.u.s.phys[j];
-    if (p >= 0 && p < num_phys) {
-      my_p = p;
-      my_valid = min(kPage, L - kPage * j);
+    const int e = wave + kRowWaves * lane;
+    const int pp = sh.plist[e];
+    if (pp >= 0) {
+      my_p = pp;
+      my_valid = min(kPage, L - kPage * sh.list[e]);
     }
   }
-  __syncthreads();  // the key / table area is reused by the merge below
+  LanePages src{my_p, my_valid, npw};
 
   WA wa;
   wa.init(WA::kQInLds ? reinterpret_cast<const char*>(sh.q)
-                      : reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G) * kRowBytes,
+                      : reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G + hq0) * kRowBytes,
           lane);
-  wa.run(npw, my_p, my_valid, reinterpret_cast<const char*>(k_pool) + (size_t)h * kTileBytes,
+  wa.run(src, reinterpret_cast<const char*>(k_pool) + (size_t)h * kTileBytes,
          reinterpret_cast<const char*>(v_pool) + (size_t)h * kTileBytes,
          (size_t)Hkv * kTileBytes, scale_log2, sh.p[wave], lane);
 
@@ -346,16 +376,16 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   wa.reduce(&mw, &lw);
   if (lane < 16) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
+    for (int hh = 0; hh < GW; ++hh)
 #pragma unroll
       for (int e = 0; e < EPC; ++e) sh.u.c.o[wave][hh][lane * EPC + e] = wa.o[hh][e];
   }
-  if (lane < G) {
+  if (lane < GW) {
     sh.u.c.ml[wave][lane][0] = mw;
     sh.u.c.ml[wave][lane][1] = lw;
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kRowThreads) {
+  for (int idx = tid; idx < GW * D; idx += kRowThreads) {
     const int hh = idx / D;
     const int d = idx - hh * D;
     float M = -__builtin_inff();
@@ -369,50 +399,58 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
       acc += sh.u.c.o[w][hh][d] * sc;
       lsum += sh.u.c.ml[w][hh][1] * sc;
     }
-    const size_t qrow = (size_t)b * Hq + h * G + hh;
+    const size_t qrow = (size_t)b * Hq + h * G + hq0 + hh;
     out[qrow * D + d] = lsum > 0.0f ? acc / lsum : 0.0f;
     if (lse != nullptr && d == 0)
       lse[qrow] = lsum > 0.0f ? (M + __log2f(lsum)) * 0.69314718055994530942f : -__builtin_inff();
   }
 }
 
+template <typename T, int G, int S>
+void launch_row(const LaunchCommon& c, const void* q, void* meta, int stride, int refresh_tail,
+                int k, float scale_log2, float* out, float* lse, float* group_scores, int* sel,
+                int* sel_count, hipStream_t stream) {
+  const int rows = c.B * c.Hkv;
+  const int wgs = S == 1 ? rows : S * ((rows + 7) / 8 * 8);
+  hipLaunchKernelGGL((sparse_row_kernel<T, G, S>), dim3(wgs), dim3(kRowThreads), 0, stream,
+                     static_cast<const T*>(q), static_cast<T*>(meta), stride,
+                     static_cast<const T*>(c.k_pool), static_cast<const T*>(c.v_pool), c.num_phys,
+                     c.Hkv, rows, c.page_indptr, c.page_indices, c.seq_lens, refresh_tail, k,
+                     scale_log2, out, lse, group_scores, sel, sel_count);
+}
+
 template <typename T>
 hipError_t launch_sparse_row_t(const LaunchCommon& c, const void* q, void* meta, int stride,
-                               int refresh_tail, int k, float scale_log2, float* out, float* lse,
-                               float* group_scores, int* sel, int* sel_count, hipStream_t stream) {
-  const dim3 grid(c.B * c.Hkv);
-  const T* qq = static_cast<const T*>(q);
-  T* mm = static_cast<T*>(meta);
-  const T* kk = static_cast<const T*>(c.k_pool);
-  const T* vv = static_cast<const T*>(c.v_pool);
-#define QSA_ROW_CASE(GG)                                                                          \
-  case GG:                                                                                        \
-    hipLaunchKernelGGL((sparse_row_kernel<T, GG>), grid, dim3(kRowThreads), 0, stream, qq, mm,    \
-                       stride, kk, vv, c.num_phys, c.Hkv, c.page_indptr, c.page_indices,          \
-                       c.seq_lens, refresh_tail, k, scale_log2, out, lse, group_scores, sel,      \
-                       sel_count);                                                                \
-    break;
+                               int refresh_tail, int k, float scale_log2, int head_split,
+                               float* out, float* lse, float* group_scores, int* sel,
+                               int* sel_count, hipStream_t stream) {
+  const bool two = head_split == 2;
+#define QSA_ROW_ARGS c, q, meta, stride, refresh_tail, k, scale_log2, out, lse, group_scores, sel, \
+                     sel_count, stream
   switch (c.G) {
-    QSA_ROW_CASE(1)
-    QSA_ROW_CASE(2)
-    QSA_ROW_CASE(4)
-    QSA_ROW_CASE(8)
+    case 1: launch_row<T, 1, 1>(QSA_ROW_ARGS); break;
+    case 2: two ? launch_row<T, 2, 2>(QSA_ROW_ARGS) : launch_row<T, 2, 1>(QSA_ROW_ARGS); break;
+    case 4: two ? launch_row<T, 4, 2>(QSA_ROW_ARGS) : launch_row<T, 4, 1>(QSA_ROW_ARGS); break;
+    case 8: two ? launch_row<T, 8, 2>(QSA_ROW_ARGS) : launch_row<T, 8, 1>(QSA_ROW_ARGS); break;
     default:
       return hipErrorInvalidValue;
   }
-#undef QSA_ROW_CASE
+#undef QSA_ROW_ARGS
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_sparse_row(const LaunchCommon& c, const void* q, void* meta, int stride,
-                             int refresh_tail, int k, float scale_log2, float* out, float* lse,
-                             float* group_scores, int* sel, int* sel_count, hipStream_t stream) {
-  return c.bf16 ? launch_sparse_row_t<bf16s>(c, q, meta, stride, refresh_tail, k, scale_log2, out,
-                                             lse, group_scores, sel, sel_count, stream)
-                : launch_sparse_row_t<float>(c, q, meta, stride, refresh_tail, k, scale_log2, out,
-                                             lse, group_scores, sel, sel_count, stream);
+                             int refresh_tail, int k, float scale_log2, int head_split, float* out,
+                             float* lse, float* group_scores, int* sel, int* sel_count,
+                             hipStream_t stream) {
+  return c.bf16 ? launch_sparse_row_t<bf16s>(c, q, meta, stride, refresh_tail, k, scale_log2,
+                                             head_split, out, lse, group_scores, sel, sel_count,
+                                             stream)
+                : launch_sparse_row_t<float>(c, q, meta, stride, refresh_tail, k, scale_log2,
+                                             head_split, out, lse, group_scores, sel, sel_count,
+                                             stream);
 }
 
 }  // namespace qsa

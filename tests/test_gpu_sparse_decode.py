@@ -29,6 +29,9 @@ CASES = [
     # rows longer than one key per thread (563 and 2500 pages) and at the limit (4096 pages)
     ("two_keys", [9000, 40000], 8, 2, "bf16", 153),
     ("max_row", [65536, 3], 4, 1, "bf16", 512),
+    # 256 rows: one workgroup per row (fewer rows than CUs split each row's
+    # query heads over two workgroups)
+    ("many_rows", [100 + (37 * i) % 900 for i in range(64)], 16, 4, "bf16", 12),
 ]
 
 
@@ -110,7 +113,7 @@ def test_sparse_decode_matches_oracle(label, lens, Hq, Hkv, dtype, k, path):
         assert torch.allclose(out, o2, atol=1e-4, rtol=0) and torch.allclose(lse, l2, atol=1e-4, rtol=0)
 
 
-@pytest.mark.parametrize("label,lens,Hq,Hkv,dtype,k", [CASES[0], CASES[1], CASES[3], CASES[7]])
+@pytest.mark.parametrize("label,lens,Hq,Hkv,dtype,k", [CASES[0], CASES[1], CASES[3], CASES[7], CASES[9]])
 def test_fused_and_split_agree(label, lens, Hq, Hkv, dtype, k):
     c = _case(label, lens, Hq, Hkv, dtype, seed=29)
     g = c.to(DEV)
