@@ -166,7 +166,7 @@ qsa::Partials carve(void* ws, const DecodeWs& w) {
   return p;
 }
 
-constexpr int kPrefixSplitTokens = 1024;  // prefix tokens per cascade split
+constexpr int kPrefixSplitTokens = 512;  // prefix tokens per cascade split
 
 int prefix_splits(int prefix_len) {
   return std::max(1, (prefix_len + kPrefixSplitTokens - 1) / kPrefixSplitTokens);

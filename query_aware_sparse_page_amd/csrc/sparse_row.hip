@@ -32,10 +32,10 @@ namespace {
 
 constexpr int kRowWaves = 8;
 constexpr int kRowThreads = kRowWaves * kWave;
-constexpr int kStepPages = kRowWaves * 4;  // pages scored per workgroup step
 static_assert(kRowThreads >= 256, "the radix histogram is cleared by 256 threads");
 constexpr int kKeysPerThread = (kRowMaxPages + kRowThreads - 1) / kRowThreads;
-constexpr int kBatch = 4;  // score steps per load batch
+constexpr int kChunkSteps = 4;                 // score steps per chunk (4 pages a step)
+constexpr int kChunkPages = 4 * kChunkSteps;    // consecutive pages scored by one wave
 
 // Page buffers of the per-wave attention (see WaveAttn).
 constexpr int row_stages(int gw) { return 2; }
@@ -62,6 +62,7 @@ struct RowShared {
   uint32_t red[2][kRowWaves];
   uint32_t wsum[kRowWaves];
   uint32_t pick[3];
+  int chunk_cursor;  // next score chunk to hand out
 };
 
 // S workgroups share one row when there are too few rows to fill the chip:
@@ -107,112 +108,137 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   const int slot = lane >> 4;  // which of the wave's 4 pages of a step
 
   // ---- phase 1: scores ---------------------------------------------------
+  // The row's pages are scored in chunks of kChunkPages consecutive pages:
+  // chunks w and w + W first, then whichever chunk an LDS counter hands out
+  // next, so that waves whose loads return late score fewer chunks (a
+  // page's score does not depend on which wave computes it).
   const int L = seq_lens[b];
   const int tbase = page_indptr[b];
   const char* mrow = reinterpret_cast<const char*>(meta) + row * stride * 512;
-  // Records of steps s0 .. s0+kBatch-1 (pages past the row read the last slot of
-  // the row's stride, which is in bounds; their scores are masked).
-  auto issue = [&](int s0, uint4 (&bm)[kBatch], uint4 (&bM)[kBatch]) {
+  // Records of chunk ci (pages past the row read the last slot of the
+  // row's stride, which is in bounds; their scores are masked).
+  auto issue = [&](int ci, uint4 (&bm)[kChunkSteps], uint4 (&bM)[kChunkSteps]) {
 #pragma unroll
-    for (int t = 0; t < kBatch; ++t) {
-      const int j = min((s0 + t) * kStepPages + wave * 4 + slot, stride - 1);
+    for (int t = 0; t < kChunkSteps; ++t) {
+      const int j = min(ci * kChunkPages + 4 * t + slot, stride - 1);
       bm[t] = ld16(mrow + (size_t)j * 512 + c * 16);
       bM[t] = ld16(mrow + (size_t)j * 512 + 256 + c * 16);
     }
   };
-  uint4 bm0[kBatch], bM0[kBatch], bm1[kBatch], bM1[kBatch];
-  issue(0, bm0, bM0);
-
+  // the query rows first: the scores wait for them but not for the records
   uint4 qn[G], qp[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     const char* qrow = reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G + hh) * kRowBytes;
-    chunk_sign_split(ld16(qrow + c * 16), qn[hh], qp[hh], T{});
+    qn[hh] = ld16(qrow + c * 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 bm0[kChunkSteps], bM0[kChunkSteps], bm1[kChunkSteps], bM1[kChunkSteps];
+  int ca = wave, cb = wave + kRowWaves;
+  issue(ca, bm0, bM0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(cb, bm1, bM1);
+  __builtin_amdgcn_sched_barrier(0);
+  if (tid == 0) sh.chunk_cursor = 2 * kRowWaves;
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const uint4 qc = qn[hh];
+    chunk_sign_split(qc, qn[hh], qp[hh], T{});
   }
   // (the host keeps rows within kRowMaxPages; the clamp guards the LDS arrays)
   const int n = L > 0 ? min(min((L + kPage - 1) / kPage, stride), kRowMaxPages) : 0;
+  // (values needed only after scoring are loaded now and stored to LDS
+  // after the chunk loop: a store would wait for the records in flight)
+  uint4 qstage = make_uint4(0, 0, 0, 0);
   if constexpr (WA::kQInLds) {
     if (tid < GW * kRowBytes / 16)
-      sh.q[tid] = ld16(reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G + hq0) * kRowBytes +
-                       tid * 16);
+      qstage = ld16(reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G + hq0) * kRowBytes +
+                    tid * 16);
   }
-  const int nsteps = (n + kStepPages - 1) / kStepPages;
-  const int last_batch = nsteps > 0 ? (nsteps - 1) / kBatch * kBatch : 0;
+  const int nchunks = (n + kChunkPages - 1) / kChunkPages;
 
   // the row's page table (to LDS for the attention phase)
+  // (unconditional loads: a fixed number of loads in flight keeps the
+  // memory-counter waits of the chunk loop partial)
   int ph[kKeysPerThread];
 #pragma unroll
   for (int i = 0; i < kKeysPerThread; ++i) {
     const int j = tid + i * kRowThreads;
-    ph[i] = j < n ? page_indices[tbase + j] : 0;
+    ph[i] = page_indices[n > 0 ? tbase + min(j, n - 1) : 0];
   }
-  // Records are double-buffered: batch b+1 is in flight while batch b is
-  // scored. Past the last batch the prefetch re-reads it (cache hits), which
-  // keeps the issue branch-free; the scheduling barriers keep the loads in
-  // issue order for the in-order memory counter.
-  __builtin_amdgcn_sched_barrier(0);
-  issue(min(kBatch, last_batch), bm1, bM1);
-  __builtin_amdgcn_sched_barrier(0);
+
+  // Tail-page refresh: wave 0 rebuilds the tail page's record, writes it
+  // back and scores the page; the chunk loop leaves that page alone.
+  const int jt = n - 1;
+  bool tail_ok = false;  // workgroup-uniform
+  int tail_p = -1;
+  if (refresh_tail && n > 0) {
+    tail_p = page_indices[tbase + jt];
+    tail_ok = tail_p >= 0 && tail_p < num_phys;  // else the stored record is scored unchanged
+  }
+  auto score_page = [&](const uint4& m, const uint4& M) -> float {
+    float gmax = -__builtin_inff();
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float acc = 0.0f;
+      acc = chunk_dot(qn[hh], m, acc, T{});
+      acc = chunk_dot(qp[hh], M, acc, T{});
+      gmax = fmaxf(gmax, sum16(acc));
+    }
+    return gmax;
+  };
+  __syncthreads();  // the chunk counter (waits for LDS and scalar loads only)
+  if (tail_ok && wave == 0) {
+    uint4 tmn, tmx;
+    const int valid = min(kPage, L - kPage * jt);
+    tile_minmax<T>(reinterpret_cast<const char*>(k_pool) + ((size_t)tail_p * Hkv + h) * kTileBytes,
+                   valid, lane, tmn, tmx);
+    if (writer && lane < 32)
+      st16(reinterpret_cast<char*>(meta) + (row * stride + jt) * 512 + (lane >> 4) * 256 + c * 16,
+           lane < 16 ? tmn : tmx);
+    const float gmax = score_page(tmn, tmx);
+    if (lane == 0) sh.u.s.key[jt] = score_key(gmax);
+  }
+
+  auto score = [&](int ci, const uint4 (&bm)[kChunkSteps], const uint4 (&bM)[kChunkSteps]) {
+#pragma unroll
+    for (int t = 0; t < kChunkSteps; ++t) {
+      const int j = ci * kChunkPages + 4 * t + slot;
+      // (branch-free: records of masked pages may hold anything; their
+      // score is replaced, never used)
+      const bool ok = j < n && !(tail_ok && j == jt);
+      const float gmax = score_page(bm[t], bM[t]);
+      if (c == 0 && ok) sh.u.s.key[j] = score_key(gmax);
+    }
+  };
+  auto grab = [&]() -> int {
+    int e = 0;
+    if (lane == 0) e = atomicAdd(&sh.chunk_cursor, 1);
+    return __builtin_amdgcn_readfirstlane(e);
+  };
+  // Double-buffered: while one buffer's chunk is scored the other's records
+  // are in flight; a scored buffer is refilled with the next chunk at once.
+  // The loop body has no early exit (chunks past the row are masked and
+  // only cost cache hits), so the memory-counter waits stay partial; the
+  // scheduling barriers keep the loads in issue order.
+  while (true) {
+    score(ca, bm0, bM0);
+    ca = grab();
+    issue(min(ca, nchunks), bm0, bM0);
+    __builtin_amdgcn_sched_barrier(0);
+    score(cb, bm1, bM1);
+    cb = grab();
+    issue(min(cb, nchunks), bm1, bM1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ca >= nchunks && cb >= nchunks) break;
+  }
 #pragma unroll
   for (int i = 0; i < kKeysPerThread; ++i) {
     const int j = tid + i * kRowThreads;
     if (j < n) sh.u.s.phys[j] = ph[i];
   }
-
-  // tail-page refresh by the wave that scores it
-  const int jt = n - 1;
-  const bool own_tail = refresh_tail && n > 0 && (jt >> 2) % kRowWaves == wave;
-  uint4 tmn = make_uint4(0, 0, 0, 0), tmx = tmn;
-  bool tail_ok = false;  // wave-uniform
-  if (own_tail) {
-    const int p = page_indices[tbase + jt];
-    if (p >= 0 && p < num_phys) {  // else the stored record is scored unchanged
-      const int valid = min(kPage, L - kPage * jt);
-      tile_minmax<T>(reinterpret_cast<const char*>(k_pool) + ((size_t)p * Hkv + h) * kTileBytes,
-                     valid, lane, tmn, tmx);
-      if (writer && lane < 32)
-        st16(reinterpret_cast<char*>(meta) + (row * stride + jt) * 512 + (lane >> 4) * 256 + c * 16,
-             lane < 16 ? tmn : tmx);
-      tail_ok = true;
-    }
-  }
-
-  auto score = [&](int s0, uint4 (&bm)[kBatch], uint4 (&bM)[kBatch]) {
-#pragma unroll
-    for (int t = 0; t < kBatch; ++t) {
-      const int j = (s0 + t) * kStepPages + wave * 4 + slot;
-      uint4 m = bm[t], M = bM[t];
-      if (tail_ok && j == jt) {
-        m = tmn;
-        M = tmx;
-      }
-      const bool ok = j < n;
-      float gmax = -__builtin_inff();
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float acc = 0.0f;
-        if (ok) {
-          acc = chunk_dot(qn[hh], m, acc, T{});
-          acc = chunk_dot(qp[hh], M, acc, T{});
-        }
-        acc = sum16(acc);
-        gmax = fmaxf(gmax, ok ? acc : -__builtin_inff());
-      }
-      if (c == 0 && ok) sh.u.s.key[j] = score_key(gmax);
-    }
-  };
-
-  for (int s = 0;;) {
-    score(s, bm0, bM0);
-    s += kBatch;
-    if (s >= nsteps) break;
-    issue(min(s + kBatch, last_batch), bm0, bM0);
-    __builtin_amdgcn_sched_barrier(0);
-    score(s, bm1, bM1);
-    s += kBatch;
-    if (s >= nsteps) break;
-    issue(min(s + kBatch, last_batch), bm1, bM1);
-    __builtin_amdgcn_sched_barrier(0);
+  if constexpr (WA::kQInLds) {
+    if (tid < GW * kRowBytes / 16) sh.q[tid] = qstage;
   }
   if (tid < 256) sh.hist[0][tid] = 0u;
 
