@@ -19,6 +19,8 @@ method:
             negative component -> min");
       §2.3  top-K pages by score, then attention over only those pages;
       §5.3  metadata refreshed every decode step.
+    Recall ground truth (what the §2.2 bound stands in for): each page's
+    largest q.k and its share of the softmax weight.
   * CS336 lecture 10 page ("推理"): §3.2 the decode token's K/V is appended
     to the cache before it attends, so the query attends every cached token;
     §5 (GQA) groups of query heads share one KV head; §9.2 PagedAttention's
@@ -267,6 +269,56 @@ def paged_decode(q, k_pool, v_pool, dtype: str, page_indptr, page_indices, seq_l
             for hq in range(h * g, (h + 1) * g):
                 out[b, hq], lse[b, hq] = softmax_attention(qv[b, hq], Kt, Vt, sm_scale)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Recall of the bound-based selection: what the bound stands in for
+# (TinyServe §2.2: the score bounds the page's largest attention logit, and
+# selecting 30% of the pages keeps most of what matters)
+# ---------------------------------------------------------------------------
+
+def page_true_scores(q, dtype: str, k_pool, page_indptr, page_indices, seq_lens,
+                     num_kv_heads: int, sm_scale: float, stride: Optional[int] = None):
+    """Per (b, h_kv, logical page j), float64:
+      max_logit[b, h, j] = max over the group's query heads and the page's
+        valid tokens of q.k (unscaled, like the bound it is compared with);
+      mass[b, h, j] = mean over the group's query heads of the softmax
+        weight (scale sm_scale, over every token of the sequence) that falls
+        on the page's tokens.
+    Entries j >= n_b are -inf (max_logit) and 0 (mass)."""
+    qv = values_f64(q, dtype)
+    kv = values_f64(k_pool, dtype)
+    B, Hq, D = qv.shape
+    g = Hq // num_kv_heads
+    ns = [num_pages(int(L)) for L in seq_lens]
+    if stride is None:
+        stride = max(ns)
+    max_logit = np.full((B, num_kv_heads, stride), -np.inf)
+    mass = np.zeros((B, num_kv_heads, stride))
+    for b in range(B):
+        L = int(seq_lens[b])
+        n = ns[b]
+        owner = np.repeat(np.arange(n), [valid_tokens(L, j) for j in range(n)])  # page of each token
+        for h in range(num_kv_heads):
+            Kt = gather_tokens(kv, page_indptr, page_indices, b, h, L, range(n))   # [L, D]
+            z = Kt @ qv[b, h * g:(h + 1) * g].T                                      # [L, g]
+            per_page_max = np.full((n, g), -np.inf)
+            np.maximum.at(per_page_max, owner, z)
+            max_logit[b, h, :n] = per_page_max.max(axis=1)
+            w = np.exp(sm_scale * (z - z.max(axis=0)))
+            w /= w.sum(axis=0)
+            page_w = np.zeros((n, g))
+            np.add.at(page_w, owner, w)
+            mass[b, h, :n] = page_w.mean(axis=1)
+    return max_logit, mass
+
+
+def recall_at_k(sel_row, count: int, truth_row, n: int, k: int) -> float:
+    """|selected pages & the min(k, n) pages of largest truth| / min(k, n),
+    the truth's top pages taken with topk_row's tie rule."""
+    ref = set(int(x) for x in topk_row(truth_row, n, k))
+    got = set(int(x) for x in sel_row[:int(count)])
+    return len(ref & got) / max(1, len(ref))
 
 
 # ---------------------------------------------------------------------------

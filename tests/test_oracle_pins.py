@@ -393,3 +393,111 @@ def test_geometry():
     assert O.valid_tokens(17, 1) == 1 and O.valid_tokens(32, 1) == 16
     with pytest.raises(ValueError):
         O.num_pages(0)
+
+
+# ---------------------------------------------------------------- recall ground truth
+
+def _recall_case(lens=(37, 80, 16, 1, 17), Hq=6, Hkv=2, D=16, seed=13):
+    c = workloads.build_case("r", len(lens), Hq, Hkv, D, list(lens), "bf16", seed, n_sentinel=3)
+    return c, case_np(c)
+
+
+def _true(d, c, q=None):
+    return O.page_true_scores(d["q"] if q is None else q, "bf16", d["k_pool"], d["page_indptr"],
+                              d["page_indices"], d["seq_lens"], c.Hkv, c.sm_scale)
+
+
+def test_true_scores_mass_sums_to_one_and_bound_holds():
+    c, d = _recall_case()
+    ml, mass = _true(d, c)
+    meta = O.build_page_meta(d["k_pool"], "bf16", d["page_indptr"], d["page_indices"], d["seq_lens"])
+    _, group = O.score_pages(d["q"], "bf16", meta, "bf16", d["page_indptr"], d["page_indices"], d["seq_lens"], c.Hkv)
+    for b, L in enumerate(d["seq_lens"]):
+        n = O.num_pages(L)
+        assert np.allclose(mass[b, :, :n].sum(-1), 1.0, atol=1e-12)
+        assert np.all(mass[b, :, n:] == 0) and np.all(np.isneginf(ml[b, :, n:]))
+        # the bound (rounded once to float32) is never below the true max logit,
+        # and a one-token page's box is that token, so the two coincide
+        tol = 4 * np.spacing(np.abs(group[b, :, :n]).astype(np.float32))
+        assert np.all(group[b, :, :n] >= ml[b, :, :n] - tol)
+        if L % 16 == 1:
+            assert np.allclose(group[b, :, n - 1], ml[b, :, n - 1], rtol=0, atol=float(tol[:, n - 1].max()))
+
+
+def test_true_scores_zero_query_is_uniform():
+    c, d = _recall_case()
+    q0 = np.zeros_like(d["q"])
+    ml, mass = _true(d, c, q0)
+    for b, L in enumerate(d["seq_lens"]):
+        n = O.num_pages(L)
+        assert np.all(ml[b, :, :n] == 0.0)
+        want = np.array([O.valid_tokens(L, j) for j in range(n)]) / L
+        assert np.allclose(mass[b, :, :n], want[None, :], rtol=0, atol=1e-15)
+
+
+def test_true_scores_follow_the_table_to_one_dominant_token():
+    # One key of logical page 3 of sequence 0 (through the permuted table) is
+    # set to 4q for its head: its page takes (almost) all the mass and its max
+    # logit is 4|q|^2, closed form; sequence 1 is untouched.
+    c, d = _recall_case(lens=(80, 40), Hq=2, Hkv=2)
+    kv = O.values_f64(d["k_pool"], "bf16") * 0.25
+    qv = O.values_f64(d["q"], "bf16")
+    p = O.physical_page(d["page_indptr"], d["page_indices"], 0, 3)
+    kv[p, 1, 5] = 4.0 * qv[0, 1]
+    d2 = dict(d, k_pool=bf16_bits(kv.astype(np.float32)))
+    ml, mass = O.page_true_scores(d["q"], "bf16", d2["k_pool"], d["page_indptr"], d["page_indices"],
+                                  d["seq_lens"], 2, 1.0)
+    big = 4.0 * float(qv[0, 1] @ qv[0, 1])
+    assert ml[0, 1, 3] == big
+    others = np.delete(np.arange(5), 3)
+    assert np.all(ml[0, 1, others] < big / 4)
+    # the other 79 logits are below big/4, so their total weight is below 79 exp(-3 big/4)
+    assert 1.0 - mass[0, 1, 3] < 79 * math.exp(-0.75 * big)
+
+
+def test_true_scores_scale_two_token_closed_form():
+    # Sequence of 17 tokens: page 0 has 16 copies of key a, page 1 one key b.
+    c, d = _recall_case(lens=(17,), Hq=1, Hkv=1, D=4)
+    q = np.array([[[1.0, 0.5, -1.0, 2.0]]])
+    a = np.array([0.5, 1.0, 0.0, -0.25])
+    bk = np.array([1.0, -1.0, 0.5, 1.0])
+    kv = np.zeros((d["k_pool"].shape[0], 1, 16, 4))
+    p0 = O.physical_page(d["page_indptr"], d["page_indices"], 0, 0)
+    p1 = O.physical_page(d["page_indptr"], d["page_indices"], 0, 1)
+    kv[p0, 0, :] = a
+    kv[p1, 0, 0] = bk
+    s = 0.75
+    ml, mass = O.page_true_scores(bf16_bits(q.astype(np.float32)), "bf16", bf16_bits(kv.astype(np.float32)),
+                                  d["page_indptr"], d["page_indices"], d["seq_lens"], 1, s)
+    za, zb = float(q[0, 0] @ a), float(q[0, 0] @ bk)
+    assert ml[0, 0, 0] == za and ml[0, 0, 1] == zb
+    w1 = math.exp(s * zb) / (16 * math.exp(s * za) + math.exp(s * zb))
+    assert abs(mass[0, 0, 1] - w1) < 1e-15 and abs(mass[0, 0, 0] - (1 - w1)) < 1e-15
+
+
+def test_true_mass_is_mean_over_group_heads():
+    # Two query heads share KV head 0: head 0 has q = 0 (uniform weights),
+    # head 1 puts everything on one token -> the mean is the average of the two.
+    c, d = _recall_case(lens=(32,), Hq=2, Hkv=1, D=4)
+    kv = np.zeros((d["k_pool"].shape[0], 1, 16, 4))
+    p1 = O.physical_page(d["page_indptr"], d["page_indices"], 0, 1)
+    kv[p1, 0, 7] = [8.0, 0, 0, 0]
+    q = np.array([[[0.0, 0, 0, 0], [8.0, 0, 0, 0]]])
+    ml, mass = O.page_true_scores(bf16_bits(q.astype(np.float32)), "bf16", bf16_bits(kv.astype(np.float32)),
+                                  d["page_indptr"], d["page_indices"], d["seq_lens"], 1, 1.0)
+    w_hot = math.exp(64.0) / (31 + math.exp(64.0))
+    assert abs(mass[0, 0, 1] - 0.5 * (0.5 + (w_hot + 15 * (1 - w_hot) / 31))) < 1e-15
+    assert ml[0, 0, 0] == 0.0 and ml[0, 0, 1] == 64.0
+
+
+def test_recall_at_k_hand_examples():
+    truth = np.array([5.0, 1.0, 4.0, 3.0, -1.0])
+    assert O.recall_at_k(np.array([2, 0, -1]), 2, truth, 5, 2) == 1.0
+    assert O.recall_at_k(np.array([2, 3]), 2, truth, 5, 2) == 0.5
+    assert O.recall_at_k(np.array([1, 4]), 2, truth, 5, 2) == 0.0
+    # only the first `count` entries count; k beyond n compares against every page
+    assert O.recall_at_k(np.array([0, 2, 3]), 1, truth, 5, 2) == 0.5
+    assert O.recall_at_k(np.arange(5), 5, truth, 5, 9) == 1.0
+    # ties at the K-th truth value go to the smaller page
+    assert O.recall_at_k(np.array([0, 1]), 2, np.array([2.0, 1.0, 1.0]), 3, 2) == 1.0
+    assert O.recall_at_k(np.array([0, 2]), 2, np.array([2.0, 1.0, 1.0]), 3, 2) == 0.5
