@@ -19,6 +19,8 @@ method:
             negative component -> min");
       §2.3  top-K pages by score, then attention over only those pages;
       §5.3  metadata refreshed every decode step.
+  * Vortex digest (optimisations; efficiency analysis): approximate radix
+    top-K that stops early and fills from the threshold bin at random.
     Recall ground truth (what the §2.2 bound stands in for): each page's
     largest q.k and its share of the softmax weight.
   * CS336 lecture 10 page ("推理"): §3.2 the decode token's K/V is appended
@@ -221,6 +223,93 @@ def topk_pages(group_scores, seq_lens, k: int):
             sel[b, h, :len(r)] = r
             cnt[b, h] = len(r)
     return sel, cnt
+
+
+# ---------------------------------------------------------------------------
+# Approximate radix top-K (Vortex digest, optimisations and efficiency
+# analysis: the radix select stops once it holds enough confident pages and
+# fills the rest by random sampling from the threshold bin)
+# ---------------------------------------------------------------------------
+
+def score_order_key(x) -> np.ndarray:
+    """fp32 scores -> uint32 keys with the same order (-0 taken as +0): a
+    non-negative float's bits with the top bit set, a negative float's bits
+    inverted."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).copy()
+    b[b == np.uint32(0x80000000)] = 0
+    neg = (b >> np.uint32(31)) == 1
+    return np.where(neg, ~b, b | np.uint32(0x80000000)).astype(np.uint32)
+
+
+def approx_topk_row(scores, n: int, k: int, digit_bits: int, min_confident: int, rand_u32: int):
+    """Approximate top-K of scores[:n] (fp32), in ascending page order.
+
+    Radix select on the order keys, most significant digit first, starting
+    at the highest bit where the row's keys differ, digit_bits bits a pass.
+    Each pass keeps the bin that holds the K_eff-th largest key; the pages in
+    higher bins are confident (certainly in the top K_eff). The passes stop
+    when the confident pages number at least min_confident, when the kept
+    bin's pages are exactly the ones still needed, or when no bits remain.
+    The r pages still needed are then drawn from the c pages of the kept bin
+    (in page order, ranks 0..c-1) by systematic sampling with a random start:
+    s = floor(rand_u32 * c / 2^32), and rank i is drawn when
+    (i*r + s) mod c >= c - r - every page of the bin has probability r/c.
+    Returns (selected pages, number of passes run)."""
+    n, k = int(n), int(k)
+    keff = min(k, n)
+    if keff == n:
+        return np.arange(n, dtype=np.int32), 0
+    keys = [int(v) for v in score_order_key(np.asarray(scores[:n], dtype=np.float32))]
+    kmin, kmax = min(keys), max(keys)
+    shift = (kmin ^ kmax).bit_length()          # bits below `shift` are still open
+    prefix = kmin >> shift
+    need = keff
+    confident = 0
+    passes = 0
+    while shift > 0:
+        nb = min(digit_bits, shift)
+        lo = shift - nb
+        hist = [0] * (1 << nb)
+        for key in keys:
+            if key >> shift == prefix:
+                hist[(key >> lo) & ((1 << nb) - 1)] += 1
+        above = 0
+        for d in range((1 << nb) - 1, -1, -1):     # the bin where the count from the top reaches `need`
+            if above + hist[d] >= need:
+                break
+            above += hist[d]
+        prefix = (prefix << nb) | d
+        shift = lo
+        need -= above
+        confident += above
+        passes += 1
+        if hist[d] == need or confident >= min_confident:
+            break
+    sel = [j for j in range(n) if keys[j] >> shift > prefix]
+    binned = [j for j in range(n) if keys[j] >> shift == prefix]
+    c, r = len(binned), need
+    start = (int(rand_u32) * c) >> 32
+    sel += [j for i, j in enumerate(binned) if (i * r + start) % c >= c - r]
+    assert len(sel) == keff
+    return np.array(sorted(sel), dtype=np.int32), passes
+
+
+def approx_topk_pages(group_scores, seq_lens, k: int, digit_bits: int, min_confident: int, row_rand):
+    """approx_topk_row over every (b, h) row; row_rand [B, Hkv] uint32 random
+    words (the method's random draws, passed in). Returns (sel [B, Hkv, k]
+    -1 padded, sel_count [B, Hkv], passes [B, Hkv])."""
+    B, Hkv, _ = group_scores.shape
+    sel = np.full((B, Hkv, k), -1, dtype=np.int32)
+    cnt = np.zeros((B, Hkv), dtype=np.int32)
+    passes = np.zeros((B, Hkv), dtype=np.int32)
+    for b in range(B):
+        n = num_pages(int(seq_lens[b]))
+        for h in range(Hkv):
+            r, p = approx_topk_row(group_scores[b, h], n, k, digit_bits, min_confident, int(row_rand[b, h]))
+            sel[b, h, :len(r)] = r
+            cnt[b, h] = len(r)
+            passes[b, h] = p
+    return sel, cnt, passes
 
 
 # ---------------------------------------------------------------------------

@@ -91,3 +91,71 @@ def sdpa_reference(qv: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: fl
     o = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale)
     lse = torch.logsumexp(scale * (k[0, 0] @ q[0, 0, 0]), dim=0)
     return o.view(-1).numpy(), float(lse)
+
+
+def approx_keys(s: np.ndarray) -> np.ndarray:
+    """IEEE-order integer keys of fp32 scores, computed from the bit patterns
+    with int64 arithmetic (independent of the oracle's key function)."""
+    bits = np.asarray(s, dtype=np.float32).view(np.uint32).astype(np.int64)
+    bits[bits == 0x80000000] = 0
+    return np.where(bits >= 0x80000000, 0xFFFFFFFF - bits, bits + 0x80000000)
+
+
+def check_approx_bins(approx_row, s: np.ndarray, k: int, w: int, mc: int, u: int):
+    """Approximate top-K (Vortex digest): every page in a higher bin than the
+    exact K-th largest key at the depth reached is kept, none from a lower
+    bin, K_eff distinct pages; min_confident = 0 stops after one pass."""
+    n = len(s)
+    keff = min(k, n)
+    sel, passes = approx_row(s, n, k, w, mc, u)
+    key = approx_keys(s)
+    T = np.sort(key)[::-1][keff - 1]
+    s0 = int(key.min() ^ key.max()).bit_length()
+    shift = max(0, s0 - passes * w)
+    hi, t = key >> shift, T >> shift
+    chosen = np.zeros(n, dtype=bool)
+    chosen[np.asarray(sel)] = True
+    assert len(sel) == keff and int(chosen.sum()) == keff
+    assert np.all(chosen[hi > t]) and not np.any(chosen[hi < t])
+    if mc == 0 and keff < n and s0 > 0:
+        assert passes == 1
+
+
+def check_approx_exact(approx_row, s: np.ndarray, k: int, w: int, u: int):
+    """With min_confident >= K_eff and distinct scores the result is the exact
+    top-K (a full sort), whatever the random word."""
+    n = len(s)
+    assert len(np.unique(s)) == n
+    sel, _ = approx_row(s, n, k, w, k, u)
+    want = np.sort(np.argsort(-s.astype(np.float64), kind="stable")[:min(k, n)])
+    assert list(np.asarray(sel)) == list(want)
+
+
+def check_approx_inclusion(approx_row, c: int = 7):
+    """Five high pages, a bin of c equal scores, lower pages below, K = 5 + r:
+    over the c random starts every bin page is drawn exactly r times (each has
+    probability r/c), each draw takes r of them and keeps the five."""
+    s = np.concatenate([np.array([9, 8, 7, 6, 5], np.float32), np.full(c, 2.0, np.float32),
+                        np.array([1, 0.5, -3], np.float32)])
+    s = s[np.random.default_rng(3).permutation(len(s))]
+    high = set(np.nonzero(s > 4)[0].tolist())
+    binp = set(np.nonzero(s == 2.0)[0].tolist())
+    for r in range(1, c + 1):
+        counts = dict.fromkeys(binp, 0)
+        subsets = set()
+        for st in range(c):
+            u = -(-(st << 32) // c)                       # smallest word with floor(u*c/2^32) = st
+            got = set(int(x) for x in approx_row(s, len(s), 5 + r, 8, 5 + r, u)[0])
+            assert high <= got and len(got & binp) == r
+            for j in got & binp:
+                counts[j] += 1
+            subsets.add(tuple(sorted(got)))
+        assert set(counts.values()) == {r}
+        assert len(subsets) == (1 if r == c else c)
+
+
+def check_approx_golden(approx_row, examples):
+    for ex in examples:
+        s = np.array(ex["scores"], dtype=np.float32)
+        sel, passes = approx_row(s, len(s), ex["k"], ex["digit_bits"], ex["min_confident"], ex["rand_u32"])
+        assert list(np.asarray(sel)) == ex["sel"] and passes == ex["passes"]

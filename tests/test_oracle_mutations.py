@@ -91,3 +91,65 @@ def test_sdpa_pin_catches_lost_scale_and_transposed_values():
     assert not np.allclose(o2, ro, atol=1e-6)
     o3, _ = O.softmax_attention(q, K, V.T.copy(), 0.35)      # transposed V
     assert not np.allclose(o3, ro, atol=1e-6)
+
+
+# ---------------------------------------------------------------- approximate top-K
+
+def _approx_variant(mutation):
+    """A test-local restatement of the approximate top-K with one switchable
+    mistake; mutation None must pass every pin."""
+    def row(scores, n, k, w, mc, u):
+        keff = min(k, n)
+        if keff == n:
+            return np.arange(n), 0
+        keys = [int(v) for v in pins.approx_keys(np.asarray(scores[:n], np.float32))]
+        kmin, kmax = min(keys), max(keys)
+        shift = 32 if mutation == "no_prefix_skip" else (kmin ^ kmax).bit_length()
+        prefix, need, conf, passes = kmin >> shift, keff, 0, 0
+        while shift > 0:
+            nb = min(w, shift)
+            lo = shift - nb
+            hist = [0] * (1 << nb)
+            for key in keys:
+                if key >> shift == prefix:
+                    hist[(key >> lo) & ((1 << nb) - 1)] += 1
+            above = 0
+            for d in range((1 << nb) - 1, -1, -1):
+                if above + hist[d] >= need:
+                    break
+                above += hist[d]
+            prefix, shift, need, conf, passes = (prefix << nb) | d, lo, need - above, conf + above, passes + 1
+            stop = conf < mc if mutation == "stop_inverted" else conf >= mc
+            if hist[d] == need or stop:
+                break
+        sel = [j for j in range(n) if keys[j] >> shift > prefix]
+        binned = [j for j in range(n) if keys[j] >> shift == prefix]
+        c, r = len(binned), need
+        st = (int(u) * c) >> 32
+        if mutation == "fill_first":
+            sel += binned[:r]
+        else:
+            sel += [j for i, j in enumerate(binned) if (i * r + st) % c >= c - r]
+        return np.array(sorted(sel)), passes
+    return row
+
+
+def _approx_pins(row):
+    from tests._util import golden
+    pins.check_approx_golden(row, golden("worked_examples.json")["approx_topk"])
+    pins.check_approx_inclusion(row)
+    rng = np.random.default_rng(11)
+    s = np.unique(rng.normal(0, 1, 2100).astype(np.float32))[:2000]
+    s = s[rng.permutation(len(s))]
+    pins.check_approx_exact(row, s, 100, 8, 77)
+    pins.check_approx_bins(row, s, 100, 8, 0, 77)
+
+
+def test_approx_pins_pass_the_faithful_restatement():
+    _approx_pins(_approx_variant(None))
+
+
+@pytest.mark.parametrize("mutation", ["no_prefix_skip", "stop_inverted", "fill_first"])
+def test_approx_pins_catch_mistakes(mutation):
+    with pytest.raises(AssertionError):
+        _approx_pins(_approx_variant(mutation))

@@ -501,3 +501,59 @@ def test_recall_at_k_hand_examples():
     # ties at the K-th truth value go to the smaller page
     assert O.recall_at_k(np.array([0, 1]), 2, np.array([2.0, 1.0, 1.0]), 3, 2) == 1.0
     assert O.recall_at_k(np.array([0, 2]), 2, np.array([2.0, 1.0, 1.0]), 3, 2) == 0.5
+
+
+# ---------------------------------------------------------------- approximate top-K
+
+def _dist_scores(dist, n, rng):
+    if dist == "bimodal":
+        s = np.where(rng.random(n) < 0.5, rng.normal(-3, 1, n), rng.normal(3, 1, n))
+    elif dist == "normal":
+        s = rng.normal(0, 1, n)
+    elif dist == "lognormal":
+        s = rng.lognormal(0, 1, n)
+    else:
+        s = rng.random(n)
+    return s.astype(np.float32)
+
+
+def test_approx_topk_golden():
+    pins.check_approx_golden(O.approx_topk_row, golden("worked_examples.json")["approx_topk"])
+
+
+@pytest.mark.parametrize("dist", ["bimodal", "normal", "lognormal", "uniform"])
+@pytest.mark.parametrize("w", [4, 8, 11, 13])
+def test_approx_topk_exact_when_confidence_never_suffices(dist, w):
+    rng = np.random.default_rng(w)
+    s = _dist_scores(dist, 3200, rng)
+    _, first = np.unique(s, return_index=True)
+    s = s[np.sort(first)][:3000]                          # distinct values, in draw order
+    pins.check_approx_exact(O.approx_topk_row, s, 150, w, int(rng.integers(0, 2**32)))
+
+
+@pytest.mark.parametrize("dist", ["bimodal", "normal", "lognormal", "uniform"])
+def test_approx_topk_bin_invariant(dist):
+    rng = np.random.default_rng(7)
+    for n, k, w, mc in [(3000, 150, 8, 0), (3000, 150, 11, 100), (512, 153, 8, 120), (8192, 128, 13, 64),
+                        (100, 99, 4, 0), (40, 1, 6, 0)]:
+        s = _dist_scores(dist, n, rng)
+        s[::9] = s[5]                                     # ties
+        pins.check_approx_bins(O.approx_topk_row, s, k, w, mc, int(rng.integers(0, 2**32)))
+
+
+def test_approx_topk_fill_has_equal_inclusion_probability():
+    pins.check_approx_inclusion(O.approx_topk_row)
+
+
+def test_approx_topk_all_equal_and_full_budget():
+    s = np.full(50, 1.5, np.float32)
+    sel, passes = O.approx_topk_row(s, 50, 10, 8, 0, 0)
+    assert len(sel) == 10 and passes == 0                # no open bit: the fill draws from all 50
+    sel2, _ = O.approx_topk_row(s, 50, 10, 8, 0, 2**31)
+    assert sel.tolist() != sel2.tolist()
+    sel, passes = O.approx_topk_row(np.arange(5, dtype=np.float32), 5, 9, 8, 0, 0)
+    assert sel.tolist() == list(range(5)) and passes == 0
+    # -0 and +0 share one key
+    assert O.score_order_key(np.array([-0.0, 0.0], np.float32)).tolist() == [0x80000000] * 2
+    assert O.score_order_key(np.array([-1.0, 1.0], np.float32)).tolist() == pins.approx_keys(
+        np.array([-1.0, 1.0], np.float32)).tolist()
