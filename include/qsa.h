@@ -130,6 +130,38 @@ qsa_status qsa_topk_pages(const qsa_dims* dims, const qsa_paged_kv* kv,
                           int32_t* sel, int32_t* sel_count, int32_t* sel_phys,
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Step 3, approximate - the randomised radix top-K of the Vortex digest
+ * (optimisations; efficiency analysis): the radix select stops once it holds
+ * enough confident pages and draws the rest at random from the threshold
+ * bin. Per (b, h) row, on the order-preserving keys of the fp32 scores (-0
+ * taken as +0), most significant digit first, starting at the highest bit
+ * where the row's keys differ, digit_bits (4..13) bits per pass:
+ *   - each pass keeps the bin holding the K_eff-th largest key; the pages in
+ *     higher bins are confident (certainly among the top K_eff);
+ *   - the passes stop when the confident pages number >= min_confident,
+ *     when the kept bin holds exactly the pages still needed, or when no
+ *     bit is left;
+ *   - the r pages still needed are drawn from the kept bin's c pages, taken
+ *     in page order with ranks i = 0..c-1, by systematic sampling with a
+ *     random start st = floor(row_rand[b][h] * c / 2^32): rank i is drawn
+ *     when (i*r + st) mod c >= c - r (each bin page has probability r/c).
+ * min_confident >= k never stops on confidence, so the result is the exact
+ * top-K except that equal scores at the threshold are drawn at random.
+ * row_rand: [B, Hkv] uint32 random words, device (the caller draws them).
+ * Outputs as in qsa_topk_pages (ascending page order, -1 padding,
+ * sel_phys nullable); passes (nullable) [B, Hkv] int32 = radix passes run
+ * (0 when K_eff = n_b or all scores are equal). Rows of up to 16384 pages.
+ * No workspace. Errors: QSA_ERR_INVALID_ARG for NULL inputs, k < 1,
+ * digit_bits outside 4..13, min_confident < 0 or stride < max n_b;
+ * QSA_ERR_UNSUPPORTED for stride > 16384. */
+qsa_status qsa_topk_pages_approx(const qsa_dims* dims, const qsa_paged_kv* kv,
+                                 const float* group_scores, int32_t stride,
+                                 int32_t k, int32_t digit_bits,
+                                 int32_t min_confident, const uint32_t* row_rand,
+                                 int32_t* sel, int32_t* sel_count,
+                                 int32_t* sel_phys, int32_t* passes,
+                                 hipStream_t stream);
+
 /* Step 4 - split-K flash-decode over the selected pages (TinyServe §2.3
  * stages 3-4; flash decoding per the CS336 page §9.2 and the Quail page).
  * For each (b, hq) with h = hq / g: attention of q[b][hq] over the valid

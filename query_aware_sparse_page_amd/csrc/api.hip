@@ -300,6 +300,33 @@ qsa_status qsa_topk_pages(const qsa_dims* dims, const qsa_paged_kv* kv, const fl
       "topk_pages launch");
 }
 
+qsa_status qsa_topk_pages_approx(const qsa_dims* dims, const qsa_paged_kv* kv,
+                                 const float* group_scores, int32_t stride, int32_t k,
+                                 int32_t digit_bits, int32_t min_confident,
+                                 const uint32_t* row_rand, int32_t* sel, int32_t* sel_count,
+                                 int32_t* sel_phys, int32_t* passes, hipStream_t stream) {
+  qsa_status s = check_dims(dims);
+  if (s != QSA_OK) return s;
+  int max_pages = 0;
+  if ((s = check_kv(dims, kv, false, &max_pages)) != QSA_OK) return s;
+  if (group_scores == nullptr || sel == nullptr || sel_count == nullptr || row_rand == nullptr)
+    return fail(QSA_ERR_INVALID_ARG, "group_scores/row_rand/sel/sel_count is NULL");
+  if (k < 1) return fail(QSA_ERR_INVALID_ARG, "k = %d (must be >= 1)", k);
+  if (digit_bits < 4 || digit_bits > 13)
+    return fail(QSA_ERR_INVALID_ARG, "digit_bits = %d (must be in 4..13)", digit_bits);
+  if (min_confident < 0)
+    return fail(QSA_ERR_INVALID_ARG, "min_confident = %d (must be >= 0)", min_confident);
+  if (stride > qsa::kTopkMaxPages)
+    return fail(QSA_ERR_UNSUPPORTED, "stride %d > %d pages per row", stride, qsa::kTopkMaxPages);
+  if (stride < max_pages)
+    return fail(QSA_ERR_INVALID_ARG, "stride %d < longest sequence's page count %d", stride,
+                max_pages);
+  return device_status(qsa::launch_topk_approx(common(dims, kv), group_scores, stride, k,
+                                               digit_bits, min_confident, row_rand, sel,
+                                               sel_count, sel_phys, passes, stream),
+                       "topk_pages_approx launch");
+}
+
 qsa_status qsa_decode_plan(const qsa_dims* dims, const int32_t* seq_lens_host, int32_t k,
                            int32_t* chunk_pages, int32_t* max_units) {
   qsa_status s = check_dims(dims);

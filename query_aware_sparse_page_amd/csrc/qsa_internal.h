@@ -45,6 +45,14 @@ constexpr int kTopkMaxPages = 16384;
 hipError_t launch_topk(const LaunchCommon& c, const float* group_scores, int stride, int k,
                        int* sel, int* sel_count, int* sel_phys, hipStream_t stream);
 
+// Approximate top-K (digit_bits-wide digits, early stop at min_confident
+// confident pages, random fill from the threshold bin driven by row_rand).
+// passes (nullable) receives each row's number of radix passes.
+hipError_t launch_topk_approx(const LaunchCommon& c, const float* group_scores, int stride, int k,
+                              int digit_bits, int min_confident, const uint32_t* row_rand,
+                              int* sel, int* sel_count, int* sel_phys, int* passes,
+                              hipStream_t stream);
+
 // Split-K decode (partials into `part`) followed by the log-sum-exp merge of
 // each (b, hq) into out / lse, which also folds in n_prefix shared-prefix
 // partials per query row laid out [Hkv][n_prefix][B*G] (cascade).

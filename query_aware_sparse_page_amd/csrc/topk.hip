@@ -2,16 +2,20 @@
 // the K highest-scoring pages; the Vortex digest names radix top-K as the
 // indexer's bottleneck).
 //
-// One workgroup per row. Scores map to order-preserving uint32 keys (-0 folded
-// onto +0), held in registers (each thread a contiguous run of pages; rows of
-// up to 16384 pages). An MSB-first radix select finds the K_eff-th largest
-// key T exactly, and how many keys equal to T are still needed (krem): it
-// starts below the bits that every key shares (from the block min and max)
-// and takes 13 bits per pass with an 8192-bin LDS histogram, so typical fp32
-// scores resolve in two passes. A compaction in page order then keeps every
-// page with key > T and the first krem pages with key == T - ties go to the
-// smaller page index and the output is in ascending page order; each kept
-// page's position comes from one block-wide scan of (greater, equal) counts.
+// Scores map to order-preserving uint32 keys (-0 folded onto +0), held in
+// registers. Rows of up to 1024 pages take one wave each (8-bit digits, no
+// workgroup barriers); longer rows one workgroup of 1024 threads each (up to
+// 16384 pages), each thread a contiguous run of pages. (The approximate
+// select below runs as a 256-thread workgroup for rows of up to 1024 pages.)
+// An MSB-first radix select finds the bin holding the K_eff-th largest key,
+// and how many of its keys are still needed (krem): it starts below the bits
+// that every key shares (from the row's min and max) and takes 8 bits per
+// pass (wave kernel) or about log2(n) + 2 bits (block kernel: at most 13, an
+// 8192-bin LDS histogram, so typical fp32 scores resolve in two passes); the
+// block kernel also stops once the bin holds exactly the keys still needed. A compaction in page order then keeps every
+// page above the bin and the first krem pages in it - ties go to the smaller
+// page index and the output is in ascending page order; each kept page's
+// position comes from one block-wide scan of (above, in-bin) counts.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -160,11 +164,27 @@ __global__ void __launch_bounds__(256) topk_wave_kernel(
   if (lane == 0) sel_count[row] = keff;
 }
 
-template <int kThreads, int kKeys>
+// Block kernel (one workgroup per row). kApprox = false is the exact select;
+// kApprox = true is the approximate select of the Vortex digest
+// (optimisations: radix top-K that terminates early once it holds enough
+// confident pages and fills the rest at random from the threshold bin):
+//   * digits are digit_bits wide (the exact select sizes them from n);
+//   * after each pass the pages in bins above the kept bin are confident;
+//     the passes stop once they number at least min_confident;
+//   * the r pages still needed come from the c pages of the kept bin, in
+//     page order (rank i), by systematic sampling with a random start
+//     st = floor(row_rand * c / 2^32): rank i is taken when
+//     (i*r + st) mod c >= c - r, so floor((i*r + st) / c) bin pages of lower
+//     rank are taken before it, and every bin page has probability r/c.
+// Both stop as soon as the kept bin is exactly the pages still needed (the
+// result is then the same as running to the last bit).
+template <int kThreads, int kKeys, bool kApprox>
 __global__ void __launch_bounds__(kThreads) topk_kernel(
     const float* __restrict__ group_scores, int stride, int Hkv, const int* __restrict__ seq_lens,
     const int* __restrict__ page_indptr, const int* __restrict__ page_indices, int k,
-    int* __restrict__ sel, int* __restrict__ sel_count, int* __restrict__ sel_phys) {
+    int digit_bits, int min_confident, const uint32_t* __restrict__ row_rand,
+    int* __restrict__ sel, int* __restrict__ sel_count, int* __restrict__ sel_phys,
+    int* __restrict__ passes_out) {
   constexpr int kWaves = kThreads / 64;
   constexpr int kRadixBits = 13;
   constexpr int kBins = 1 << kRadixBits;
@@ -172,7 +192,7 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t wsum[kWaves];
   __shared__ uint32_t wmin[kWaves], wmax[kWaves];
-  __shared__ uint32_t s_digit, s_krem;
+  __shared__ uint32_t s_digit, s_krem, s_bin;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -200,7 +220,10 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
       out[i] = i < n ? i : -1;
       if (outp) outp[i] = i < n ? table[i] : -1;
     }
-    if (tid == 0) sel_count[row] = keff;
+    if (tid == 0) {
+      sel_count[row] = keff;
+      if (passes_out) passes_out[row] = 0;
+    }
     return;
   }
 
@@ -229,17 +252,20 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
     kmax = max(kmax, wmax[w]);
   }
 
-  // Radix select of the keff-th largest key T, MSB first, starting below the
-  // bits every key shares; krem = how many keys equal to T are taken.
+  // Radix select, MSB first, starting below the bits every key shares. After
+  // the loop the kept bin is {keys with key >> shift == prefix}; krem of its
+  // pages are still needed.
   uint32_t krem = (uint32_t)keff;
-  uint32_t T = kmin;
+  uint32_t prefix = kmin;
+  int shift = 0;
+  int passes = 0;
   const uint32_t diff = kmin ^ kmax;
-  // digit width: about log2(n) + 2 bits, so the histogram stays small for
-  // short rows and a pass splits a long row finely
-  const int width = min(kRadixBits, max(4, 34 - __builtin_clz((uint32_t)n)));
+  // exact: digit width about log2(n) + 2 bits, so the histogram stays small
+  // for short rows and a pass splits a long row finely
+  const int width = kApprox ? digit_bits : min(kRadixBits, max(4, 34 - __builtin_clz((uint32_t)n)));
   if (diff != 0u) {
-    int shift = 32 - __builtin_clz(diff);          // bits below `shift` still open
-    uint32_t prefix = (uint32_t)((uint64_t)kmin >> shift);
+    shift = 32 - __builtin_clz(diff);               // bits below `shift` still open
+    prefix = (uint32_t)((uint64_t)kmin >> shift);
     while (shift > 0) {
       const int nb = shift < width ? shift : width;
       const int lo = shift - nb;
@@ -269,6 +295,7 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
           if (above < krem && above + cnt[i] >= krem) {
             s_digit = nbins - 1u - (uint32_t)(tid * kBinsPerThread + i);
             s_krem = krem - above;
+            s_bin = cnt[i];
           }
           above += cnt[i];
         }
@@ -276,33 +303,49 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
       __syncthreads();
       prefix = (prefix << nb) | s_digit;
       krem = s_krem;
+      const uint32_t bin = s_bin;
       shift = lo;
+      ++passes;
       __syncthreads();
+      if (bin == krem) break;                          // the whole bin is taken
+      if (kApprox && (uint32_t)keff - krem >= (uint32_t)min_confident) break;
     }
-    T = prefix;
   }
 
-  // Compaction in page order: one block scan of (greater, equal) counts.
+  // Compaction in page order: one block scan of (above the bin, in the bin)
+  // counts gives each kept page its output position.
   uint32_t gt_n = 0, eq_n = 0;
 #pragma unroll
   for (int i = 0; i < kKeys; ++i) {
     if (j0 + i < n) {
-      gt_n += keys[i] > T ? 1u : 0u;
-      eq_n += keys[i] == T ? 1u : 0u;
+      const uint32_t hi = (uint32_t)((uint64_t)keys[i] >> shift);
+      gt_n += hi > prefix ? 1u : 0u;
+      eq_n += hi == prefix ? 1u : 0u;
     }
   }
   uint32_t total;
   const uint32_t excl = block_excl_scan<kWaves>(gt_n | (eq_n << 16), wsum, &total);
   uint32_t gt_before = excl & 0xFFFFu;
   uint32_t eq_before = excl >> 16;
+  const uint32_t c = total >> 16;                     // pages in the kept bin
+  uint32_t st = 0;
+  if (kApprox) st = (uint32_t)(((uint64_t)row_rand[row] * c) >> 32);
+  // bin pages of rank < i that are taken
+  auto taken_before = [&](uint32_t i) -> uint32_t {
+    if (kApprox) return (i * krem + st) / c;
+    return i < krem ? i : krem;
+  };
 #pragma unroll
   for (int i = 0; i < kKeys; ++i) {
     const int j = j0 + i;
     if (j >= n) break;
-    const bool gt = keys[i] > T;
-    const bool eq = keys[i] == T;
-    if (gt || (eq && eq_before < krem)) {
-      const uint32_t pos = gt_before + (eq_before < krem ? eq_before : krem);
+    const uint32_t hi = (uint32_t)((uint64_t)keys[i] >> shift);
+    const bool gt = hi > prefix;
+    const bool eq = hi == prefix;
+    bool take = gt;
+    if (eq) take = kApprox ? (eq_before * krem + st) % c >= c - krem : eq_before < krem;
+    if (take) {
+      const uint32_t pos = gt_before + taken_before(eq_before);
       if (pos < (uint32_t)keff) {
         out[pos] = j;
         if (outp) outp[pos] = table[j];
@@ -315,7 +358,10 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
     out[i] = -1;
     if (outp) outp[i] = -1;
   }
-  if (tid == 0) sel_count[row] = keff;
+  if (tid == 0) {
+    sel_count[row] = keff;
+    if (passes_out) passes_out[row] = passes;
+  }
 }
 
 }  // namespace
@@ -333,11 +379,36 @@ hipError_t launch_topk(const LaunchCommon& c, const float* group_scores, int str
                        group_scores, stride, c.Hkv, rows, c.seq_lens, c.page_indptr, c.page_indices,
                        k, sel, sel_count, sel_phys);
   } else if (stride <= 1024 * 8) {
-    hipLaunchKernelGGL((topk_kernel<1024, 8>), grid, dim3(1024), 0, stream, group_scores, stride,
-                       c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, k, sel, sel_count, sel_phys);
+    hipLaunchKernelGGL((topk_kernel<1024, 8, false>), grid, dim3(1024), 0, stream, group_scores,
+                       stride, c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, k, 0, 0, nullptr,
+                       sel, sel_count, sel_phys, nullptr);
   } else if (stride <= kTopkMaxPages) {
-    hipLaunchKernelGGL((topk_kernel<1024, 16>), grid, dim3(1024), 0, stream, group_scores, stride,
-                       c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, k, sel, sel_count, sel_phys);
+    hipLaunchKernelGGL((topk_kernel<1024, 16, false>), grid, dim3(1024), 0, stream, group_scores,
+                       stride, c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, k, 0, 0, nullptr,
+                       sel, sel_count, sel_phys, nullptr);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_approx(const LaunchCommon& c, const float* group_scores, int stride, int k,
+                              int digit_bits, int min_confident, const uint32_t* row_rand,
+                              int* sel, int* sel_count, int* sel_phys, int* passes,
+                              hipStream_t stream) {
+  dim3 grid(c.Hkv, c.B);
+  if (stride <= 256 * 4) {
+    hipLaunchKernelGGL((topk_kernel<256, 4, true>), grid, dim3(256), 0, stream, group_scores,
+                       stride, c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, k, digit_bits,
+                       min_confident, row_rand, sel, sel_count, sel_phys, passes);
+  } else if (stride <= 1024 * 8) {
+    hipLaunchKernelGGL((topk_kernel<1024, 8, true>), grid, dim3(1024), 0, stream, group_scores,
+                       stride, c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, k, digit_bits,
+                       min_confident, row_rand, sel, sel_count, sel_phys, passes);
+  } else if (stride <= kTopkMaxPages) {
+    hipLaunchKernelGGL((topk_kernel<1024, 16, true>), grid, dim3(1024), 0, stream, group_scores,
+                       stride, c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, k, digit_bits,
+                       min_confident, row_rand, sel, sel_count, sel_phys, passes);
   } else {
     return hipErrorInvalidValue;
   }

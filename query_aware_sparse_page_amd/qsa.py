@@ -53,6 +53,7 @@ def lib():
             "qsa_build_page_meta": (i32, [D, KV, i32, vp, i32, vp]),
             "qsa_score_pages": (i32, [D, vp, KV, vp, vp, vp, i32, i32, vp]),
             "qsa_topk_pages": (i32, [D, KV, vp, i32, i32, vp, vp, vp, vp, sz, vp]),
+            "qsa_topk_pages_approx": (i32, [D, KV, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
             "qsa_paged_decode": (i32, [D, vp, KV, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
             "qsa_cascade_decode": (i32, [D, vp, vp, i32, KV, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
             "qsa_sparse_decode": (i32, [D, vp, KV, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, i32, vp,
@@ -190,6 +191,34 @@ def topk_pages(group_scores: torch.Tensor, kv: PagedKV, k: int, num_q_heads: Opt
     _check(L.qsa_topk_pages(ctypes.byref(d), ctypes.byref(s), _ptr(group_scores), stride, k, _ptr(sel),
                             _ptr(cnt), _ptr(phys), _ptr(ws), ws_bytes, _stream()))
     return sel, cnt, phys
+
+
+def topk_pages_approx(group_scores: torch.Tensor, kv: PagedKV, k: int, row_rand: torch.Tensor,
+                      digit_bits: int = 11, min_confident: Optional[int] = None,
+                      num_q_heads: Optional[int] = None, with_phys: bool = True,
+                      with_passes: bool = False, out=None):
+    """Approximate top-K (qsa_topk_pages_approx). row_rand: [B, Hkv] uint32
+    random words on the device (torch.int32 storage is accepted: the bits are
+    what count). min_confident defaults to k (exact except for the random
+    choice among equal threshold scores)."""
+    B, H, stride = group_scores.shape
+    dev = group_scores.device
+    if row_rand.shape != (B, H) or row_rand.element_size() != 4 or not row_rand.is_contiguous():
+        raise ValueError("row_rand must be a contiguous [B, Hkv] tensor of 32-bit words")
+    if min_confident is None:
+        min_confident = k
+    if out is None:
+        sel = torch.empty(B, H, k, dtype=torch.int32, device=dev)
+        cnt = torch.empty(B, H, dtype=torch.int32, device=dev)
+        phys = torch.empty(B, H, k, dtype=torch.int32, device=dev) if with_phys else None
+        passes = torch.empty(B, H, dtype=torch.int32, device=dev) if with_passes else None
+    else:
+        sel, cnt, phys, passes = out
+    d, s = kv.dims(num_q_heads), kv.struct()
+    _check(lib().qsa_topk_pages_approx(ctypes.byref(d), ctypes.byref(s), _ptr(group_scores), stride, k,
+                                       digit_bits, min_confident, _ptr(row_rand), _ptr(sel), _ptr(cnt),
+                                       _ptr(phys), _ptr(passes), _stream()))
+    return sel, cnt, phys, passes
 
 
 def decode_workspace_size(kv: PagedKV, num_q_heads: int, k: int = 0) -> int:

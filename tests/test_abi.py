@@ -166,3 +166,22 @@ def test_sparse_decode_validation(L):
     # the split path checks its workspace before launching anything
     st = call(args(path=qsa.PATHS["split"]))
     assert st == qsa.QSA_ERR_WORKSPACE and b"workspace" in L.qsa_last_error()
+
+
+def test_topk_approx_validation(L):
+    d = _dims()
+    lens = _lens([40, 40, 40, 40])                        # 3 pages each
+    kv = qsa.PagedKVStruct(1, 1, 10, 1, 1, 1, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)))
+    f = L.qsa_topk_pages_approx
+
+    def call(stride=8, k=2, bits=11, mc=2, rand=1, sel=1, cnt=1):
+        return f(ctypes.byref(d), ctypes.byref(kv), 1, stride, k, bits, mc, rand, sel, cnt, None, None, None)
+
+    assert call(rand=None) == qsa.QSA_ERR_INVALID_ARG and b"row_rand" in L.qsa_last_error()
+    assert call(sel=None) == qsa.QSA_ERR_INVALID_ARG
+    assert call(k=0) == qsa.QSA_ERR_INVALID_ARG
+    for bits in (3, 14):
+        assert call(bits=bits) == qsa.QSA_ERR_INVALID_ARG and b"digit_bits" in L.qsa_last_error()
+    assert call(mc=-1) == qsa.QSA_ERR_INVALID_ARG and b"min_confident" in L.qsa_last_error()
+    assert call(stride=2) == qsa.QSA_ERR_INVALID_ARG and b"stride" in L.qsa_last_error()
+    assert call(stride=20000) == qsa.QSA_ERR_UNSUPPORTED

@@ -303,3 +303,66 @@ CONFIGS = {
     "c4_long": c4_long,
     "c5_cascade": c5_cascade,
 }
+
+
+# ---------------------------------------------------------------------------
+# Score rows for the top-K microbenchmark and parity tests: the four score
+# distributions of the Vortex digest's top-K study (bimodal, normal,
+# lognormal, uniform), laid out as group scores [B, Hkv, stride] behind a
+# permuted page table. Selection reads only the scores, seq_lens and the
+# table, so the K/V pool is a one-page placeholder.
+# ---------------------------------------------------------------------------
+
+SCORE_DISTS = ("bimodal", "normal", "lognormal", "uniform")
+
+
+@dataclasses.dataclass
+class ScoreRows:
+    dist: str
+    scores: torch.Tensor            # float32 [B, Hkv, stride]; -inf past each row's n_b
+    row_rand: torch.Tensor          # int32 [B, Hkv]: uint32 random words (bit patterns)
+    seq_lens: torch.Tensor          # int32 [B]
+    page_indptr: torch.Tensor       # int32 [B+1]
+    page_indices: torch.Tensor      # int32 [sum n_b]
+    k_pool: torch.Tensor            # float32 [1, Hkv, 16, 64] placeholder (never read)
+
+    def to(self, device) -> "ScoreRows":
+        return dataclasses.replace(self, **{f.name: getattr(self, f.name).to(device)
+                                            for f in dataclasses.fields(self) if f.name != "dist"})
+
+
+def score_rows(dist: str, lens: List[int], Hkv: int, seed: int, stride: Optional[int] = None,
+               ties_every: int = 0) -> ScoreRows:
+    """Draw order: scores [B, Hkv, stride] (fp32, the distribution's own
+    parameters: bimodal = equal mixture of N(-3,1) and N(3,1), normal N(0,1),
+    lognormal with log-mean 0 and log-sd 1, uniform [0,1)), then the random
+    words, then the table permutation. ties_every = t > 0 sets every t-th
+    page of a row to the row's page-5 value (planted ties)."""
+    g = torch.Generator().manual_seed(seed)
+    B = len(lens)
+    nps = [n_pages(L) for L in lens]
+    stride = stride or max(nps)
+    shape = (B, Hkv, stride)
+    if dist == "bimodal":
+        pick = torch.rand(shape, generator=g) < 0.5
+        s = torch.where(pick, torch.randn(shape, generator=g) - 3.0, torch.randn(shape, generator=g) + 3.0)
+    elif dist == "normal":
+        s = torch.randn(shape, generator=g)
+    elif dist == "lognormal":
+        s = torch.exp(torch.randn(shape, generator=g))
+    elif dist == "uniform":
+        s = torch.rand(shape, generator=g)
+    else:
+        raise ValueError(dist)
+    s = s.float()
+    if ties_every > 0 and stride > 5:
+        s[:, :, ::ties_every] = s[:, :, 5:6]
+    for b, n in enumerate(nps):
+        s[b, :, n:] = float("-inf")
+    words = torch.randint(0, 2 ** 32, (B, Hkv), generator=g, dtype=torch.int64)
+    row_rand = torch.where(words >= 2 ** 31, words - 2 ** 32, words).to(torch.int32)
+    total = sum(nps)
+    perm = torch.randperm(total, generator=g).to(torch.int32)
+    indptr = torch.tensor([0] + list(torch.tensor(nps).cumsum(0).tolist()), dtype=torch.int32)
+    return ScoreRows(dist, s.contiguous(), row_rand, torch.tensor(lens, dtype=torch.int32), indptr, perm,
+                     torch.zeros(1, Hkv, PAGE_SIZE, 64, dtype=torch.float32))
