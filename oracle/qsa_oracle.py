@@ -19,6 +19,8 @@ method:
             negative component -> min");
       §2.3  top-K pages by score, then attention over only those pages;
       §5.3  metadata refreshed every decode step.
+  * Vortex digest (cache phase): a page's mean key (centroid) as an
+    alternative summary, scored by q . centroid.
   * Vortex digest (optimisations; efficiency analysis): approximate radix
     top-K that stops early and fills from the threshold bin at random.
     Recall ground truth (what the §2.2 bound stands in for): each page's
@@ -191,6 +193,74 @@ def score_pages(q, q_dtype: str, meta, meta_dtype: str, page_indptr, page_indice
                 h = hq // g
                 s = bound_score(qv[b, hq], mv[p, h, 0], mv[p, h, 1])
                 head[b, hq, j] = np.float32(s)
+        for h in range(num_kv_heads):
+            group[b, h, :ns[b]] = head[b, h * g:(h + 1) * g, :ns[b]].max(axis=0)
+    return head, group
+
+
+# ---------------------------------------------------------------------------
+# Centroid page summary (Vortex digest: the cache phase keeps each block's
+# mean key; the indexer scores blocks by the query's dot product with it)
+# ---------------------------------------------------------------------------
+
+def round_to_dtype(x, dtype: str) -> np.ndarray:
+    """float64 values -> the nearest `dtype` values (ties to even), as float64.
+    bf16: 8 significant bits (frexp gives |m| in [0.5, 1); rint rounds half to
+    even; ldexp is exact). f32: numpy's float64 -> float32 conversion."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def page_centroid(keys: np.ndarray) -> np.ndarray:
+    """keys [n_tokens, D] (float64, the page's valid tokens) -> their mean:
+    a correctly rounded float64 sum per dimension divided by the count."""
+    return np.array([math.fsum(keys[:, i]) for i in range(keys.shape[1])]) / keys.shape[0]
+
+
+def build_page_centroids(k_pool, dtype: str, page_indptr, page_indices, seq_lens,
+                         tail_pages: int = 0, init=None) -> np.ndarray:
+    """Centroids [P, Hkv, D] in the key dtype's stored form: the mean of each
+    page's valid keys rounded once to the key dtype. Pages not reached (or
+    outside the last tail_pages of each sequence when tail_pages > 0) keep
+    `init` (zeros if None)."""
+    kv = values_f64(k_pool, dtype)
+    P, Hkv, S, D = kv.shape
+    cent = np.zeros((P, Hkv, D)) if init is None else values_f64(init, dtype).copy()
+    for b in range(len(seq_lens)):
+        L = int(seq_lens[b])
+        n = num_pages(L, S)
+        first = 0 if tail_pages <= 0 else max(0, n - tail_pages)
+        for j in range(first, n):
+            p = physical_page(page_indptr, page_indices, b, j)
+            v = valid_tokens(L, j, S)
+            for h in range(Hkv):
+                cent[p, h] = round_to_dtype(page_centroid(kv[p, h, :v, :]), dtype)
+    return to_storage(cent, dtype)
+
+
+def centroid_scores(q, q_dtype: str, cent, cent_dtype: str, page_indptr, page_indices,
+                    seq_lens, num_kv_heads: int, stride: Optional[int] = None):
+    """(head_scores [B, Hq, stride], group_scores [B, Hkv, stride]), float32:
+    q . c_j exact in float64, rounded once to float32; the group score is the
+    max over the group's query heads (the same combination as the bound
+    score's); entries j >= n_b are -inf."""
+    qv = values_f64(q, q_dtype)
+    cv = values_f64(cent, cent_dtype)                    # [P, Hkv, D]
+    B, Hq, D = qv.shape
+    g = Hq // num_kv_heads
+    ns = [num_pages(int(L)) for L in seq_lens]
+    if stride is None:
+        stride = max(ns)
+    head = np.full((B, Hq, stride), -np.inf, dtype=np.float32)
+    group = np.full((B, num_kv_heads, stride), -np.inf, dtype=np.float32)
+    for b in range(B):
+        for j in range(ns[b]):
+            p = physical_page(page_indptr, page_indices, b, j)
+            for hq in range(Hq):
+                head[b, hq, j] = np.float32(math.fsum(qv[b, hq] * cv[p, hq // g]))
         for h in range(num_kv_heads):
             group[b, h, :ns[b]] = head[b, h * g:(h + 1) * g, :ns[b]].max(axis=0)
     return head, group

@@ -159,3 +159,31 @@ def check_approx_golden(approx_row, examples):
         s = np.array(ex["scores"], dtype=np.float32)
         sel, passes = approx_row(s, len(s), ex["k"], ex["digit_bits"], ex["min_confident"], ex["rand_u32"])
         assert list(np.asarray(sel)) == ex["sel"] and passes == ex["passes"]
+
+
+def rne_fraction(x: Fraction, bits: int = 8) -> Fraction:
+    """x rounded to `bits` significant bits, ties to even, in exact rational
+    arithmetic (Python's round() of a Fraction rounds half to even)."""
+    if x == 0:
+        return Fraction(0)
+    e = 0
+    a = abs(x)
+    while a >= 1:
+        a /= 2
+        e += 1
+    while a < Fraction(1, 2):
+        a *= 2
+        e -= 1
+    # x = sign * a * 2^e with a in [1/2, 1)
+    r = Fraction(round(a * 2 ** bits), 2 ** bits)
+    return (r if x > 0 else -r) * Fraction(2) ** e
+
+
+def check_centroid(page_centroid_rounded, keys: np.ndarray):
+    """Centroid summary (Vortex digest, cache phase): the exact mean of the
+    page's keys, rounded once to bf16 (8 significant bits, ties to even),
+    checked element by element in rational arithmetic."""
+    got = page_centroid_rounded(keys)
+    for i in range(keys.shape[1]):
+        mean = sum(Fraction(float(v)) for v in keys[:, i]) / keys.shape[0]
+        assert Fraction(float(got[i])) == rne_fraction(mean), (i, float(got[i]), float(mean))

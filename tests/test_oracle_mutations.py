@@ -153,3 +153,26 @@ def test_approx_pins_pass_the_faithful_restatement():
 def test_approx_pins_catch_mistakes(mutation):
     with pytest.raises(AssertionError):
         _approx_pins(_approx_variant(mutation))
+
+
+# ---------------------------------------------------------------- centroid
+
+def _centroid_sum(keys):
+    return O.round_to_dtype(keys.sum(0), "bf16")                     # no division
+
+
+def _centroid_over_16(keys):
+    return O.round_to_dtype(keys.sum(0) / 16.0, "bf16")              # full page assumed
+
+
+def _centroid_truncated(keys):
+    m, e = np.frexp(O.page_centroid(keys))
+    return np.ldexp(np.trunc(m * 256.0), e - 8)                     # rounds toward zero
+
+
+@pytest.mark.parametrize("bad", [_centroid_sum, _centroid_over_16, _centroid_truncated])
+def test_centroid_pin_catches_mistakes(bad):
+    keys = _bf16((5, 16))
+    pins.check_centroid(lambda k: O.round_to_dtype(O.page_centroid(k), "bf16"), keys)
+    with pytest.raises(AssertionError):
+        pins.check_centroid(bad, keys)

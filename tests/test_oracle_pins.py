@@ -557,3 +557,88 @@ def test_approx_topk_all_equal_and_full_budget():
     assert O.score_order_key(np.array([-0.0, 0.0], np.float32)).tolist() == [0x80000000] * 2
     assert O.score_order_key(np.array([-1.0, 1.0], np.float32)).tolist() == pins.approx_keys(
         np.array([-1.0, 1.0], np.float32)).tolist()
+
+
+# ---------------------------------------------------------------- centroid scorer
+
+def _centroid_bf16(keys):
+    return O.round_to_dtype(O.page_centroid(keys), "bf16")
+
+
+@pytest.mark.parametrize("valid", [1, 3, 7, 16])
+def test_centroid_exact_rational_mean_rounded_once(valid):
+    for _ in range(5):
+        pins.check_centroid(_centroid_bf16, bf16_values((valid, 24)))
+
+
+def test_round_to_bf16_ties_and_rational_check():
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, 255.5, 256.5, 257.0])
+    r = O.round_to_dtype(x, "bf16")
+    assert r.tolist() == [1.0, 1.0, 1 + 2 ** -6, -1.0, 0.0, 256.0, 256.0, 256.0]
+    v = RNG.standard_normal(300) * 10.0 ** RNG.integers(-3, 4, 300)
+    from fractions import Fraction
+    for xi, ri in zip(v, O.round_to_dtype(v, "bf16")):
+        assert Fraction(float(ri)) == pins.rne_fraction(Fraction(float(xi)))
+    assert np.array_equal(O.round_to_dtype(v, "f32"), v.astype(np.float32).astype(np.float64))
+
+
+def test_centroid_closed_forms():
+    k = bf16_values((1, 16))
+    assert np.array_equal(_centroid_bf16(np.repeat(k, 16, axis=0)), k[0])      # identical keys
+    assert np.array_equal(_centroid_bf16(k), k[0])                               # one token
+    assert np.all(_centroid_bf16(np.concatenate([k, -k])) == 0.0)               # symmetric pair
+
+
+def test_centroids_through_table_and_tail_pages():
+    c = workloads.build_case("t", 3, 4, 2, 16, [40, 16, 5], "bf16", 7, n_sentinel=3)
+    d = case_np(c)
+    cent = O.build_page_centroids(d["k_pool"], "bf16", d["page_indptr"], d["page_indices"], d["seq_lens"])
+    kv = O.values_f64(d["k_pool"], "bf16")
+    cv = O.values_f64(cent, "bf16")
+    from fractions import Fraction
+    for b, L in enumerate(d["seq_lens"]):
+        for j in range(O.num_pages(L)):
+            p = O.physical_page(d["page_indptr"], d["page_indices"], b, j)
+            v = O.valid_tokens(L, j)
+            for h in range(2):
+                for i in range(16):
+                    mean = sum(Fraction(float(x)) for x in kv[p, h, :v, i]) / v
+                    assert Fraction(float(cv[p, h, i])) == pins.rne_fraction(mean)
+    # tail-only rebuild touches exactly the last page of each sequence
+    init = np.full_like(cent, 0x3F80)                      # bf16 1.0
+    tail = O.build_page_centroids(d["k_pool"], "bf16", d["page_indptr"], d["page_indices"], d["seq_lens"],
+                                  tail_pages=1, init=init)
+    for b, L in enumerate(d["seq_lens"]):
+        n = O.num_pages(L)
+        for j in range(n):
+            p = O.physical_page(d["page_indptr"], d["page_indices"], b, j)
+            want = cent[p] if j == n - 1 else init[p]
+            assert np.array_equal(tail[p], want)
+
+
+def test_centroid_score_is_mean_logit_up_to_centroid_rounding():
+    # q . mean(k) = mean(q . k): the centroid score differs from the page's
+    # mean logit only through the centroid's rounding (at most half a bf16 ulp
+    # per element) and the final float32 rounding.
+    c = workloads.build_case("t", 2, 4, 2, 32, [48, 20], "bf16", 11)
+    d = case_np(c)
+    cent = O.build_page_centroids(d["k_pool"], "bf16", d["page_indptr"], d["page_indices"], d["seq_lens"])
+    head, group = O.centroid_scores(d["q"], "bf16", cent, "bf16", d["page_indptr"], d["page_indices"],
+                                    d["seq_lens"], 2, stride=5)
+    assert head.dtype == np.float32 and group.shape == (2, 2, 5)
+    assert np.all(np.isneginf(group[1, :, 2:]))
+    qv = O.values_f64(d["q"], "bf16")
+    kv = O.values_f64(d["k_pool"], "bf16")
+    cv = O.values_f64(cent, "bf16")
+    for b in range(2):
+        L = d["seq_lens"][b]
+        for j in range(O.num_pages(L)):
+            p = O.physical_page(d["page_indptr"], d["page_indices"], b, j)
+            v = O.valid_tokens(L, j)
+            for hq in range(4):
+                h = hq // 2
+                mean_logit = float(np.mean(kv[p, h, :v] @ qv[b, hq]))
+                slack = float(np.sum(np.abs(qv[b, hq]) * np.abs(cv[p, h]))) * 2.0 ** -8 + 1e-6
+                assert abs(float(head[b, hq, j]) - mean_logit) <= slack
+            for h in range(2):
+                assert group[b, h, j] == max(head[b, 2 * h, j], head[b, 2 * h + 1, j])
