@@ -116,6 +116,35 @@ qsa_status qsa_score_pages(const qsa_dims* dims, const void* q,
                            int32_t stride, int32_t refresh_tail,
                            hipStream_t stream);
 
+/* Alternative page summary - the centroid (Vortex digest, cache phase: each
+ * block's mean key, the summary its Block Top-K indexer scores). For each
+ * sequence b, logical page j (physical slot read through the page table) and
+ * KV head h: cent[b][h][j][:] = the mean of the page's valid keys, element
+ * by element, rounded once to dims->dtype (bf16: nearest, ties to even; the
+ * sum of a page's keys is exact in the fp64 the kernel sums in unless their
+ * magnitudes span more than ~2^41, and means below 2^-126 in magnitude are
+ * not supported). Layout [B, Hkv, stride, D] in dims->dtype, logical page
+ * order (one 256-byte row per page). tail_pages and stride as in
+ * qsa_build_page_meta. Reads kv->k_pool only. */
+qsa_status qsa_build_page_centroids(const qsa_dims* dims, const qsa_paged_kv* kv,
+                                    int32_t tail_pages, void* cent, int32_t stride,
+                                    hipStream_t stream);
+
+/* Centroid page score (Vortex digest, indexer phase of Block Top-K):
+ * s[b][hq][j] = q[b][hq] . cent[b][hq / g][j], fp32 accumulation;
+ * group_scores[b][h][j] = max over the g query heads of KV head h (the same
+ * combination as qsa_score_pages; the centroid score is not an upper bound
+ * of the page's logits, it is their mean up to the centroid's rounding).
+ * Outputs, -inf padding, stride and refresh_tail (which rebuilds the tail
+ * page's centroid from kv->k_pool, as qsa_build_page_centroids(tail_pages =
+ * 1) would) as in qsa_score_pages. The result feeds qsa_topk_pages and
+ * qsa_paged_decode unchanged. */
+qsa_status qsa_score_pages_centroid(const qsa_dims* dims, const void* q,
+                                    const qsa_paged_kv* kv, void* cent,
+                                    float* group_scores, float* head_scores,
+                                    int32_t stride, int32_t refresh_tail,
+                                    hipStream_t stream);
+
 /* Step 3 - top-K page selection per (sequence, KV head) (TinyServe §2.3; the
  * radix select of the Vortex digest, optimisations). For each (b, h):
  * the K_eff = min(k, n_b) logical pages with the largest group score, ties

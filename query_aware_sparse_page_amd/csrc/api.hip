@@ -271,6 +271,42 @@ qsa_status qsa_score_pages(const qsa_dims* dims, const void* q, const qsa_paged_
                        "score_pages launch");
 }
 
+qsa_status qsa_build_page_centroids(const qsa_dims* dims, const qsa_paged_kv* kv,
+                                   int32_t tail_pages, void* cent, int32_t stride,
+                                   hipStream_t stream) {
+  qsa_status s = check_dims(dims);
+  if (s != QSA_OK) return s;
+  int max_pages = 0;
+  if ((s = check_kv(dims, kv, false, &max_pages)) != QSA_OK) return s;
+  if (cent == nullptr) return fail(QSA_ERR_INVALID_ARG, "cent is NULL");
+  if (tail_pages < 0) return fail(QSA_ERR_INVALID_ARG, "tail_pages %d < 0", tail_pages);
+  if (stride < max_pages)
+    return fail(QSA_ERR_INVALID_ARG, "stride %d < longest sequence's page count %d", stride,
+                max_pages);
+  return device_status(
+      qsa::launch_build_centroids(common(dims, kv), max_pages, tail_pages, cent, stride, stream),
+      "build_page_centroids launch");
+}
+
+qsa_status qsa_score_pages_centroid(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv,
+                                    void* cent, float* group_scores, float* head_scores,
+                                    int32_t stride, int32_t refresh_tail, hipStream_t stream) {
+  qsa_status s = check_dims(dims);
+  if (s != QSA_OK) return s;
+  int max_pages = 0;
+  if ((s = check_kv(dims, kv, false, &max_pages)) != QSA_OK) return s;
+  if (q == nullptr || cent == nullptr || group_scores == nullptr)
+    return fail(QSA_ERR_INVALID_ARG, "q/cent/group_scores is NULL");
+  if (stride < max_pages)
+    return fail(QSA_ERR_INVALID_ARG, "stride %d < longest sequence's page count %d", stride,
+                max_pages);
+  if (refresh_tail != 0 && refresh_tail != 1)
+    return fail(QSA_ERR_INVALID_ARG, "refresh_tail %d (0 or 1)", refresh_tail);
+  return device_status(qsa::launch_score_centroid(common(dims, kv), q, cent, refresh_tail,
+                                                  group_scores, head_scores, stride, stream),
+                       "score_pages_centroid launch");
+}
+
 size_t qsa_topk_workspace_size(const qsa_dims* dims, int32_t max_pages, int32_t k) {
   (void)dims;
   (void)max_pages;

@@ -8,6 +8,10 @@
 // order, -0 < +0), so the result is exact and independent of reduction order.
 //
 // One wave per (page, KV head) tile (tile_minmax).
+//
+// The centroid summary (build_centroid_kernel) is the alternative page
+// summary of the Vortex digest's cache phase, laid out the same way with one
+// 256-byte row per page.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -46,7 +50,54 @@ __global__ void __launch_bounds__(256) build_meta_kernel(
   }
 }
 
+// Centroid summary (Vortex digest, cache phase: each block's mean key):
+// cent[b][h][j][:] = mean of the valid keys of logical page j, rounded once to
+// the key type (tile_mean). Same launch geometry as the min/max build; lanes
+// 0..15 write the 256-byte row.
+template <typename T>
+__global__ void __launch_bounds__(256) build_centroid_kernel(
+    const T* __restrict__ k_pool, int num_phys, int Hkv, const int* __restrict__ page_indptr,
+    const int* __restrict__ page_indices, const int* __restrict__ seq_lens, int tail_pages,
+    T* __restrict__ cent, int stride) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int b = blockIdx.y;
+  const int L = seq_lens[b];
+  if (L <= 0) return;
+  const int n = min((L + kPage - 1) / kPage, stride);
+  const int first = tail_pages > 0 ? (n > tail_pages ? n - tail_pages : 0) : 0;
+  const int tile = blockIdx.x * 4 + wave;
+  const int j = first + tile / Hkv;
+  const int h = tile - (tile / Hkv) * Hkv;
+  if (j >= n) return;
+  const int p = page_indices[page_indptr[b] + j];
+  if (p < 0 || p >= num_phys) return;
+  const int valid = min(kPage, L - kPage * j);
+  const char* src = reinterpret_cast<const char*>(k_pool) + ((size_t)p * Hkv + h) * kTileBytes;
+  const uint4 mean = tile_mean<T>(src, valid, lane);
+  if (lane < 16) {
+    char* dst = reinterpret_cast<char*>(cent) + (((size_t)b * Hkv + h) * stride + j) * kRowBytes;
+    st16(dst + lane * 16, mean);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_build_centroids(const LaunchCommon& c, int max_pages, int tail_pages, void* cent,
+                                  int stride, hipStream_t stream) {
+  const int pages = tail_pages > 0 ? (tail_pages < max_pages ? tail_pages : max_pages) : max_pages;
+  dim3 grid((pages * c.Hkv + 3) / 4, c.B);
+  if (c.bf16) {
+    hipLaunchKernelGGL(build_centroid_kernel<bf16s>, grid, dim3(256), 0, stream,
+                       static_cast<const bf16s*>(c.k_pool), c.num_phys, c.Hkv, c.page_indptr,
+                       c.page_indices, c.seq_lens, tail_pages, static_cast<bf16s*>(cent), stride);
+  } else {
+    hipLaunchKernelGGL(build_centroid_kernel<float>, grid, dim3(256), 0, stream,
+                       static_cast<const float*>(c.k_pool), c.num_phys, c.Hkv, c.page_indptr,
+                       c.page_indices, c.seq_lens, tail_pages, static_cast<float*>(cent), stride);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_build_meta(const LaunchCommon& c, int max_pages, int tail_pages, void* meta,
                              int stride, hipStream_t stream) {

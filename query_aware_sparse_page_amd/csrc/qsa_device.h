@@ -311,6 +311,67 @@ __device__ __forceinline__ void tile_minmax(const char* tile, int valid, int lan
   vmx = make_uint4(Ops::unkey(mx[0]), Ops::unkey(mx[1]), Ops::unkey(mx[2]), Ops::unkey(mx[3]));
 }
 
+// fp64 -> nearest bf16 (ties to even), as the bf16 bit pattern: the value is
+// rounded to 8 significant bits inside the fp64 encoding (a carry moves into
+// the exponent by itself), after which the conversion to fp32 is exact.
+// Values of magnitude below 2^-126 are not handled (bf16 subnormals).
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
+  unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  b += 0x00000FFFFFFFFFFFull + ((b >> 45) & 1ull);
+  b &= ~0x00001FFFFFFFFFFFull;
+  return __float_as_uint((float)__longlong_as_double((long long)b)) >> 16;
+}
+
+__device__ __forceinline__ double xshfl_d(double v, int mask) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = xshfl_u((uint32_t)b, mask);
+  const uint32_t hi = xshfl_u((uint32_t)(b >> 32), mask);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Mean of the valid rows of one (page, KV head) tile, element-wise, rounded
+// once to the element type: the row sums are taken in fp64 (the sum of up to
+// 16 bf16 values is exact there unless their magnitudes span more than about
+// 2^41), divided by `valid` in fp64 (correctly rounded), then rounded to bf16
+// (ties to even) or converted to fp32. Rows are distributed as in
+// tile_minmax; on return every lane holds the mean of chunk lane % 16.
+template <typename T>
+__device__ __forceinline__ uint4 tile_mean(const char* tile, int valid, int lane) {
+  constexpr int E = Elem<T>::kPerChunk;
+  uint4 rows[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) rows[r] = ld16(tile + r * 1024 + lane * 16);
+  double acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (4 * r + (lane >> 4) < valid) {
+      float f[E];
+      chunk_unpack(rows[r], f, T{});
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += (double)f[e];
+    }
+  }
+  const double count = (double)valid;
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    acc[e] += xshfl_d(acc[e], 16);
+    acc[e] += xshfl_d(acc[e], 32);
+    acc[e] = acc[e] / count;
+  }
+  if constexpr (E == 8) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = f64_to_bf16_rne(acc[2 * e]) | (f64_to_bf16_rne(acc[2 * e + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = __float_as_uint((float)acc[e]);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Orders this wave's LDS accesses before and after the call point (all lanes
 // of one wave; no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync() {

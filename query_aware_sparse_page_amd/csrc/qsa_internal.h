@@ -36,8 +36,16 @@ struct Partials {
 hipError_t launch_build_meta(const LaunchCommon& c, int max_pages, int tail_pages, void* meta,
                              int stride, hipStream_t stream);
 
+hipError_t launch_build_centroids(const LaunchCommon& c, int max_pages, int tail_pages, void* cent,
+                                  int stride, hipStream_t stream);
+
 hipError_t launch_score(const LaunchCommon& c, const void* q, void* meta, int refresh_tail,
                         float* group_scores, float* head_scores, int stride, hipStream_t stream);
+
+// Centroid scores q . c_j (records of one 256-byte row), same outputs.
+hipError_t launch_score_centroid(const LaunchCommon& c, const void* q, void* cent,
+                                 int refresh_tail, float* group_scores, float* head_scores,
+                                 int stride, hipStream_t stream);
 
 // Longest row the top-K kernel handles (pages): 1024 threads x 16 keys.
 constexpr int kTopkMaxPages = 16384;

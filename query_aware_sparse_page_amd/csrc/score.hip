@@ -17,6 +17,11 @@
 // bytes each). A wave covers 4 consecutive pages per step (2 KiB contiguous),
 // a workgroup (4 waves) 64 pages. Lane partials are summed over the row with
 // DPP; the group max over the g query heads is in-lane.
+//
+// kCentroid = true scores the centroid summary instead (Vortex digest: a
+// block's score is the query's dot product with its mean key): 256-byte
+// records [c], q unsplit, score = q . c_j, the same group max; the tail-page
+// refresh rebuilds the centroid (tile_mean).
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -25,7 +30,7 @@ namespace {
 
 constexpr int kScorePagesPerBlock = 64;
 
-template <typename T, int G>
+template <typename T, int G, bool kCentroid>
 __global__ void __launch_bounds__(256) score_kernel(
     const T* __restrict__ q, T* __restrict__ meta, int Hkv, const int* __restrict__ seq_lens,
     const int* __restrict__ page_indptr, const int* __restrict__ page_indices,
@@ -38,7 +43,8 @@ __global__ void __launch_bounds__(256) score_kernel(
   const int c = lane & 15;      // chunk within a metadata row
   const int slot = lane >> 4;   // which of the wave's 4 pages
   const int base_j = blockIdx.x * kScorePagesPerBlock;
-  char* mrow_base = reinterpret_cast<char*>(meta) + ((size_t)b * Hkv + h) * stride * 512;
+  constexpr int kRec = kCentroid ? kRowBytes : 2 * kRowBytes;  // bytes per page record
+  char* mrow_base = reinterpret_cast<char*>(meta) + ((size_t)b * Hkv + h) * stride * kRec;
 
   // Metadata loads first (any j < stride is in bounds), then the row length.
   constexpr int kSteps = kScorePagesPerBlock / 16;
@@ -48,26 +54,29 @@ __global__ void __launch_bounds__(256) score_kernel(
   for (int s = 0; s < kSteps; ++s) {
     jj[s] = base_j + s * 16 + wave * 4 + slot;
     if (jj[s] < stride) {
-      const char* rec = mrow_base + (size_t)jj[s] * 512;
+      const char* rec = mrow_base + (size_t)jj[s] * kRec;
       mrow[s] = ld16(rec + c * 16);
-      Mrow[s] = ld16(rec + 256 + c * 16);
+      if (!kCentroid) Mrow[s] = ld16(rec + 256 + c * 16);
     }
   }
-  // Query chunks of the group's heads, split by sign.
+  // Query chunks of the group's heads (split by sign for the bound).
   uint4 qn[G], qp[G];
   const int Hq = Hkv * G;
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     const char* qrow = reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G + hh) * kRowBytes;
     uint4 qc = ld16(qrow + c * 16);
-    chunk_sign_split(qc, qn[hh], qp[hh], T{});
+    if (kCentroid)
+      qn[hh] = qc;
+    else
+      chunk_sign_split(qc, qn[hh], qp[hh], T{});
   }
   const int L = seq_lens[b];
   const int n = L > 0 ? min((L + kPage - 1) / kPage, stride) : 0;
 
-  // Optional refresh of the tail page's metadata (the page a decode step
-  // appends to), by the wave whose slots hold it: min/max of its valid keys,
-  // written back and used for this score.
+  // Optional refresh of the tail page's record (the page a decode step
+  // appends to), by the wave whose slots hold it: min/max (or mean) of its
+  // valid keys, written back and used for this score.
   if (refresh_tail && n > 0) {
     const int jt = n - 1;
     const int off = jt - base_j;
@@ -77,15 +86,20 @@ __global__ void __launch_bounds__(256) score_kernel(
         const int valid = min(kPage, L - kPage * jt);
         const char* src = reinterpret_cast<const char*>(k_pool) + ((size_t)p * Hkv + h) * kTileBytes;
         uint4 vmn, vmx;
-        tile_minmax<T>(src, valid, lane, vmn, vmx);
-        if (lane < 32) st16(mrow_base + (size_t)jt * 512 + (lane >> 4) * 256 + c * 16, lane < 16 ? vmn : vmx);
+        if (kCentroid) {
+          vmn = tile_mean<T>(src, valid, lane);
+          if (lane < 16) st16(mrow_base + (size_t)jt * kRec + c * 16, vmn);
+        } else {
+          tile_minmax<T>(src, valid, lane, vmn, vmx);
+          if (lane < 32) st16(mrow_base + (size_t)jt * kRec + (lane >> 4) * 256 + c * 16, lane < 16 ? vmn : vmx);
+        }
         const int st = off >> 4;
         if (slot == (off & 3)) {
 #pragma unroll
           for (int s = 0; s < kSteps; ++s)
             if (s == st) {
               mrow[s] = vmn;
-              Mrow[s] = vmx;
+              if (!kCentroid) Mrow[s] = vmx;
             }
         }
       }
@@ -104,7 +118,7 @@ __global__ void __launch_bounds__(256) score_kernel(
       float acc = 0.0f;
       if (ok) {
         acc = chunk_dot(qn[hh], mrow[s], acc, T{});
-        acc = chunk_dot(qp[hh], Mrow[s], acc, T{});
+        if (!kCentroid) acc = chunk_dot(qp[hh], Mrow[s], acc, T{});
       }
       acc = sum16(acc);
       hs[hh] = ok ? acc : -__builtin_inff();
@@ -120,7 +134,7 @@ __global__ void __launch_bounds__(256) score_kernel(
   }
 }
 
-template <typename T>
+template <typename T, bool kCentroid>
 hipError_t launch_score_t(const LaunchCommon& c, const void* q, void* meta, int refresh_tail,
                           float* gs, float* hs, int stride, hipStream_t stream) {
   dim3 grid((stride + kScorePagesPerBlock - 1) / kScorePagesPerBlock, c.Hkv, c.B);
@@ -129,9 +143,9 @@ hipError_t launch_score_t(const LaunchCommon& c, const void* q, void* meta, int 
   const T* kp = static_cast<const T*>(c.k_pool);
 #define QSA_SCORE_CASE(GG)                                                                       \
   case GG:                                                                                       \
-    hipLaunchKernelGGL((score_kernel<T, GG>), grid, dim3(256), 0, stream, qq, mm, c.Hkv,      \
-                       c.seq_lens, c.page_indptr, c.page_indices, kp, c.num_phys, refresh_tail,  \
-                       gs, hs, stride);                                                          \
+    hipLaunchKernelGGL((score_kernel<T, GG, kCentroid>), grid, dim3(256), 0, stream, qq, mm,    \
+                       c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, kp, c.num_phys,        \
+                       refresh_tail, gs, hs, stride);                                            \
     break;
   switch (c.G) {
     QSA_SCORE_CASE(1)
@@ -149,10 +163,19 @@ hipError_t launch_score_t(const LaunchCommon& c, const void* q, void* meta, int 
 
 hipError_t launch_score(const LaunchCommon& c, const void* q, void* meta, int refresh_tail,
                         float* group_scores, float* head_scores, int stride, hipStream_t stream) {
-  return c.bf16 ? launch_score_t<bf16s>(c, q, meta, refresh_tail, group_scores, head_scores, stride,
-                                        stream)
-                : launch_score_t<float>(c, q, meta, refresh_tail, group_scores, head_scores, stride,
-                                        stream);
+  return c.bf16 ? launch_score_t<bf16s, false>(c, q, meta, refresh_tail, group_scores, head_scores,
+                                               stride, stream)
+                : launch_score_t<float, false>(c, q, meta, refresh_tail, group_scores, head_scores,
+                                               stride, stream);
+}
+
+hipError_t launch_score_centroid(const LaunchCommon& c, const void* q, void* cent,
+                                 int refresh_tail, float* group_scores, float* head_scores,
+                                 int stride, hipStream_t stream) {
+  return c.bf16 ? launch_score_t<bf16s, true>(c, q, cent, refresh_tail, group_scores, head_scores,
+                                              stride, stream)
+                : launch_score_t<float, true>(c, q, cent, refresh_tail, group_scores, head_scores,
+                                              stride, stream);
 }
 
 }  // namespace qsa

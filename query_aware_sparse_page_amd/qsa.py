@@ -52,6 +52,8 @@ def lib():
         sig = {
             "qsa_build_page_meta": (i32, [D, KV, i32, vp, i32, vp]),
             "qsa_score_pages": (i32, [D, vp, KV, vp, vp, vp, i32, i32, vp]),
+            "qsa_build_page_centroids": (i32, [D, KV, i32, vp, i32, vp]),
+            "qsa_score_pages_centroid": (i32, [D, vp, KV, vp, vp, vp, i32, i32, vp]),
             "qsa_topk_pages": (i32, [D, KV, vp, i32, i32, vp, vp, vp, vp, sz, vp]),
             "qsa_topk_pages_approx": (i32, [D, KV, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
             "qsa_paged_decode": (i32, [D, vp, KV, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
@@ -171,6 +173,36 @@ def score_pages(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor,
     d, s = kv.dims(Hq), kv.struct()
     _check(lib().qsa_score_pages(ctypes.byref(d), _ptr(q), ctypes.byref(s), _ptr(meta), _ptr(gs), _ptr(hs),
                                  stride, int(refresh_tail), _stream()))
+    return gs, hs
+
+
+def build_page_centroids(kv: PagedKV, cent: Optional[torch.Tensor] = None, tail_pages: int = 0,
+                         stride: Optional[int] = None):
+    """Centroids [B, Hkv, stride, D] (each page's mean key, in the key dtype)
+    in logical page order (stride defaults to the longest sequence's page
+    count, or cent's own stride)."""
+    if cent is None:
+        stride = stride or kv.max_pages()
+        cent = torch.zeros(kv.num_seqs, kv.num_kv_heads, stride, kv.head_dim,
+                           dtype=kv.k_pool.dtype, device=kv.k_pool.device)
+    stride = int(cent.shape[2])
+    d, s = kv.dims(), kv.struct()
+    _check(lib().qsa_build_page_centroids(ctypes.byref(d), ctypes.byref(s), tail_pages, _ptr(cent), stride,
+                                          _stream()))
+    return cent
+
+
+def score_pages_centroid(q: torch.Tensor, kv: PagedKV, cent: torch.Tensor, head_scores: bool = False,
+                         out: Optional[torch.Tensor] = None, refresh_tail: bool = False):
+    """Centroid scores q . c_j: [B, Hkv, stride] group max (and per-head
+    [B, Hq, stride]) with the centroids' stride."""
+    B, Hq, _ = q.shape
+    stride = int(cent.shape[2])
+    gs = out if out is not None else torch.empty(B, kv.num_kv_heads, stride, dtype=torch.float32, device=q.device)
+    hs = torch.empty(B, Hq, stride, dtype=torch.float32, device=q.device) if head_scores else None
+    d, s = kv.dims(Hq), kv.struct()
+    _check(lib().qsa_score_pages_centroid(ctypes.byref(d), _ptr(q), ctypes.byref(s), _ptr(cent), _ptr(gs),
+                                          _ptr(hs), stride, int(refresh_tail), _stream()))
     return gs, hs
 
 

@@ -185,3 +185,21 @@ def test_topk_approx_validation(L):
     assert call(mc=-1) == qsa.QSA_ERR_INVALID_ARG and b"min_confident" in L.qsa_last_error()
     assert call(stride=2) == qsa.QSA_ERR_INVALID_ARG and b"stride" in L.qsa_last_error()
     assert call(stride=20000) == qsa.QSA_ERR_UNSUPPORTED
+
+
+def test_centroid_validation(L):
+    d = _dims()
+    lens = _lens([40, 40, 40, 40])                        # 3 pages each
+    kv = qsa.PagedKVStruct(1, 1, 10, 1, 1, 1, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)))
+    st = L.qsa_build_page_centroids(ctypes.byref(d), ctypes.byref(kv), 0, None, 8, None)
+    assert st == qsa.QSA_ERR_INVALID_ARG and b"cent" in L.qsa_last_error()
+    st = L.qsa_build_page_centroids(ctypes.byref(d), ctypes.byref(kv), -1, 1, 8, None)
+    assert st == qsa.QSA_ERR_INVALID_ARG and b"tail_pages" in L.qsa_last_error()
+    st = L.qsa_build_page_centroids(ctypes.byref(d), ctypes.byref(kv), 0, 1, 2, None)
+    assert st == qsa.QSA_ERR_INVALID_ARG and b"stride" in L.qsa_last_error()
+    st = L.qsa_score_pages_centroid(ctypes.byref(d), 1, ctypes.byref(kv), None, 1, None, 8, 0, None)
+    assert st == qsa.QSA_ERR_INVALID_ARG and b"cent" in L.qsa_last_error()
+    st = L.qsa_score_pages_centroid(ctypes.byref(d), 1, ctypes.byref(kv), 1, 1, None, 8, 2, None)
+    assert st == qsa.QSA_ERR_INVALID_ARG and b"refresh_tail" in L.qsa_last_error()
+    st = L.qsa_score_pages_centroid(ctypes.byref(_dims(D=96)), 1, ctypes.byref(kv), 1, 1, None, 8, 0, None)
+    assert st == qsa.QSA_ERR_UNSUPPORTED
