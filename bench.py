@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--replicas", type=int, default=4, help="KV pool copies rotated over steps")
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "split"],
                     help="kernels of a sparse step (auto: the library's choice)")
+    ap.add_argument("--scorer", default="bound", choices=["bound", "centroid"],
+                    help="page summary and score: the min/max upper bound, or the mean key "
+                         "(centroid; split path only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
@@ -137,7 +140,7 @@ def main():
         vp = case.v_pool if r == 0 else case.v_pool.clone()
         kv = qsa.PagedKV(kp, vp, case.page_indptr, case.page_indices, case.seq_lens, lens)
         kvs.append(kv)
-        metas.append(qsa.build_page_meta(kv))
+        metas.append(qsa.build_page_centroids(kv) if args.scorer == "centroid" else qsa.build_page_meta(kv))
     torch.cuda.synchronize()
 
     gs = torch.empty(B, Hkv, stride, dtype=torch.float32, device=dev)
@@ -152,11 +155,18 @@ def main():
         ws_bytes = qsa.decode_workspace_size(kvs[0], Hq, k or 0)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
-    path = qsa.sparse_decode_path(kvs[0], Hq, stride, k, args.path) if (k and not cascade) else None
+    centroid = args.scorer == "centroid"
+    if centroid and (not k or cascade or args.path == "fused"):
+        sys.exit("--scorer centroid needs a sparse workload on the split path")
+    path = qsa.sparse_decode_path(kvs[0], Hq, stride, k, "split" if centroid else args.path) \
+        if (k and not cascade) else None
 
     def stage_score(r):
         # scores with the tail page's metadata refreshed in the same launch
-        qsa.score_pages(case.q, kvs[r], metas[r], out=gs, refresh_tail=True)
+        if centroid:
+            qsa.score_pages_centroid(case.q, kvs[r], metas[r], out=gs, refresh_tail=True)
+        else:
+            qsa.score_pages(case.q, kvs[r], metas[r], out=gs, refresh_tail=True)
 
     def stage_topk(r):
         qsa.topk_pages(gs, kvs[r], k, num_q_heads=Hq, with_phys=False, out=(sel, cnt, None))
@@ -268,9 +278,10 @@ def main():
         dom_name, dom_bytes = "sparse_decode_fused", fz["total"]
         dom_kernel = "sparse_row_kernel (fused scores, top-K, decode and merge; one workgroup per row)"
     else:
-        sc = accounting.score_bytes(lens, Hq, Hkv, D, elem) if k else {"total": 0}
+        rows = 1 if centroid else 2
+        sc = accounting.score_bytes(lens, Hq, Hkv, D, elem, rows_per_record=rows) if k else {"total": 0}
         tk = accounting.topk_bytes(lens, Hkv, k) if k else {"total": 0}
-        mt = accounting.meta_bytes(lens, Hkv, D, elem, tail_pages=1) if k else {"total": 0}
+        mt = accounting.meta_bytes(lens, Hkv, D, elem, tail_pages=1, rows_per_record=rows) if k else {"total": 0}
         step_bytes = dec["total"] + sc["total"] + tk["total"] + mt["total"]
         dom_name, dom_bytes = "decode", dec["total"]
         dom_kernel = ("cascade prefix (MFMA) + split-K suffix decode + LSE merge" if cascade
@@ -300,6 +311,7 @@ def main():
             "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": 16,
             "budget_pages": k, "kv_pool_replicas": R, "timing": "hip graph replay" if graph else "eager",
             "path": path or ("cascade" if cascade else "dense"),
+            "scorer": args.scorer if k else None,
         },
         "effective_kv_gbps": round(dec["kv"] / (ms_step / 1e3) / 1e9, 1),
         "step_algorithmic_gbps": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
@@ -315,7 +327,7 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": measured_traffic(args.config, path),
+            "traffic": None if centroid else measured_traffic(args.config, path),
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": round(dom_ms, 5),
         },
@@ -356,11 +368,19 @@ def cpu_baseline(case, args, kv, meta):
         ip = np.array([0, len(phys)], dtype=np.int32)
         ix = np.arange(len(phys), dtype=np.int32)
         sl = np.array([lens[b]], dtype=np.int32)
-        meta0 = O.build_page_meta(pool_k, case.dtype, ip, ix, sl)
+        centroid = args.scorer == "centroid"
+        if centroid:
+            meta0 = O.build_page_centroids(pool_k, case.dtype, ip, ix, sl)
+        else:
+            meta0 = O.build_page_meta(pool_k, case.dtype, ip, ix, sl)
         t0 = time.perf_counter()
-        m1 = O.build_page_meta(pool_k, case.dtype, ip, ix, sl, tail_pages=1, meta_init=meta0)
+        if centroid:
+            m1 = O.build_page_centroids(pool_k, case.dtype, ip, ix, sl, tail_pages=1, init=meta0)
+        else:
+            m1 = O.build_page_meta(pool_k, case.dtype, ip, ix, sl, tail_pages=1, meta_init=meta0)
         if case.k_pages:
-            _, grp = O.score_pages(q, case.dtype, m1, case.dtype, ip, ix, sl, case.Hkv)
+            score = O.centroid_scores if centroid else O.score_pages
+            _, grp = score(q, case.dtype, m1, case.dtype, ip, ix, sl, case.Hkv)
             s, c = O.topk_pages(grp, sl, case.k_pages)
             O.paged_decode(q, pool_k, pool_v, case.dtype, ip, ix, sl, case.sm_scale, sel=s, sel_count=c)
         else:
@@ -375,7 +395,7 @@ def cpu_baseline(case, args, kv, meta):
         "cores": 1,
         "kind": "oracle",
         "sample": f"{done} decode queries (sequences of the batch, cycled), full step each: tail "
-                  f"metadata, scores, top-K, attention (NumPy fp64, BLAS 1 thread), {t_work:.1f} s of CPU work",
+                  f"{'centroid' if args.scorer == 'centroid' else 'metadata'}, scores, top-K, attention (NumPy fp64, BLAS 1 thread), {t_work:.1f} s of CPU work",
         "cpu": cpu_info(),
         "host_cpus_available": len(os.sched_getaffinity(0)),
     }

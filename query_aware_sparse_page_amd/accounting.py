@@ -52,11 +52,11 @@ def decode_bytes(seq_lens, Hq, Hkv, D, elem_bytes, k=None, page_size=16, with_ls
     return {"kv": kv, "q": q, "out": o, "table": table, "total": kv + q + o + table}
 
 
-def score_bytes(seq_lens, Hq, Hkv, D, elem_bytes, page_size=16):
-    """Scoring: every page's [m | M] metadata row per KV head, Q, and the
-    fp32 group scores written."""
+def score_bytes(seq_lens, Hq, Hkv, D, elem_bytes, page_size=16, rows_per_record=2):
+    """Scoring: every page's metadata record per KV head ([m | M]: two rows
+    of D; a centroid: one row), Q, and the fp32 group scores written."""
     n_tot = sum(pages(L, page_size) for L in seq_lens)
-    meta = n_tot * Hkv * 2 * D * elem_bytes
+    meta = n_tot * Hkv * rows_per_record * D * elem_bytes
     q = len(seq_lens) * Hq * D * elem_bytes
     out = n_tot * Hkv * 4
     table = n_tot * 4
@@ -69,14 +69,15 @@ def topk_bytes(seq_lens, Hkv, k, page_size=16):
     return {"scores": n_tot * Hkv * 4, "sel": B * Hkv * k * 4 * 2, "total": n_tot * Hkv * 4 + B * Hkv * k * 8}
 
 
-def meta_bytes(seq_lens, Hkv, D, elem_bytes, tail_pages=0, page_size=16):
-    """Metadata build: the keys of the (re)built pages in, [m | M] out."""
+def meta_bytes(seq_lens, Hkv, D, elem_bytes, tail_pages=0, page_size=16, rows_per_record=2):
+    """Metadata build: the keys of the (re)built pages in, their records
+    ([m | M], or a centroid row) out."""
     n = 0
     for L in seq_lens:
         np_ = pages(L, page_size)
         n += np_ if tail_pages <= 0 else min(tail_pages, np_)
     rd = n * Hkv * page_size * D * elem_bytes
-    wr = n * Hkv * 2 * D * elem_bytes
+    wr = n * Hkv * rows_per_record * D * elem_bytes
     return {"read": rd, "write": wr, "total": rd + wr}
 
 

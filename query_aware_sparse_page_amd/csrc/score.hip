@@ -15,8 +15,8 @@
 // is one contiguous stream of 512-byte [m | M] records. 16 lanes (one DPP
 // row) per page; lane c of the row holds chunk c of m and chunk c of M (16
 // bytes each). A wave covers 4 consecutive pages per step (2 KiB contiguous),
-// a workgroup (4 waves) 64 pages. Lane partials are summed over the row with
-// DPP; the group max over the g query heads is in-lane.
+// a workgroup (4 waves) 64 pages. Lane partials are summed
+// over the row with DPP; the group max over the g query heads is in-lane.
 //
 // kCentroid = true scores the centroid summary instead (Vortex digest: a
 // block's score is the query's dot product with its mean key): 256-byte

@@ -15,8 +15,12 @@ structure supports, each stated next to the chance level:
     share of attention mass;
   * the same drift at 8192 tokens: recall above 55% (chance: 30%).
 
-Ground truth is the oracle's per-page maximum logit and attention mass.
+Ground truth is the oracle's per-page maximum logit and attention mass. The
+same harness measures the centroid scorer (the Vortex digest's mean-key page
+summary, scored by q . centroid) on the same rows.
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -25,16 +29,37 @@ from oracle import qsa_oracle as O
 from tests._util import case_np
 
 
-def _recall_rows(case):
+CASES = {
+    "planted": lambda: workloads.c2_sparse(B=2),
+    "drift_long": lambda: workloads.c4_long(B=1),
+    "drift_8192": lambda: workloads.build_case("drift", 2, 32, 8, 128, [8192, 8192], "bf16", 5, k_pages=153,
+                                               drift=(0.9, 0.5)),
+}
+
+
+@functools.lru_cache(maxsize=None)
+def _case_and_truth(name):
+    case = CASES[name]()
+    d = case_np(case)
+    ml, mass = O.page_true_scores(d["q"], case.dtype, d["k_pool"], d["page_indptr"], d["page_indices"],
+                                  d["seq_lens"], case.Hkv, case.sm_scale)
+    return case, d, ml, mass
+
+
+@functools.lru_cache(maxsize=None)
+def _recall_rows(name, scorer="bound"):
     """Per (b, h): recall vs true max logit, recall vs attention mass, mass
     kept, best mass any k pages keep, and the chance level min(k, n)/n."""
-    d = case_np(case)
+    case, d, ml, mass = _case_and_truth(name)
     dt = case.dtype
-    meta = O.build_page_meta(d["k_pool"], dt, d["page_indptr"], d["page_indices"], d["seq_lens"])
-    _, group = O.score_pages(d["q"], dt, meta, dt, d["page_indptr"], d["page_indices"], d["seq_lens"], case.Hkv)
+    args = (d["page_indptr"], d["page_indices"], d["seq_lens"])
+    if scorer == "bound":
+        meta = O.build_page_meta(d["k_pool"], dt, *args)
+        _, group = O.score_pages(d["q"], dt, meta, dt, *args, case.Hkv)
+    else:
+        cent = O.build_page_centroids(d["k_pool"], dt, *args)
+        _, group = O.centroid_scores(d["q"], dt, cent, dt, *args, case.Hkv)
     sel, cnt = O.topk_pages(group, d["seq_lens"], case.k_pages)
-    ml, mass = O.page_true_scores(d["q"], dt, d["k_pool"], d["page_indptr"], d["page_indices"], d["seq_lens"],
-                                  case.Hkv, case.sm_scale)
     rows = []
     for b, L in enumerate(d["seq_lens"]):
         n = O.num_pages(int(L))
@@ -45,7 +70,7 @@ def _recall_rows(case):
                          float(mass[b, h, s].sum()),
                          float(np.sort(mass[b, h, :n])[::-1][:case.k_pages].sum()),
                          min(case.k_pages, n) / n))
-    return sel, cnt, np.array(rows)
+    return case, sel, cnt, np.array(rows)
 
 
 def _report(label, r):
@@ -54,10 +79,10 @@ def _report(label, r):
           f"mass kept {m[2]:.3f} of best {m[3]:.3f}  chance {m[4]:.3f}", flush=True)
 
 
-def test_planted_rows_keep_the_attention_mass():
-    case = workloads.c2_sparse(B=2)
-    sel, cnt, r = _recall_rows(case)
-    _report("8192 tokens, 5% planted, 30% budget", r)
+@pytest.mark.parametrize("scorer", ["bound", "centroid"])
+def test_planted_rows_keep_the_attention_mass(scorer):
+    case, sel, cnt, r = _recall_rows("planted", scorer)
+    _report(f"{scorer}: 8192 tokens, 5% planted, 30% budget", r)
     for b in range(case.B):
         planted = set(int(x) for x in case.planted[b])
         for h in range(case.Hkv):
@@ -66,23 +91,24 @@ def test_planted_rows_keep_the_attention_mass():
     assert r[:, 0].mean() > r[:, 4].mean() + 0.08
 
 
-def test_drifting_long_rows_beat_chance():
-    case = workloads.c4_long(B=1)
-    _, _, r = _recall_rows(case)
-    _report("131072 tokens, AR(1) drift, 128 pages", r)
+@pytest.mark.parametrize("scorer", ["bound", "centroid"])
+def test_drifting_long_rows_beat_chance(scorer):
+    _, _, _, r = _recall_rows("drift_long", scorer)
+    _report(f"{scorer}: 131072 tokens, AR(1) drift, 128 pages", r)
     assert r[:, 0].mean() >= 15 * r[:, 4].mean()
     assert r[:, 2].mean() >= 3 * r[:, 4].mean() and r[:, 2].mean() >= 0.6 * r[:, 3].mean()
 
 
-def test_drifting_rows_recall_at_30_percent():
-    case = workloads.build_case("drift", 2, 32, 8, 128, [8192, 8192], "bf16", 5, k_pages=153, drift=(0.9, 0.5))
-    _, _, r = _recall_rows(case)
-    _report("8192 tokens, AR(1) drift, 30% budget", r)
+@pytest.mark.parametrize("scorer", ["bound", "centroid"])
+def test_drifting_rows_recall_at_30_percent(scorer):
+    _, _, _, r = _recall_rows("drift_8192", scorer)
+    _report(f"{scorer}: 8192 tokens, AR(1) drift, 30% budget", r)
     assert r[:, 0].mean() >= 0.55 and r[:, 1].mean() >= 0.55
 
 
 @pytest.mark.parametrize("k", [64, 1000])
 def test_full_budget_recalls_everything(k):
-    case = workloads.build_case("all", 2, 4, 2, 32, [1000, 700], "bf16", 9, k_pages=k)
-    _, _, r = _recall_rows(case)
-    assert np.allclose(r[:, :2], 1.0) and np.allclose(r[:, 2], 1.0) and np.allclose(r[:, 2], r[:, 3])
+    CASES[f"all{k}"] = lambda: workloads.build_case("all", 2, 4, 2, 32, [1000, 700], "bf16", 9, k_pages=k)
+    for scorer in ("bound", "centroid"):
+        _, _, _, r = _recall_rows(f"all{k}", scorer)
+        assert np.allclose(r[:, :2], 1.0) and np.allclose(r[:, 2], 1.0) and np.allclose(r[:, 2], r[:, 3])
