@@ -6,24 +6,49 @@
 // Work unit = (sequence b, KV head h, a chunk of `chunk` consecutive entries
 // of the row's page list). The unit's workgroup has 4 waves; wave w takes
 // entries w, w+4, ... of the chunk and runs them through the per-wave
-// attention of decode_wave.h. Unit results (o unnormalised, max, sum) go to
+// attention: on the matrix cores (decode_mfma.h) for bf16 groups of 4 or
+// more heads, else on the vector ALU (decode_wave.h). Unit results (o unnormalised, max, sum) go to
 // the workspace and are merged per (b, hq) by merge_kernel. (Merging inside
 // the last-arriving unit would need device-scope release fences in every
 // unit; on this chip those write back the XCD's L2 and cost far more than the
 // separate launch.)
+#include "decode_mfma.h"
 #include "decode_wave.h"
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
 
+// bf16 groups of 4 or more query heads attend on the matrix cores
+// (decode_mfma.h); fp32 pools and smaller groups on the vector ALU
+// (decode_wave.h), where the products are too narrow to gain.
+template <typename T>
+struct IsBf16 {
+  static constexpr bool value = false;
+};
+template <>
+struct IsBf16<bf16s> {
+  static constexpr bool value = true;
+};
 template <typename T, int G>
+constexpr bool use_mfma() {
+  return IsBf16<T>::value && G >= 4;
+}
+
+template <typename T, int G, bool kMfma = use_mfma<T, G>()>
 struct DecodeShared {
   static constexpr int D = WaveAttn<T, G>::D;
   float p[4][WaveAttn<T, G>::kPBufFloats];  // per wave, double-buffered page probabilities
   float o[4][G][D];                         // per-wave results for the workgroup combine
   float ml[4][G][2];
   uint4 q[WaveAttn<T, G>::kQInLds ? G * kRowBytes / 16 : 1];  // the group's query rows
+};
+template <typename T, int G>
+struct DecodeShared<T, G, true> {
+  static constexpr int D = WaveAttnMfma<G>::D;
+  alignas(16) char v[4][WaveAttnMfma<G>::kLdsBytes];  // per wave, the staged V tiles
+  alignas(16) float o[4][G][D];
+  float ml[4][G][2];
 };
 
 template <typename T, int G>
@@ -38,6 +63,7 @@ decode_split_kernel(
   using WA = WaveAttn<T, G>;
   constexpr int EPC = WA::EPC;
   constexpr int D = WA::D;
+  constexpr bool kMfma = use_mfma<T, G>();
   __shared__ DecodeShared<T, G> sh;
 
   const int tid = threadIdx.x;
@@ -84,32 +110,39 @@ decode_split_kernel(
   }
 
   const char* qrows = reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G) * kRowBytes;
-  if constexpr (WA::kQInLds) {
-    if (tid < G * kRowBytes / 16) sh.q[tid] = ld16(qrows + tid * 16);
-    __syncthreads();
-    qrows = reinterpret_cast<const char*>(sh.q);
-  }
-  WA wa;
-  wa.init(qrows, lane);
   LanePages src{my_p, my_valid, npw};
-  wa.run(src, reinterpret_cast<const char*>(k_pool) + (size_t)h * kTileBytes,
-         reinterpret_cast<const char*>(v_pool) + (size_t)h * kTileBytes,
-         (size_t)Hkv * kTileBytes, scale_log2, sh.p[wave], lane);
-
-  // ---- wave epilogue, then the workgroup combine of the 4 waves -> one
-  // partial per (unit, head)
-  float mw, lw;
-  wa.reduce(&mw, &lw);
-  if (lane < 16) {
+  const char* kbase = reinterpret_cast<const char*>(k_pool) + (size_t)h * kTileBytes;
+  const char* vbase = reinterpret_cast<const char*>(v_pool) + (size_t)h * kTileBytes;
+  const size_t page_stride = (size_t)Hkv * kTileBytes;
+  if constexpr (kMfma) {
+    WaveAttnMfma<G> wa;
+    wa.init(qrows, lane);
+    wa.run(src, kbase, vbase, page_stride, scale_log2, sh.v[wave], lane);
+    wa.store(&sh.o[wave][0][0], &sh.ml[wave][0][0], lane);
+  } else {
+    if constexpr (WA::kQInLds) {
+      if (tid < G * kRowBytes / 16) sh.q[tid] = ld16(qrows + tid * 16);
+      __syncthreads();
+      qrows = reinterpret_cast<const char*>(sh.q);
+    }
+    WA wa;
+    wa.init(qrows, lane);
+    wa.run(src, kbase, vbase, page_stride, scale_log2, sh.p[wave], lane);
+    // ---- wave epilogue
+    float mw, lw;
+    wa.reduce(&mw, &lw);
+    if (lane < 16) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
+      for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) sh.o[wave][hh][lane * EPC + e] = wa.o[hh][e];
+        for (int e = 0; e < EPC; ++e) sh.o[wave][hh][lane * EPC + e] = wa.o[hh][e];
+    }
+    if (lane < G) {
+      sh.ml[wave][lane][0] = mw;
+      sh.ml[wave][lane][1] = lw;
+    }
   }
-  if (lane < G) {
-    sh.ml[wave][lane][0] = mw;
-    sh.ml[wave][lane][1] = lw;
-  }
+  // ---- the workgroup combine of the 4 waves -> one partial per (unit, head)
   __syncthreads();
 
   const size_t unit = row * (size_t)max_units + u;

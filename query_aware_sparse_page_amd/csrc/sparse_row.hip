@@ -36,6 +36,7 @@ static_assert(kRowThreads >= 256, "the radix histogram is cleared by 256 threads
 constexpr int kKeysPerThread = (kRowMaxPages + kRowThreads - 1) / kRowThreads;
 constexpr int kChunkSteps = 4;                 // score steps per chunk (4 pages a step)
 constexpr int kChunkPages = 4 * kChunkSteps;    // consecutive pages scored by one wave
+constexpr int kScoreBufs = 2;                   // chunks of records in flight per wave
 
 // Page buffers of the per-wave attention (see WaveAttn).
 constexpr int row_stages(int gw) { return 2; }
@@ -133,13 +134,15 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     qn[hh] = ld16(qrow + c * 16);
   }
   __builtin_amdgcn_sched_barrier(0);
-  uint4 bm0[kChunkSteps], bM0[kChunkSteps], bm1[kChunkSteps], bM1[kChunkSteps];
-  int ca = wave, cb = wave + kRowWaves;
-  issue(ca, bm0, bM0);
-  __builtin_amdgcn_sched_barrier(0);
-  issue(cb, bm1, bM1);
-  __builtin_amdgcn_sched_barrier(0);
-  if (tid == 0) sh.chunk_cursor = 2 * kRowWaves;
+  uint4 bm[kScoreBufs][kChunkSteps], bM[kScoreBufs][kChunkSteps];
+  int cc[kScoreBufs];
+#pragma unroll
+  for (int u = 0; u < kScoreBufs; ++u) {
+    cc[u] = wave + u * kRowWaves;
+    issue(cc[u], bm[u], bM[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (tid == 0) sh.chunk_cursor = kScoreBufs * kRowWaves;
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     const uint4 qc = qn[hh];
@@ -216,21 +219,22 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     if (lane == 0) e = atomicAdd(&sh.chunk_cursor, 1);
     return __builtin_amdgcn_readfirstlane(e);
   };
-  // Double-buffered: while one buffer's chunk is scored the other's records
-  // are in flight; a scored buffer is refilled with the next chunk at once.
-  // The loop body has no early exit (chunks past the row are masked and
-  // only cost cache hits), so the memory-counter waits stay partial; the
-  // scheduling barriers keep the loads in issue order.
+  // kScoreBufs buffers in rotation: while one buffer's chunk is scored the
+  // others' records are in flight; a scored buffer is refilled with the next
+  // chunk at once. The loop body has no early exit (chunks past the row are
+  // masked and only cost cache hits), so the memory-counter waits stay
+  // partial; the scheduling barriers keep the loads in issue order.
   while (true) {
-    score(ca, bm0, bM0);
-    ca = grab();
-    issue(min(ca, nchunks), bm0, bM0);
-    __builtin_amdgcn_sched_barrier(0);
-    score(cb, bm1, bM1);
-    cb = grab();
-    issue(min(cb, nchunks), bm1, bM1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (ca >= nchunks && cb >= nchunks) break;
+    bool more = false;
+#pragma unroll
+    for (int u = 0; u < kScoreBufs; ++u) {
+      score(cc[u], bm[u], bM[u]);
+      cc[u] = grab();
+      issue(min(cc[u], nchunks), bm[u], bM[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      more |= cc[u] < nchunks;
+    }
+    if (!more) break;
   }
 #pragma unroll
   for (int i = 0; i < kKeysPerThread; ++i) {
