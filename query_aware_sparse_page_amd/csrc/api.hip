@@ -135,7 +135,9 @@ qsa::DecodePlan make_plan(const qsa_dims* d, const int32_t* lens, int32_t k) {
     total += (long long)d->num_kv_heads * c;
   }
   const long long per = (total + target_units() - 1) / target_units();
-  int chunk = (int)std::min<long long>(256, std::max<long long>(4, (per + 3) / 4 * 4));
+  // (at most 128 pages per unit: smaller units fill the last round of
+  // workgroups better on long rows, measured)
+  int chunk = (int)std::min<long long>(128, std::max<long long>(4, (per + 3) / 4 * 4));
   plan.chunk = chunk;
   plan.max_units = (maxc + chunk - 1) / chunk;
   return plan;

@@ -6,22 +6,27 @@
 // dense [R = B*g, D] block and the prefix a [D, prefix_len] block: a real
 // contraction, so it runs on the matrix cores (v_mfma_f32_16x16x32_bf16,
 // fp32 accumulate). Flash-attention style: a workgroup owns 128 query rows
-// (32 per wave, two 16-column tiles) and one split of the prefix keys; it
+// (8 waves, one 16-column tile each) and one split of the prefix keys; it
 // walks the split in blocks of 32 keys (two pages), keeping an online
 // softmax per query.
 //
 // Orientation: the wave computes S^T = K . Q^T (rows = keys, cols = queries),
 // so the probabilities come out of the MFMA already in the layout of the B
-// operand of O^T = V^T . P^T and never leave registers. K blocks are staged
-// row-major in LDS (padded rows: conflict-free operand reads), V blocks
-// transposed; both double-buffered, with the global loads of the next
-// kDepth blocks in flight in registers while a block is computed.
+// operand of O^T = V^T . P^T and never leave registers. K and V blocks are
+// staged row-major in LDS (16-byte stores into padded rows), double-buffered,
+// with the global loads of the next kDepth blocks in flight in registers
+// while a block is computed; the A operand V^T is read with
+// ds_read_b64_tr_b16, which transposes 4 keys x 16 dims on the way (a 16-lane
+// group's lane s reads key row key0 + s/4, dims d0 + 4 (s%4) .. +3, and lane
+// s receives V[key0 .. key0+3][d0 + s]).
 //
-// MFMA 16x16x32 operand layouts (lane l, g = l/16):
-//   A[i][k]: i = l%16, k = 8g .. 8g+7     B[k][j]: j = l%16, k = 8g .. 8g+7
-//   C[i][j]: j = l%16, i = 4g .. 4g+3
-// The k-slots 8g+e of a 32-key block hold keys 4g+e (e < 4) and 16+4g+e-4
-// (e >= 4): exactly the rows the two 16-key S^T tiles leave in lane l.
+// MFMA operand layouts (lane l, g = l/16):
+//   16x16x32: A[i][k]: i = l%16, k = 8g .. 8g+7     B[k][j]: j = l%16, k = 8g .. 8g+7
+//   16x16x16: A[i][k]: i = l%16, k = 4g .. 4g+3     B[k][j]: j = l%16, k = 4g .. 4g+3
+//   both:     C[i][j]: j = l%16, i = 4g .. 4g+3
+// S^T (16x16x32 over the head dim) leaves lane l the logits of keys 4g .. 4g+3
+// of each 16-key tile: the k-slots of the B operand of that tile's
+// 16x16x16 product O^T += V^T . P^T.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -32,12 +37,16 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kCD = 128;            // head dim
-constexpr int kQT = 2;              // 16-query tiles per wave
-constexpr int kRowsPerWG = 4 * 16 * kQT;
+constexpr int kWaves = 8;           // waves per workgroup
+constexpr int kQT = 1;              // 16-query tiles per wave (one: 114 VGPRs, 4 waves per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWG = kWaves * 16 * kQT;
+constexpr int kStageReps = 512 / kThreads;  // 16-byte K and V chunks a thread stages per block
+static_assert(kStageReps >= 1 && kStageReps * kThreads == 512, "a block is 32 keys x 16 chunks");
 constexpr int kKeyBlock = 32;       // keys per block
 constexpr int kDepth = 2;           // blocks whose global loads are in flight
 constexpr int kKPitch = kCD + 8;    // LDS row of K in bf16 (256 B + 16 B pad)
-constexpr int kVtRow = 36;          // LDS row of V^T in bf16 (32 keys + pad)
+constexpr int kVPitch = kCD + 16;   // LDS row of V in bf16 (256 B + 32 B pad)
 constexpr int kMaxSplitPages = 80;  // pages of one split (the host keeps splits <= 1056 tokens)
 constexpr float kCasTau = 8.0f;
 
@@ -46,19 +55,20 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x4_t mfma16k16(const uint2& a, const uint2& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                   __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
 }
 
 struct CascadeShared {
   alignas(16) uint16_t k[2][kKeyBlock][kKPitch];
-  alignas(16) uint16_t vt[2][kCD][kVtRow];
+  alignas(16) uint16_t v[2][kKeyBlock][kVPitch];
   int pg[kMaxSplitPages];
 };
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) cascade_prefix_kernel(
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(512 / kThreads))) cascade_prefix_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, int num_phys, int B, int Hkv, int G,
     const int* __restrict__ prefix_pages, int prefix_len, int split_tokens, int n_splits,
@@ -89,7 +99,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
   const int pg0 = kbeg / kPage;
 
   // the split's physical pages (-1: outside the prefix or out of range)
-  for (int i = tid; i < kMaxSplitPages; i += 256) {
+  for (int i = tid; i < kMaxSplitPages; i += kThreads) {
     const int pgi = pg0 + i;
     int p = -1;
     if (pgi < n_pre_pages && pgi * kPage < kend) {
@@ -118,47 +128,34 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
   const char* kbase = reinterpret_cast<const char*>(k_pool) + (size_t)h * kTileBytes;
   const char* vbase = reinterpret_cast<const char*>(v_pool) + (size_t)h * kTileBytes;
 
-  // Staging of block bi: thread -> K (key = idx/16, chunk = idx%16) and
-  // V (key = idx%32, chunk = idx/32) for idx = tid, tid + 256. Blocks past
-  // the split load its last block again (cache hits); keys past the split,
-  // or on pages out of range, are staged as zeros.
+  // Staging of block bi: chunk idx = tid + kThreads * rep (rep <
+  // kStageReps) is key idx / 16 (page idx / 256 of the block's two, row
+  // (idx / 16) % 16), 16-byte chunk idx % 16, of K and of V. Blocks past the
+  // split load its last block again (cache hits); keys past the split, or on
+  // pages out of range, are staged as zeros.
   const int last_blk = nblk > 0 ? nblk - 1 : 0;
-  auto key_src = [&](int bi, int key, const char* base) -> const char* {
-    const int gk = kbeg + min(bi, last_blk) * kKeyBlock + key;
-    const int p = sh.pg[min(gk, kend > 0 ? kend - 1 : 0) / kPage - pg0];
-    return base + (size_t)(p >= 0 ? p : 0) * page_stride + (gk & 15) * kRowBytes;
+  const int last_pg = kend > kbeg ? (kend - 1) / kPage - pg0 : 0;  // the split's last page (relative)
+  const int toff = ((tid >> 4) & 15) * kRowBytes + (tid & 15) * 16;
+  auto page_of = [&](int bi, int pg) -> int {  // physical page, -1 if out of range
+    return sh.pg[min(2 * min(bi, last_blk) + pg, last_pg)];
   };
-  auto issue = [&](int bi, uint4 (&kr)[2], uint4 (&vr)[2]) {
+  auto issue = [&](int bi, uint4 (&kr)[kStageReps], uint4 (&vr)[kStageReps]) {
 #pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int idx = tid + 256 * rep;
-      kr[rep] = ld16(key_src(bi, idx >> 4, kbase) + (idx & 15) * 16);
-      vr[rep] = ld16(key_src(bi, idx & 31, vbase) + (idx >> 5) * 16);
+    for (int rep = 0; rep < kStageReps; ++rep) {
+      const int idx = tid + kThreads * rep;
+      const size_t off = (size_t)max(page_of(bi, idx >> 8), 0) * page_stride + toff;
+      kr[rep] = ld16(kbase + off);
+      vr[rep] = ld16(vbase + off);
     }
   };
-  auto stage = [&](int bi, int buf, const uint4 (&kr)[2], const uint4 (&vr)[2]) {
+  auto stage = [&](int bi, int buf, const uint4 (&kr)[kStageReps], const uint4 (&vr)[kStageReps]) {
 #pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int idx = tid + 256 * rep;
-      {
-        const int key = idx >> 4;
-        const int gk = kbeg + bi * kKeyBlock + key;
-        const bool ok = bi < nblk && gk < kend && sh.pg[gk / kPage - pg0] >= 0;
-        *reinterpret_cast<uint4*>(&sh.k[buf][key][(idx & 15) * 8]) = ok ? kr[rep] : make_uint4(0, 0, 0, 0);
-      }
-      {
-        const int key = idx & 31;
-        const int chunk = idx >> 5;
-        const int gk = kbeg + bi * kKeyBlock + key;
-        const bool ok = bi < nblk && gk < kend && sh.pg[gk / kPage - pg0] >= 0;
-        const uint4 v = ok ? vr[rep] : make_uint4(0, 0, 0, 0);
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(&v);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sh.vt[buf][chunk * 8 + 2 * e][key] = (uint16_t)(w[e] & 0xFFFFu);
-          sh.vt[buf][chunk * 8 + 2 * e + 1][key] = (uint16_t)(w[e] >> 16);
-        }
-      }
+    for (int rep = 0; rep < kStageReps; ++rep) {
+      const int idx = tid + kThreads * rep;
+      const int key = idx >> 4;
+      const bool ok = bi < nblk && kbeg + bi * kKeyBlock + key < kend && page_of(bi, idx >> 8) >= 0;
+      *reinterpret_cast<uint4*>(&sh.k[buf][key][(idx & 15) * 8]) = ok ? kr[rep] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&sh.v[buf][key][(idx & 15) * 8]) = ok ? vr[rep] : make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -182,16 +179,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int qt = 0; qt < kQT; ++qt) sacc[kt][qt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // (ks outermost: the 2 x kQT accumulation chains interleave, so
+    // consecutive products never wait on each other's results)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 a[2];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&sh.k[buf][16 * kt + c16][8 * g4 + 32 * ks]);
+      for (int kt = 0; kt < 2; ++kt)
+        a[kt] = *reinterpret_cast<const uint4*>(&sh.k[buf][16 * kt + c16][8 * g4 + 32 * ks]);
 #pragma unroll
-        for (int qt = 0; qt < kQT; ++qt) sacc[kt][qt] = mfma16(a, qb[qt][ks], sacc[kt][qt]);
-      }
+      for (int qt = 0; qt < kQT; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) sacc[kt][qt] = mfma16(a[kt], qb[qt][ks], sacc[kt][qt]);
+    }
     // ---- online softmax over this block, per query column c16 of each tile
-    uint4 pb[kQT];
+    // (only a split's last block can hold keys past its end)
+    const bool full = kb + kKeyBlock <= kend;
+    uint2 pt[kQT][2];  // B operands: P^T of key tile 0 and 1 (keys 4g .. 4g+3)
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
       float s[8];
@@ -200,14 +204,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int gk = kb + 16 * kt + 4 * g4 + i;
-          const float v = gk < kend ? sacc[kt][qt][i] * scale_log2 : -__builtin_inff();
-          s[4 * kt + i] = v;
-          mx = fmaxf(mx, v);
+          const float v = sacc[kt][qt][i] * scale_log2;
+          s[4 * kt + i] = (full || kb + 16 * kt + 4 * g4 + i < kend) ? v : -__builtin_inff();
+          mx = fmaxf(mx, s[4 * kt + i]);
         }
-      mx = fmaxf(mx, xshfl(mx, 16));
-      mx = fmaxf(mx, xshfl(mx, 32));
+      // the lane's own keys decide whether the reference must move (the
+      // ballot is the cross-lane OR); only then is the column max reduced
       if (__builtin_amdgcn_ballot_w64(mx > m_run[qt] + kCasTau) != 0) {
+        mx = fmaxf(mx, xshfl(mx, 16));
+        mx = fmaxf(mx, xshfl(mx, 32));
         const float mn = fmaxf(m_run[qt], mx);
         const float al = (mn == -__builtin_inff()) ? 1.0f : fast_exp2(m_run[qt] - mn);
         m_run[qt] = mn;
@@ -215,35 +220,42 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) oacc[qt][dt] *= al;
       }
-      // k-slot 8g+e holds s[e]: key 4g+e of tile 0 (e < 4), of tile 1 (e >= 4)
+      // m_run is finite from the first block on (its first key lies inside
+      // the split, so every column has a finite logit there and the
+      // reference moves); bf16 weights, rounded to nearest even in hardware
       uint32_t pk[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = (m_run[qt] == -__builtin_inff()) ? 0.0f : fast_exp2(s[2 * e] - m_run[qt]);
-        const float p1 = (m_run[qt] == -__builtin_inff()) ? 0.0f : fast_exp2(s[2 * e + 1] - m_run[qt]);
-        const uint32_t b0 = bf16_rne(p0), b1 = bf16_rne(p1);
+        const bf16x2_t w = {(__bf16)fast_exp2(s[2 * e] - m_run[qt]),
+                            (__bf16)fast_exp2(s[2 * e + 1] - m_run[qt])};
+        pk[e] = __builtin_bit_cast(uint32_t, w);
         // the denominator sums the same bf16-rounded weights the MFMA uses
-        l_part[qt] += __uint_as_float(b0 << 16) + __uint_as_float(b1 << 16);
-        pk[e] = b0 | (b1 << 16);
+        l_part[qt] += __uint_as_float(pk[e] << 16) + __uint_as_float(pk[e] & 0xFFFF0000u);
       }
-      pb[qt] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      pt[qt][0] = make_uint2(pk[0], pk[1]);
+      pt[qt][1] = make_uint2(pk[2], pk[3]);
     }
-    // ---- O^T += V^T . P^T : A rows = dims 16 dt + c16, k-slots as above
+    // ---- O^T += V^T . P^T, one 16x16x16 product per 16-key tile: A rows =
+    // dims 16 dt + c16, keys 4 g4 .. +3 of the tile, read transposed
+    typedef short lds_v4i16 __attribute__((ext_vector_type(4)));
+    const uint16_t* vsrc = &sh.v[buf][4 * g4 + (c16 >> 2)][4 * (c16 & 3)];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const uint16_t* vrow = &sh.vt[buf][16 * dt + c16][0];
-      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * g4);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g4);
-      const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
-      for (int qt = 0; qt < kQT; ++qt) oacc[qt][dt] = mfma16(a, pb[qt], oacc[qt][dt]);
+      for (int kt = 0; kt < 2; ++kt) {
+        const lds_v4i16 a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) lds_v4i16*)(vsrc + 16 * kt * kVPitch + 16 * dt));
+        const uint2 a = __builtin_bit_cast(uint2, a4);
+#pragma unroll
+        for (int qt = 0; qt < kQT; ++qt) oacc[qt][dt] = mfma16k16(a, pt[qt][kt], oacc[qt][dt]);
+      }
     }
   };
 
   // ---- pipeline: loads of blocks bi+1 .. bi+kDepth in flight while block
   // bi is computed; buffers rotate through an unrolled loop (no copies)
   if (nblk > 0) {
-    uint4 kr[kDepth][2], vr[kDepth][2];
+    uint4 kr[kDepth][kStageReps], vr[kDepth][kStageReps];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       issue(d, kr[d], vr[d]);
@@ -301,7 +313,7 @@ hipError_t launch_cascade_prefix(const LaunchCommon& c, const void* q, const int
   split_tokens = (split_tokens + kKeyBlock - 1) / kKeyBlock * kKeyBlock;
   if (split_tokens / kPage + 1 > kMaxSplitPages) return hipErrorInvalidValue;
   const int row_tiles = (R + kRowsPerWG - 1) / kRowsPerWG;
-  hipLaunchKernelGGL(cascade_prefix_kernel, dim3(row_tiles * c.Hkv * n_splits), dim3(256), 0, stream,
+  hipLaunchKernelGGL(cascade_prefix_kernel, dim3(row_tiles * c.Hkv * n_splits), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(c.k_pool),
                      static_cast<const uint16_t*>(c.v_pool), c.num_phys, c.B, c.Hkv, c.G,
                      prefix_pages, prefix_len, split_tokens, n_splits, scale_log2, prefix.o,

@@ -180,7 +180,7 @@ __global__ void __launch_bounds__(256) merge_kernel(
     const float* __restrict__ pre_ml, int n_pre, float* __restrict__ out,
     float* __restrict__ lse) {
   constexpr int PER = D / 64;
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;  // partial slots loaded per round (a cascade row has 8 prefix splits + suffix units)
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Hq = Hkv * G;

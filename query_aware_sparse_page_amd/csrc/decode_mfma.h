@@ -41,11 +41,7 @@ __device__ __forceinline__ mf_f32x4_t mfma_k16(const uint2& a, const uint2& b, m
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mf_i16x4_t, a),
                                                    __builtin_bit_cast(mf_i16x4_t, b), c, 0, 0, 0);
 }
-// fp32 -> bf16 bits, nearest even (finite inputs)
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+typedef __bf16 mf_bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Two page buffers (one page in flight while one is computed) measured
 // faster than three or four.
@@ -119,9 +115,14 @@ struct WaveAttnMfma {
       }
 
       // ---- S^T = K . Q^T: lane holds keys 4 grp + i of head c16
-      mf_f32x4_t s = mf_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) s = mfma_k32(kA[ks], qb[ks], s);
+      // (two accumulation chains, summed at the end, halve the dependent
+      // latency of the four products)
+      mf_f32x4_t s0 = mf_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
+      s0 = mfma_k32(kA[0], qb[0], s0);
+      s1 = mfma_k32(kA[1], qb[1], s1);
+      s0 = mfma_k32(kA[2], qb[2], s0);
+      s1 = mfma_k32(kA[3], qb[3], s1);
+      const mf_f32x4_t s = s0 + s1;
       float z[4];
       float mx = -__builtin_inff();
 #pragma unroll
@@ -129,10 +130,12 @@ struct WaveAttnMfma {
         z[i] = (4 * grp + i < valid) ? s[i] * scale_log2 : -__builtin_inff();
         mx = fmaxf(mx, z[i]);
       }
-      mx = fmaxf(mx, xshfl(mx, 16));
-      mx = fmaxf(mx, xshfl(mx, 32));
-      // ---- lazily moved reference max (every lane of a head agrees)
+      // ---- lazily moved reference max: the lane's own keys decide whether
+      // it must move (the ballot is the cross-lane OR); only then is the
+      // head's max reduced over the lane groups (every lane of a head agrees)
       if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyTau) != 0) {
+        mx = fmaxf(mx, xshfl(mx, 16));
+        mx = fmaxf(mx, xshfl(mx, 32));
         const float mn = fmaxf(m_run, mx);
         const float alpha = (mn == -__builtin_inff()) ? 1.0f : fast_exp2(m_run - mn);
         m_run = mn;
@@ -141,16 +144,26 @@ struct WaveAttnMfma {
         for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
       }
       // ---- probabilities: fp32 into the sum, hi + lo bf16 into the product
-      uint32_t hi[4], lo[4];
+      // (m_run is finite here: the wave's first attended page has a valid
+      // key in every column, so the reference moved on it; the bf16
+      // conversions round to nearest even in hardware)
+      float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = (m_run == -__builtin_inff()) ? 0.0f : fast_exp2(z[i] - m_run);
-        l_run += p;
-        hi[i] = f32_to_bf16_rne(p);
-        lo[i] = f32_to_bf16_rne(p - __uint_as_float(hi[i] << 16));
+        p[i] = fast_exp2(z[i] - m_run);
+        l_run += p[i];
       }
-      const uint2 phi = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-      const uint2 plo = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const mf_bf16x2_t h = {(__bf16)p[2 * e], (__bf16)p[2 * e + 1]};
+        hi[e] = __builtin_bit_cast(uint32_t, h);
+        const mf_bf16x2_t r = {(__bf16)(p[2 * e] - __uint_as_float(hi[e] << 16)),
+                               (__bf16)(p[2 * e + 1] - __uint_as_float(hi[e] & 0xFFFF0000u))};
+        lo[e] = __builtin_bit_cast(uint32_t, r);
+      }
+      const uint2 phi = make_uint2(hi[0], hi[1]);
+      const uint2 plo = make_uint2(lo[0], lo[1]);
       wave_lds_sync();  // the V tile stores, before the transposing reads
       // ---- O^T += V^T . P^T, dims 16 dt .. +15
       const char* vsrc = vt + (4 * grp + (c16 >> 2)) * (kVPitch * 2) + (c16 & 3) * 8;
