@@ -113,13 +113,7 @@ int device_cus() {
 
 // Work units wanted per launch: two 4-wave units per CU, i.e. two waves per
 // SIMD, so that every SIMD gets the same number of pages in one round.
-int target_units() {
-  static const int env = [] {
-    const char* e = std::getenv("QSA_DECODE_TARGET_UNITS");
-    return e ? std::atoi(e) : 0;
-  }();
-  return env > 0 ? env : 2 * device_cus();
-}
+int target_units() { return 2 * device_cus(); }
 
 // Pages per unit: a multiple of 4 (one quarter per wave) sized so that the
 // rows' pages fill about target_units() equal units; counts per (b, h) row are
