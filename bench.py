@@ -71,8 +71,7 @@ def parse():
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "split"],
                     help="kernels of a sparse step (auto: the library's choice)")
     ap.add_argument("--scorer", default="bound", choices=["bound", "centroid"],
-                    help="page summary and score: the min/max upper bound, or the mean key "
-                         "(centroid; split path only)")
+                    help="page summary and score: the min/max upper bound, or the mean key (centroid)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
@@ -156,10 +155,9 @@ def main():
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     centroid = args.scorer == "centroid"
-    if centroid and (not k or cascade or args.path == "fused"):
-        sys.exit("--scorer centroid needs a sparse workload on the split path")
-    path = qsa.sparse_decode_path(kvs[0], Hq, stride, k, "split" if centroid else args.path) \
-        if (k and not cascade) else None
+    if centroid and (not k or cascade):
+        sys.exit("--scorer centroid needs a sparse (non-cascade) workload")
+    path = qsa.sparse_decode_path(kvs[0], Hq, stride, k, args.path) if (k and not cascade) else None
 
     def stage_score(r):
         # scores with the tail page's metadata refreshed in the same launch
@@ -182,7 +180,7 @@ def main():
 
     def stage_fused(r):
         qsa.sparse_decode(case.q, kvs[r], metas[r], k, sm_scale=case.sm_scale, refresh_tail=True, path="fused",
-                          out=(out, lse))
+                          out=(out, lse), scorer=args.scorer)
 
     if path == "fused":
         stages = [("sparse_decode_fused", stage_fused)]
@@ -273,7 +271,7 @@ def main():
         dec["kv"] += pre_kv
         dec["total"] += pre_kv
     if path == "fused":
-        fz = accounting.fused_step_bytes(lens, Hq, Hkv, D, elem, k)
+        fz = accounting.fused_step_bytes(lens, Hq, Hkv, D, elem, k, rows_per_record=1 if centroid else 2)
         step_bytes = fz["total"]
         dom_name, dom_bytes = "sparse_decode_fused", fz["total"]
         dom_kernel = "sparse_row_kernel (fused scores, top-K, decode and merge; one workgroup per row)"

@@ -260,6 +260,22 @@ qsa_status qsa_sparse_decode(const qsa_dims* dims, const void* q,
                              int32_t* sel, int32_t* sel_count, qsa_path path,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* qsa_sparse_decode with the centroid scorer (Vortex digest, Block Top-K's
+ * mean-key summary): cent holds the centroid rows written by
+ * qsa_build_page_centroids ([B, Hkv, stride, D] in dims->dtype); computes
+ * exactly what qsa_score_pages_centroid(refresh_tail) -> qsa_topk_pages(k) ->
+ * qsa_paged_decode(sel) compute (refresh_tail rebuilds the tail page's
+ * centroid). Paths, limits, optional outputs and workspace as for
+ * qsa_sparse_decode (the same qsa_sparse_decode_path and workspace size). */
+qsa_status qsa_sparse_decode_centroid(const qsa_dims* dims, const void* q,
+                                      const qsa_paged_kv* kv, void* cent,
+                                      int32_t stride, int32_t refresh_tail,
+                                      int32_t k, float sm_scale, float* out,
+                                      float* lse, float* group_scores,
+                                      int32_t* sel, int32_t* sel_count,
+                                      qsa_path path, void* ws, size_t ws_bytes,
+                                      hipStream_t stream);
+
 /* The kernels qsa_sparse_decode will run for these arguments (QSA_PATH_FUSED
  * or QSA_PATH_SPLIT), in *chosen. */
 qsa_status qsa_sparse_decode_path(const qsa_dims* dims, const int32_t* seq_lens_host,

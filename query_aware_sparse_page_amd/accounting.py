@@ -81,15 +81,17 @@ def meta_bytes(seq_lens, Hkv, D, elem_bytes, tail_pages=0, page_size=16, rows_pe
     return {"read": rd, "write": wr, "total": rd + wr}
 
 
-def fused_step_bytes(seq_lens, Hq, Hkv, D, elem_bytes, k, page_size=16, with_lse=True):
+def fused_step_bytes(seq_lens, Hq, Hkv, D, elem_bytes, k, page_size=16, with_lse=True,
+                     rows_per_record=2):
     """One fused sparse decode step (scores, selection and attention in one
-    pass, nothing materialised between them): every page's [m | M] record,
-    the tail page's keys in and its record out, the page table, Q, the
-    selected pages' K and V, O and LSE."""
+    pass, nothing materialised between them): every page's record ([m | M],
+    or a centroid row), the tail page's keys in and its record out, the page
+    table, Q, the selected pages' K and V, O and LSE."""
     B = len(seq_lens)
     n_tot = sum(pages(L, page_size) for L in seq_lens)
-    meta = n_tot * Hkv * 2 * D * elem_bytes
-    tail = meta_bytes(seq_lens, Hkv, D, elem_bytes, tail_pages=1, page_size=page_size)["total"]
+    meta = n_tot * Hkv * rows_per_record * D * elem_bytes
+    tail = meta_bytes(seq_lens, Hkv, D, elem_bytes, tail_pages=1, page_size=page_size,
+                      rows_per_record=rows_per_record)["total"]
     kv = selected_tokens(seq_lens, k, page_size) * Hkv * D * 2 * elem_bytes
     q = B * Hq * D * elem_bytes
     o = B * Hq * D * 4 + (B * Hq * 4 if with_lse else 0)

@@ -489,11 +489,17 @@ size_t qsa_sparse_decode_workspace_size(const qsa_dims* dims, const int32_t* seq
   return sparse_ws(dims, seq_lens_host, stride, k).total();
 }
 
-qsa_status qsa_sparse_decode(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv, void* meta,
-                             int32_t stride, int32_t refresh_tail, int32_t k, float sm_scale,
-                             float* out, float* lse, float* group_scores, int32_t* sel,
-                             int32_t* sel_count, qsa_path path, void* ws, size_t ws_bytes,
-                             hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// One sparse decode step with the bound scorer or the centroid scorer (meta
+// then holds centroid rows).
+qsa_status sparse_decode_impl(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv,
+                              void* meta, int32_t stride, int32_t refresh_tail, int32_t k,
+                              float sm_scale, float* out, float* lse, float* group_scores,
+                              int32_t* sel, int32_t* sel_count, qsa_path path, void* ws,
+                              size_t ws_bytes, bool centroid, hipStream_t stream) {
   qsa_status s = check_dims(dims);
   if (s != QSA_OK) return s;
   int max_pages = 0;
@@ -514,8 +520,8 @@ qsa_status qsa_sparse_decode(const qsa_dims* dims, const void* q, const qsa_page
     const int rows = dims->num_seqs * dims->num_kv_heads;
     const int head_split = (c.G >= 2 && rows < device_cus()) ? 2 : 1;
     return device_status(qsa::launch_sparse_row(c, q, meta, stride, refresh_tail, k, scale_log2,
-                                                 head_split, out, lse, group_scores, sel, sel_count,
-                                                 stream),
+                                                 head_split, centroid, out, lse, group_scores, sel,
+                                                 sel_count, stream),
                          "sparse_decode (fused) launch");
   }
   const SparseWs w = sparse_ws(dims, kv->seq_lens_host, stride, k);
@@ -531,7 +537,9 @@ qsa_status qsa_sparse_decode(const qsa_dims* dims, const void* q, const qsa_page
   if (group_scores != nullptr) gs = group_scores;
   if (sel != nullptr) sl = sel;
   if (sel_count != nullptr) cn = sel_count;
-  hipError_t e = qsa::launch_score(c, q, meta, refresh_tail, gs, nullptr, stride, stream);
+  hipError_t e = centroid
+                    ? qsa::launch_score_centroid(c, q, meta, refresh_tail, gs, nullptr, stride, stream)
+                    : qsa::launch_score(c, q, meta, refresh_tail, gs, nullptr, stride, stream);
   if (e != hipSuccess) return device_status(e, "sparse_decode score launch");
   e = qsa::launch_topk(c, gs, stride, k, sl, cn, nullptr, stream);
   if (e != hipSuccess) return device_status(e, "sparse_decode top-K launch");
@@ -540,6 +548,28 @@ qsa_status qsa_sparse_decode(const qsa_dims* dims, const void* q, const qsa_page
   return device_status(qsa::launch_decode(c, q, sl, cn, k, scale_log2, plan, part, qsa::Partials{},
                                           0, out, lse, stream),
                        "sparse_decode decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+qsa_status qsa_sparse_decode(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv, void* meta,
+                             int32_t stride, int32_t refresh_tail, int32_t k, float sm_scale,
+                             float* out, float* lse, float* group_scores, int32_t* sel,
+                             int32_t* sel_count, qsa_path path, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  return sparse_decode_impl(dims, q, kv, meta, stride, refresh_tail, k, sm_scale, out, lse,
+                            group_scores, sel, sel_count, path, ws, ws_bytes, false, stream);
+}
+
+qsa_status qsa_sparse_decode_centroid(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv,
+                                      void* cent, int32_t stride, int32_t refresh_tail, int32_t k,
+                                      float sm_scale, float* out, float* lse, float* group_scores,
+                                      int32_t* sel, int32_t* sel_count, qsa_path path, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  return sparse_decode_impl(dims, q, kv, cent, stride, refresh_tail, k, sm_scale, out, lse,
+                            group_scores, sel, sel_count, path, ws, ws_bytes, true, stream);
 }
 
 }  // extern "C"

@@ -76,9 +76,11 @@ hipError_t launch_decode(const LaunchCommon& c, const void* q, const int* sel, c
 constexpr int kRowMaxPages = 4096;
 constexpr int kRowMaxSelect = 512;
 
+// centroid: meta holds centroid rows (256 bytes per page) scored as q . c
+// instead of [m | M] records scored by the bound.
 hipError_t launch_sparse_row(const LaunchCommon& c, const void* q, void* meta, int stride,
-                             int refresh_tail, int k, float scale_log2, int head_split, float* out,
-                             float* lse, float* group_scores, int* sel, int* sel_count,
+                             int refresh_tail, int k, float scale_log2, int head_split, bool centroid,
+                             float* out, float* lse, float* group_scores, int* sel, int* sel_count,
                              hipStream_t stream);
 
 // Cascade prefix on the matrix cores (bf16, D = 128): partials per

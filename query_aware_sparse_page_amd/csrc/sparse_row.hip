@@ -24,6 +24,9 @@
 //     paged attention of decode_wave.h.
 //  4. Merge: the 8 waves' (max, sum, o) are combined by log-sum-exp in LDS and
 //     the normalised output and LSE are written; no partials leave the chip.
+// kCentroid = true runs phase 1 on centroid rows instead (the Vortex digest's
+// mean-key page summary: 256-byte records scored as q . c, the tail page's
+// centroid rebuilt with tile_mean); phases 2-4 are unchanged.
 #include "decode_wave.h"
 #include "qsa_internal.h"
 
@@ -73,7 +76,7 @@ struct RowShared {
 // are dispatched to the same XCD (workgroups go round-robin over the 8 XCDs)
 // and share its L2 for the row's records and K/V tiles, which they stream in
 // the same order at the same time.
-template <typename T, int G, int S>
+template <typename T, int G, int S, bool kCentroid>
 __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     const T* __restrict__ q, T* __restrict__ meta, int stride, const T* __restrict__ k_pool,
     const T* __restrict__ v_pool, int num_phys, int Hkv, int rows,
@@ -115,15 +118,17 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   // page's score does not depend on which wave computes it).
   const int L = seq_lens[b];
   const int tbase = page_indptr[b];
-  const char* mrow = reinterpret_cast<const char*>(meta) + row * stride * 512;
+  // page records: [m | M] (512 bytes) or a centroid row (256 bytes)
+  constexpr int kRec = kCentroid ? kRowBytes : 2 * kRowBytes;
+  const char* mrow = reinterpret_cast<const char*>(meta) + row * stride * kRec;
   // Records of chunk ci (pages past the row read the last slot of the
   // row's stride, which is in bounds; their scores are masked).
   auto issue = [&](int ci, uint4 (&bm)[kChunkSteps], uint4 (&bM)[kChunkSteps]) {
 #pragma unroll
     for (int t = 0; t < kChunkSteps; ++t) {
       const int j = min(ci * kChunkPages + 4 * t + slot, stride - 1);
-      bm[t] = ld16(mrow + (size_t)j * 512 + c * 16);
-      bM[t] = ld16(mrow + (size_t)j * 512 + 256 + c * 16);
+      bm[t] = ld16(mrow + (size_t)j * kRec + c * 16);
+      if (!kCentroid) bM[t] = ld16(mrow + (size_t)j * kRec + 256 + c * 16);
     }
   };
   // the query rows first: the scores wait for them but not for the records
@@ -143,10 +148,12 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
   if (tid == 0) sh.chunk_cursor = kScoreBufs * kRowWaves;
+  if constexpr (!kCentroid) {
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const uint4 qc = qn[hh];
-    chunk_sign_split(qc, qn[hh], qp[hh], T{});
+    for (int hh = 0; hh < G; ++hh) {
+      const uint4 qc = qn[hh];
+      chunk_sign_split(qc, qn[hh], qp[hh], T{});
+    }
   }
   // (the host keeps rows within kRowMaxPages; the clamp guards the LDS arrays)
   const int n = L > 0 ? min(min((L + kPage - 1) / kPage, stride), kRowMaxPages) : 0;
@@ -185,7 +192,7 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     for (int hh = 0; hh < G; ++hh) {
       float acc = 0.0f;
       acc = chunk_dot(qn[hh], m, acc, T{});
-      acc = chunk_dot(qp[hh], M, acc, T{});
+      if (!kCentroid) acc = chunk_dot(qp[hh], M, acc, T{});
       gmax = fmaxf(gmax, sum16(acc));
     }
     return gmax;
@@ -194,11 +201,16 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   if (tail_ok && wave == 0) {
     uint4 tmn, tmx;
     const int valid = min(kPage, L - kPage * jt);
-    tile_minmax<T>(reinterpret_cast<const char*>(k_pool) + ((size_t)tail_p * Hkv + h) * kTileBytes,
-                   valid, lane, tmn, tmx);
-    if (writer && lane < 32)
-      st16(reinterpret_cast<char*>(meta) + (row * stride + jt) * 512 + (lane >> 4) * 256 + c * 16,
-           lane < 16 ? tmn : tmx);
+    const char* tile = reinterpret_cast<const char*>(k_pool) + ((size_t)tail_p * Hkv + h) * kTileBytes;
+    char* trec = reinterpret_cast<char*>(meta) + (row * stride + jt) * kRec;
+    if constexpr (kCentroid) {
+      tmn = tile_mean<T>(tile, valid, lane);
+      tmx = tmn;
+      if (writer && lane < 16) st16(trec + c * 16, tmn);
+    } else {
+      tile_minmax<T>(tile, valid, lane, tmn, tmx);
+      if (writer && lane < 32) st16(trec + (lane >> 4) * 256 + c * 16, lane < 16 ? tmn : tmx);
+    }
     const float gmax = score_page(tmn, tmx);
     if (lane == 0) sh.u.s.key[jt] = score_key(gmax);
   }
@@ -436,20 +448,20 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   }
 }
 
-template <typename T, int G, int S>
+template <typename T, int G, int S, bool kCentroid>
 void launch_row(const LaunchCommon& c, const void* q, void* meta, int stride, int refresh_tail,
                 int k, float scale_log2, float* out, float* lse, float* group_scores, int* sel,
                 int* sel_count, hipStream_t stream) {
   const int rows = c.B * c.Hkv;
   const int wgs = S == 1 ? rows : S * ((rows + 7) / 8 * 8);
-  hipLaunchKernelGGL((sparse_row_kernel<T, G, S>), dim3(wgs), dim3(kRowThreads), 0, stream,
+  hipLaunchKernelGGL((sparse_row_kernel<T, G, S, kCentroid>), dim3(wgs), dim3(kRowThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<T*>(meta), stride,
                      static_cast<const T*>(c.k_pool), static_cast<const T*>(c.v_pool), c.num_phys,
                      c.Hkv, rows, c.page_indptr, c.page_indices, c.seq_lens, refresh_tail, k,
                      scale_log2, out, lse, group_scores, sel, sel_count);
 }
 
-template <typename T>
+template <typename T, bool kCen>
 hipError_t launch_sparse_row_t(const LaunchCommon& c, const void* q, void* meta, int stride,
                                int refresh_tail, int k, float scale_log2, int head_split,
                                float* out, float* lse, float* group_scores, int* sel,
@@ -458,10 +470,10 @@ hipError_t launch_sparse_row_t(const LaunchCommon& c, const void* q, void* meta,
 #define QSA_ROW_ARGS c, q, meta, stride, refresh_tail, k, scale_log2, out, lse, group_scores, sel, \
                      sel_count, stream
   switch (c.G) {
-    case 1: launch_row<T, 1, 1>(QSA_ROW_ARGS); break;
-    case 2: two ? launch_row<T, 2, 2>(QSA_ROW_ARGS) : launch_row<T, 2, 1>(QSA_ROW_ARGS); break;
-    case 4: two ? launch_row<T, 4, 2>(QSA_ROW_ARGS) : launch_row<T, 4, 1>(QSA_ROW_ARGS); break;
-    case 8: two ? launch_row<T, 8, 2>(QSA_ROW_ARGS) : launch_row<T, 8, 1>(QSA_ROW_ARGS); break;
+    case 1: launch_row<T, 1, 1, kCen>(QSA_ROW_ARGS); break;
+    case 2: two ? launch_row<T, 2, 2, kCen>(QSA_ROW_ARGS) : launch_row<T, 2, 1, kCen>(QSA_ROW_ARGS); break;
+    case 4: two ? launch_row<T, 4, 2, kCen>(QSA_ROW_ARGS) : launch_row<T, 4, 1, kCen>(QSA_ROW_ARGS); break;
+    case 8: two ? launch_row<T, 8, 2, kCen>(QSA_ROW_ARGS) : launch_row<T, 8, 1, kCen>(QSA_ROW_ARGS); break;
     default:
       return hipErrorInvalidValue;
   }
@@ -472,15 +484,15 @@ hipError_t launch_sparse_row_t(const LaunchCommon& c, const void* q, void* meta,
 }  // namespace
 
 hipError_t launch_sparse_row(const LaunchCommon& c, const void* q, void* meta, int stride,
-                             int refresh_tail, int k, float scale_log2, int head_split, float* out,
-                             float* lse, float* group_scores, int* sel, int* sel_count,
+                             int refresh_tail, int k, float scale_log2, int head_split, bool centroid,
+                             float* out, float* lse, float* group_scores, int* sel, int* sel_count,
                              hipStream_t stream) {
-  return c.bf16 ? launch_sparse_row_t<bf16s>(c, q, meta, stride, refresh_tail, k, scale_log2,
-                                             head_split, out, lse, group_scores, sel, sel_count,
-                                             stream)
-                : launch_sparse_row_t<float>(c, q, meta, stride, refresh_tail, k, scale_log2,
-                                             head_split, out, lse, group_scores, sel, sel_count,
-                                             stream);
+#define QSA_ROW_CALL(TT, CC)                                                                      \
+  launch_sparse_row_t<TT, CC>(c, q, meta, stride, refresh_tail, k, scale_log2, head_split, out, lse, \
+                              group_scores, sel, sel_count, stream)
+  if (c.bf16) return centroid ? QSA_ROW_CALL(bf16s, true) : QSA_ROW_CALL(bf16s, false);
+  return centroid ? QSA_ROW_CALL(float, true) : QSA_ROW_CALL(float, false);
+#undef QSA_ROW_CALL
 }
 
 }  // namespace qsa

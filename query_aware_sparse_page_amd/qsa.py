@@ -60,6 +60,8 @@ def lib():
             "qsa_cascade_decode": (i32, [D, vp, vp, i32, KV, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
             "qsa_sparse_decode": (i32, [D, vp, KV, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, i32, vp,
                                         sz, vp]),
+            "qsa_sparse_decode_centroid": (i32, [D, vp, KV, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, i32,
+                                                 vp, sz, vp]),
             "qsa_sparse_decode_path": (i32, [D, _i32p, i32, i32, i32, _i32p]),
             "qsa_sparse_decode_workspace_size": (sz, [D, _i32p, i32, i32, i32]),
             "qsa_topk_workspace_size": (sz, [D, i32, i32]),
@@ -327,10 +329,14 @@ def sparse_decode(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, k: int, sm_s
                   refresh_tail: bool = True, path: str = "auto", with_lse: bool = True,
                   group_scores: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None,
                   sel_count: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  out=None):
+                  out=None, scorer: str = "bound"):
     """One sparse decode step (scores -> top-k pages -> attention) in one
     call; group_scores / sel / sel_count are optional extra outputs (pass
-    tensors of shape [B, Hkv, stride] / [B, Hkv, k] / [B, Hkv] to get them)."""
+    tensors of shape [B, Hkv, stride] / [B, Hkv, k] / [B, Hkv] to get them).
+    scorer="centroid": meta holds centroid rows (build_page_centroids) and
+    pages are scored by q . centroid."""
+    if scorer not in ("bound", "centroid"):
+        raise ValueError(f"scorer {scorer!r}")
     B, Hq, D = q.shape
     stride = int(meta.shape[2])
     sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
@@ -340,10 +346,11 @@ def sparse_decode(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, k: int, sm_s
     if workspace is None and need > 0:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     d, s = kv.dims(Hq), kv.struct()
-    _check(lib().qsa_sparse_decode(ctypes.byref(d), _ptr(q), ctypes.byref(s), _ptr(meta), stride, int(refresh_tail),
-                                   k, ctypes.c_float(sm_scale), _ptr(o), _ptr(lse), _ptr(group_scores), _ptr(sel),
-                                   _ptr(sel_count), PATHS[path], _ptr(workspace),
-                                   0 if workspace is None else workspace.numel(), _stream()))
+    fn = lib().qsa_sparse_decode_centroid if scorer == "centroid" else lib().qsa_sparse_decode
+    _check(fn(ctypes.byref(d), _ptr(q), ctypes.byref(s), _ptr(meta), stride, int(refresh_tail),
+              k, ctypes.c_float(sm_scale), _ptr(o), _ptr(lse), _ptr(group_scores), _ptr(sel),
+              _ptr(sel_count), PATHS[path], _ptr(workspace),
+              0 if workspace is None else workspace.numel(), _stream()))
     return o, lse
 
 

@@ -138,3 +138,50 @@ def test_centroid_identical_keys_and_single_token_pages():
         for j in range(O.num_pages(L)):
             p = O.physical_page(d["page_indptr"], d["page_indices"], b, j)
             assert np.array_equal(cent[b, :, j], kst[p, :, 0]), (b, j)
+
+
+@pytest.mark.parametrize("label,lens,Hq,Hkv,dtype,k", [CASES[0], CASES[1], CASES[3], CASES[5],
+                                                     ("two_keys", [9000, 40000], 8, 2, "bf16", 153)])
+def test_centroid_sparse_decode_fused_and_split(label, lens, Hq, Hkv, dtype, k):
+    # The one-call step with the centroid scorer: the fused kernel and the
+    # split kernels give the same scores (bit for bit) and selection, and the
+    # output agrees with the oracle's attention over the oracle's selection.
+    c = _case(label, lens, Hq, Hkv, dtype)
+    d = case_np(c)
+    g = c.to(DEV)
+    kv = qsa.PagedKV.from_case(g)
+    stride = kv.max_pages() + 1
+    res = {}
+    for path in ("fused", "split"):
+        cent = qsa.build_page_centroids(kv, stride=stride)
+        for b, L in enumerate(c.seq_lens_list()):
+            cent[b, :, -(-L // 16) - 1] = 3.0          # stale tail: refresh_tail must rebuild it
+        gs = torch.full((c.B, Hkv, stride), 5.0, dtype=torch.float32, device=DEV)
+        sel = torch.full((c.B, Hkv, k), -7, dtype=torch.int32, device=DEV)
+        cnt = torch.full((c.B, Hkv), -7, dtype=torch.int32, device=DEV)
+        out, lse = qsa.sparse_decode(g.q, kv, cent, k, sm_scale=c.sm_scale, refresh_tail=True, path=path,
+                                     group_scores=gs, sel=sel, sel_count=cnt, scorer="centroid")
+        torch.cuda.synchronize()
+        res[path] = (cent, gs, sel, cnt, out, lse)
+    cf, gf, sf, nf, of, lf = res["fused"]
+    cs, gsp, ss, ns, osp, ls = res["split"]
+    assert torch.equal(cf, cs) and torch.equal(gf, gsp) and torch.equal(sf, ss) and torch.equal(nf, ns)
+    assert torch.allclose(of, osp, atol=1e-4, rtol=0) and torch.allclose(lf, ls, atol=1e-4, rtol=0)
+
+    ref = O.build_page_centroids(d["k_pool"], dtype, d["page_indptr"], d["page_indices"], d["seq_lens"])
+    _check_centroids(c, d, cf, ref)
+    _, ogroup = O.centroid_scores(d["q"], dtype, ref, dtype, d["page_indptr"], d["page_indices"],
+                                  d["seq_lens"], Hkv, stride=stride)
+    osel, ocnt = O.topk_pages(ogroup, d["seq_lens"], k)
+    oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], dtype, d["page_indptr"], d["page_indices"],
+                            d["seq_lens"], c.sm_scale, sel=osel, sel_count=ocnt)
+    sel_n, cnt_n, o_n, l_n = sf.cpu().numpy(), nf.cpu().numpy(), of.cpu().numpy(), lf.cpu().numpy()
+    G = Hq // Hkv
+    for b, L in enumerate(d["seq_lens"]):
+        n = O.num_pages(L)
+        table = d["page_indices"][d["page_indptr"][b]:d["page_indptr"][b + 1]]
+        for h in range(Hkv):
+            got, want = check_selection_row(sel_n[b, h], cnt_n[b, h], None, ogroup[b, h], n, k, table)
+            if set(got) == set(want):
+                hs_ = slice(h * G, (h + 1) * G)
+                assert_close_out(o_n[b, hs_], l_n[b, hs_], oo[b, hs_], ol[b, hs_])
