@@ -39,18 +39,18 @@ PEAK_HBM_GBPS = 8000.0
 # the kernel sources it was taken on: their SHA-256 is recorded with it and
 # "traffic" is null when the sources differ.
 MEASURED_TRAFFIC = {
-    ("c2_sparse", "fused"): {
-        "bytes": 197520012,
+    ("c2_sparse", "fused", "bound"): {
+        "bytes": 197331429,
         "sources": ["sparse_row.hip", "decode_wave.h", "qsa_device.h", "qsa_internal.h"],
-        "sha256_16": "6105731cfd4f7ca9",
+        "sha256_16": "d6ec458717733296",
         "profile": "profiles/sparse_row_kernel_c2_sparse.md",
     },
 }
 
 
-def measured_traffic(config, path):
+def measured_traffic(config, path, scorer):
     import hashlib
-    rec = MEASURED_TRAFFIC.get((config, path))
+    rec = MEASURED_TRAFFIC.get((config, path, scorer))
     if rec is None:
         return None
     h = hashlib.sha256()
@@ -325,7 +325,7 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": None if centroid else measured_traffic(args.config, path),
+            "traffic": measured_traffic(args.config, path, args.scorer),
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": round(dom_ms, 5),
         },
