@@ -55,7 +55,8 @@ typedef enum qsa_dtype { QSA_F32 = 0, QSA_BF16 = 1 } qsa_dtype;
 /* Problem sizes. B = num_seqs, Hq = num_q_heads, Hkv = num_kv_heads
  * (Hq % Hkv == 0; query head hq belongs to KV head hq / (Hq/Hkv)),
  * D = head_dim, page_size = tokens per page (16). dtype is the element type
- * of q, both pools and the page metadata. */
+ * of q, both pools and the page metadata. B is at most 65535 (a launch grid
+ * dimension); QSA_ERR_UNSUPPORTED otherwise. */
 typedef struct qsa_dims {
   int32_t num_seqs;
   int32_t num_q_heads;

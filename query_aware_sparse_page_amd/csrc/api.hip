@@ -39,12 +39,18 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int pages_of(int L) { return (L + 15) / 16; }
 
+// Largest second or third launch grid dimension (the sequence index, the
+// decode unit index).
+constexpr int kMaxGridDim = 65535;
+
 // Shape checks shared by every entry point.
 qsa_status check_dims(const qsa_dims* d) {
   if (d == nullptr) return fail(QSA_ERR_INVALID_ARG, "dims is NULL");
   if (d->num_seqs < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1)
     return fail(QSA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d D=%d)", d->num_seqs,
                 d->num_q_heads, d->num_kv_heads, d->head_dim);
+  if (d->num_seqs > kMaxGridDim)
+    return fail(QSA_ERR_UNSUPPORTED, "num_seqs %d > %d", d->num_seqs, kMaxGridDim);
   if (d->num_q_heads % d->num_kv_heads != 0)
     return fail(QSA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
                 d->num_q_heads, d->num_kv_heads);
@@ -117,7 +123,8 @@ int target_units() { return 2 * device_cus(); }
 
 // Pages per unit: a multiple of 4 (one quarter per wave) sized so that the
 // rows' pages fill about target_units() equal units; counts per (b, h) row are
-// min(k, n_b) (every page when k <= 0). Capped at 256 (64 pages per wave).
+// min(k, n_b) (every page when k <= 0). Capped at 192 (48 pages per wave; the
+// kernel takes up to 256).
 qsa::DecodePlan make_plan(const qsa_dims* d, const int32_t* lens, int32_t k) {
   qsa::DecodePlan plan;
   long long total = 0;
@@ -129,12 +136,22 @@ qsa::DecodePlan make_plan(const qsa_dims* d, const int32_t* lens, int32_t k) {
     total += (long long)d->num_kv_heads * c;
   }
   const long long per = (total + target_units() - 1) / target_units();
-  // (at most 128 pages per unit: smaller units fill the last round of
-  // workgroups better on long rows, measured)
-  int chunk = (int)std::min<long long>(128, std::max<long long>(4, (per + 3) / 4 * 4));
+  // (long rows: 192-256 pages per unit measured fastest; each unit start
+  // and end costs a few microseconds, which smaller units pay more often,
+  // while larger ones leave a longer tail in the last round)
+  int chunk = (int)std::min<long long>(192, std::max<long long>(4, (per + 3) / 4 * 4));
   plan.chunk = chunk;
   plan.max_units = (maxc + chunk - 1) / chunk;
   return plan;
+}
+
+// The decode grid is (Hkv, B, units per row): a row may need at most
+// kMaxGridDim units.
+qsa_status check_plan(const qsa::DecodePlan& p) {
+  if (p.max_units > kMaxGridDim)
+    return fail(QSA_ERR_UNSUPPORTED, "a row needs %d decode units of %d pages (at most %d)", p.max_units,
+                p.chunk, kMaxGridDim);
+  return QSA_OK;
 }
 
 // Decode workspace: [unit partial outputs][unit partial (max, sum)], each
@@ -368,6 +385,7 @@ qsa_status qsa_decode_plan(const qsa_dims* dims, const int32_t* seq_lens_host, i
   for (int b = 0; b < dims->num_seqs; ++b)
     if (seq_lens_host[b] < 1) return fail(QSA_ERR_INVALID_ARG, "seq_lens[%d] < 1", b);
   qsa::DecodePlan p = make_plan(dims, seq_lens_host, k);
+  if ((s = check_plan(p)) != QSA_OK) return s;
   *chunk_pages = p.chunk;
   *max_units = p.max_units;
   return ok();
@@ -394,6 +412,7 @@ qsa_status qsa_paged_decode(const qsa_dims* dims, const void* q, const qsa_paged
   if (!std::isfinite(sm_scale)) return fail(QSA_ERR_INVALID_ARG, "sm_scale is not finite");
   const int32_t kk = sel != nullptr ? k : 0;
   const qsa::DecodePlan plan = make_plan(dims, kv->seq_lens_host, kk);
+  if ((s = check_plan(plan)) != QSA_OK) return s;
   const DecodeWs w = decode_ws(dims, plan);
   if (ws_bytes < w.total() || (w.total() > 0 && ws == nullptr))
     return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, w.total());
@@ -432,6 +451,7 @@ qsa_status qsa_cascade_decode(const qsa_dims* dims, const void* q, const int32_t
   if (!std::isfinite(sm_scale)) return fail(QSA_ERR_INVALID_ARG, "sm_scale is not finite");
   const int32_t kk = sel != nullptr ? k : 0;
   const qsa::DecodePlan plan = make_plan(dims, kv->seq_lens_host, kk);
+  if ((s = check_plan(plan)) != QSA_OK) return s;
   const DecodeWs w = decode_ws(dims, plan);
   const size_t need = w.total() + prefix_ws_bytes(dims, prefix_len);
   if (ws_bytes < need || ws == nullptr)

@@ -4,7 +4,7 @@
 // and the Quail page's join attention).
 //
 // Work unit = (sequence b, KV head h, a chunk of `chunk` consecutive entries
-// of the row's page list). The unit's workgroup has 4 waves; wave w takes
+// of the row's page list), block (h, b, chunk). The unit's workgroup has 4 waves; wave w takes
 // entries w, w+4, ... of the chunk and runs them through the per-wave
 // attention: on the matrix cores (decode_mfma.h) for bf16 groups of 4 or
 // more heads, else on the vector ALU (decode_wave.h). Unit results (o unnormalised, max, sum) go to
@@ -69,9 +69,9 @@ decode_split_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int u = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int u = blockIdx.z;
   const int Hq = Hkv * G;
   const size_t row = (size_t)b * Hkv + h;
   const int ubeg = u * chunk;
@@ -264,7 +264,12 @@ hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
                            const int* sel_count, int k, float scale_log2, const DecodePlan& plan,
                            Partials part, Partials prefix, int n_prefix, float* out, float* lse,
                            hipStream_t stream) {
-  dim3 grid(plan.max_units, c.Hkv, c.B);
+  // The KV head is the fastest grid dimension and the unit the slowest.
+  // Workgroups go round-robin over the 8 XCDs by linear id, so with 8 KV
+  // heads every XCD serves one head of every row (equal work); with the unit
+  // fastest instead, XCD x would get units x and x + 8 of every row, and
+  // only long rows have the high units.
+  dim3 grid(c.Hkv, c.B, plan.max_units);
   const T* qq = static_cast<const T*>(q);
   const T* kk = static_cast<const T*>(c.k_pool);
   const T* vv = static_cast<const T*>(c.v_pool);

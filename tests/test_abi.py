@@ -105,6 +105,17 @@ def test_decode_plan_and_workspace(L):
     assert cw > L.qsa_decode_workspace_size(ctypes.byref(d), lens, 0)
 
 
+def test_sequence_count_limit(L):
+    # the sequence index is a launch grid dimension: at most 65535
+    d = _dims(B=65536)
+    lens = _lens([16] * 65536)
+    c, m = ctypes.c_int32(), ctypes.c_int32()
+    assert L.qsa_decode_plan(ctypes.byref(d), lens, 0, ctypes.byref(c), ctypes.byref(m)) == qsa.QSA_ERR_UNSUPPORTED
+    d = _dims(B=65535)
+    lens = _lens([16] * 65535)
+    assert L.qsa_decode_plan(ctypes.byref(d), lens, 0, ctypes.byref(c), ctypes.byref(m)) == 0
+
+
 def test_topk_workspace_query(L):
     assert L.qsa_topk_workspace_size(ctypes.byref(_dims()), 8192, 128) >= 0
 
