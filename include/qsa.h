@@ -291,11 +291,17 @@ size_t qsa_cascade_workspace_size(const qsa_dims* dims, int32_t prefix_len,
 size_t qsa_sparse_decode_workspace_size(const qsa_dims* dims, const int32_t* seq_lens_host,
                                         int32_t stride, int32_t k, qsa_path path);
 
-/* The decode work split the library will use: pages per work unit and the
- * largest number of units of one (b, h). Returns QSA_ERR_INVALID_ARG on bad
- * arguments. */
+/* The decode work split the library will use. bf16 groups of 4 or more
+ * query heads with at most 1024 sequences take the stream split: every wave
+ * gets an equal share of all rows' pages; *chunk_pages is that share (rounded
+ * up) and *max_units the most partial results one (b, h) row can have.
+ * Otherwise rows are cut into work units: *chunk_pages pages per unit and
+ * *max_units the most units of one row. *stream (may be NULL) is 1 for the
+ * stream split, else 0. Returns QSA_ERR_INVALID_ARG on bad arguments,
+ * QSA_ERR_UNSUPPORTED when a row would need more than 65535 units. */
 qsa_status qsa_decode_plan(const qsa_dims* dims, const int32_t* seq_lens_host,
-                           int32_t k, int32_t* chunk_pages, int32_t* max_units);
+                           int32_t k, int32_t* chunk_pages, int32_t* max_units,
+                           int32_t* stream);
 
 /* floor(budget_tokens / page_size): a token budget in whole pages (>= 0). */
 int32_t qsa_budget_pages(int32_t budget_tokens, int32_t page_size);

@@ -142,6 +142,31 @@ qsa::DecodePlan make_plan(const qsa_dims* d, const int32_t* lens, int32_t k) {
   int chunk = (int)std::min<long long>(192, std::max<long long>(4, (per + 3) / 4 * 4));
   plan.chunk = chunk;
   plan.max_units = (maxc + chunk - 1) / chunk;
+  // Stream split when the units would take more than one round of
+  // workgroups (many short rows, or long rows cut into many units): there
+  // its equal per-wave shares avoid the rounds' restarts and uneven ends.
+  // Within one round the units' shorter start (one level of independent
+  // loads, one combined partial per unit) measured faster.
+  long long unit_count = 0;
+  for (int b = 0; b < d->num_seqs; ++b) {
+    int c = pages_of(lens[b]);
+    if (k > 0) c = std::min(c, (int)k);
+    unit_count += (long long)d->num_kv_heads * ((c + chunk - 1) / chunk);
+  }
+  const int g = d->num_q_heads / d->num_kv_heads;
+  if (d->dtype == QSA_BF16 && g >= 4 && d->num_seqs <= qsa::kStreamMaxB &&
+      unit_count > target_units()) {
+    // One wave per (total / waves) pages, at least kStreamMinPages each, two
+    // 4-wave workgroups per CU at most.
+    constexpr long long kStreamMinPages = 4;
+    const long long wgs = std::max<long long>(
+        1, std::min<long long>(target_units(), (total + 4 * kStreamMinPages - 1) / (4 * kStreamMinPages)));
+    plan.stream = true;
+    plan.waves = (int)(4 * wgs);
+    plan.chunk = (int)((total + plan.waves - 1) / plan.waves);
+    const long long per_wave = std::max<long long>(1, total / plan.waves);
+    plan.max_units = (int)std::min<long long>(plan.waves, (maxc + per_wave - 1) / per_wave + 1);
+  }
   return plan;
 }
 
@@ -154,20 +179,23 @@ qsa_status check_plan(const qsa::DecodePlan& p) {
   return QSA_OK;
 }
 
-// Decode workspace: [unit partial outputs][unit partial (max, sum)], each
-// region 256-byte aligned.
+// Decode workspace: [partial outputs][partial (max, sum)][stream split: the
+// rows' (first, last) waves], each region 256-byte aligned. Partial slots:
+// rows x max_units (units), or waves + rows (stream: slot w + r for the
+// segment of row r in wave w).
 struct DecodeWs {
-  size_t o_bytes = 0, ml_bytes = 0;
-  size_t total() const { return align_up(o_bytes) + align_up(ml_bytes); }
+  size_t o_bytes = 0, ml_bytes = 0, rs_bytes = 0;
+  size_t total() const { return align_up(o_bytes) + align_up(ml_bytes) + align_up(rs_bytes); }
 };
 
 DecodeWs decode_ws(const qsa_dims* d, const qsa::DecodePlan& plan) {
   const size_t rows = (size_t)d->num_seqs * d->num_kv_heads;
-  const size_t units = rows * plan.max_units;
+  const size_t slots = plan.stream ? (size_t)plan.waves + rows : rows * plan.max_units;
   const int g = d->num_q_heads / d->num_kv_heads;
   DecodeWs w;
-  w.o_bytes = units * g * d->head_dim * sizeof(float);
-  w.ml_bytes = units * g * 2 * sizeof(float);
+  w.o_bytes = slots * g * d->head_dim * sizeof(float);
+  w.ml_bytes = slots * g * 2 * sizeof(float);
+  w.rs_bytes = plan.stream ? rows * 2 * sizeof(int) : 0;
   return w;
 }
 
@@ -176,6 +204,7 @@ qsa::Partials carve(void* ws, const DecodeWs& w) {
   qsa::Partials p;
   p.o = reinterpret_cast<float*>(base);
   p.ml = reinterpret_cast<float*>(base + align_up(w.o_bytes));
+  if (w.rs_bytes > 0) p.row_slots = reinterpret_cast<int*>(base + align_up(w.o_bytes) + align_up(w.ml_bytes));
   return p;
 }
 
@@ -377,7 +406,7 @@ qsa_status qsa_topk_pages_approx(const qsa_dims* dims, const qsa_paged_kv* kv,
 }
 
 qsa_status qsa_decode_plan(const qsa_dims* dims, const int32_t* seq_lens_host, int32_t k,
-                           int32_t* chunk_pages, int32_t* max_units) {
+                           int32_t* chunk_pages, int32_t* max_units, int32_t* stream) {
   qsa_status s = check_dims(dims);
   if (s != QSA_OK) return s;
   if (seq_lens_host == nullptr || chunk_pages == nullptr || max_units == nullptr)
@@ -388,6 +417,7 @@ qsa_status qsa_decode_plan(const qsa_dims* dims, const int32_t* seq_lens_host, i
   if ((s = check_plan(p)) != QSA_OK) return s;
   *chunk_pages = p.chunk;
   *max_units = p.max_units;
+  if (stream != nullptr) *stream = p.stream ? 1 : 0;
   return ok();
 }
 

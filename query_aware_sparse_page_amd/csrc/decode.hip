@@ -3,8 +3,12 @@
 // load; flash decoding's split + log-sum-exp merge per the CS336 page §9.2
 // and the Quail page's join attention).
 //
-// Work unit = (sequence b, KV head h, a chunk of `chunk` consecutive entries
-// of the row's page list), block (h, b, chunk). The unit's workgroup has 4 waves; wave w takes
+// Two work splits, chosen by the host's plan:
+//  * stream (bf16 groups of 4 or more heads, up to kStreamMaxB sequences):
+//    decode_stream_kernel gives every wave an equal, contiguous share of all
+//    rows' page lists; below.
+//  * units: work unit = (sequence b, KV head h, a chunk of `chunk`
+//    consecutive entries of the row's page list), block (h, b, chunk). The unit's workgroup has 4 waves; wave w takes
 // entries w, w+4, ... of the chunk and runs them through the per-wave
 // attention: on the matrix cores (decode_mfma.h) for bf16 groups of 4 or
 // more heads, else on the vector ALU (decode_wave.h). Unit results (o unnormalised, max, sum) go to
@@ -168,6 +172,293 @@ decode_split_kernel(
   }
 }
 
+// ---- stream split ---------------------------------------------------------
+// Rows r = b * Hkv + h are concatenated in that order, row r holding c_b
+// entries: its selected pages (c_b = min(k, n_b)) or every page (c_b = n_b),
+// at least one. Wave w of W takes entries [w T / W, (w + 1) T / W) of the T
+// in all, so every wave attends the same number of pages, and runs them as
+// one pipelined page loop: where its share crosses from one row into the
+// next, the finished row segment's (o, max, sum) goes to partial slot w + r
+// and the state restarts with the next row's query while the next page's
+// loads are already in flight. A row's slots are consecutive (from its first
+// wave's to its last wave's); row_slots[r] = (first wave, last wave) for the
+// merge. No workgroup barrier follows the table set-up, so a wave never
+// waits for another.
+
+struct StreamTables {
+  long long pre[kStreamMaxB + 1];  // pre[b] = c_0 + ... + c_{b-1}
+  int len[kStreamMaxB];            // seq_lens
+  int base[kStreamMaxB];           // page_indptr
+  __device__ __forceinline__ int count(int b) const { return (int)(pre[b + 1] - pre[b]); }
+};
+
+// A wave's share of the entries, fetched 64 at a time (one entry per lane) a
+// batch ahead of use. Pages are returned as tile indices p * Hkv + h.
+struct StreamSrc {
+  const StreamTables* t;
+  const char* q;
+  const int* page_indices;
+  const int* sel;
+  const int* sel_count;
+  int Hkv, G, k, num_phys, lane;
+  long long e_next, e_end;  // next entry to fetch; end of the share
+  int fb, fh, fj;           // (b, h, j) of entry e_next
+  int row0, first0;         // the share's first row; 1 if the share starts at its j = 0
+  // current batch, one entry per lane: tile, valid tokens, row, segment word
+  int c_p = 0, c_v = 0, c_r = 0, c_w = 0;
+  // next batch (raw): row, logical page, loaded table entry, word
+  int n_r = 0, n_j = -1, n_raw = -1, n_w = 0;
+  int c_n = 0, n_n = 0, i = 0;
+  int segw = 0;
+  int cur_row;
+  uint4 qn[4];  // query of the row most recently entered (B operand layout)
+
+  // nothing left to return (the first batch is fetched before the page loop
+  // asks, which already moves e_next)
+  __device__ __forceinline__ bool empty() const { return i >= c_n && n_n <= 0; }
+
+  // Fill the next batch with the entries from e_next on.
+  __device__ __forceinline__ void fill() {
+    const long long left = e_end - e_next;
+    const int n = left < 64 ? (int)left : 64;
+    n_n = n;
+    if (n <= 0) return;
+    int b = fb, h = fh, j = fj;
+    if (lane < n) {
+      int rem = lane;
+      int c = t->count(b);
+      while (rem >= c - j) {  // each step leaves a row: at most lane steps
+        rem -= c - j;
+        j = 0;
+        if (++h == Hkv) {
+          h = 0;
+          ++b;
+        }
+        c = t->count(b);
+      }
+      j += rem;
+    }
+    const int row = b * Hkv + h;
+    // the entry after this batch: (fb, fh, fj) for the next fill
+    {
+      int lb = __builtin_amdgcn_readlane(b, n - 1), lh = __builtin_amdgcn_readlane(h, n - 1);
+      int lj = __builtin_amdgcn_readlane(j, n - 1) + 1;
+      if (lj == t->count(lb)) {
+        lj = 0;
+        if (++lh == Hkv) {
+          lh = 0;
+          ++lb;
+        }
+      }
+      fb = lb;
+      fh = lh;
+      fj = lj;
+    }
+    e_next += n;
+    const int row_after = e_next < e_end ? fb * Hkv + fh : -1;
+    const int nxt_lane = __builtin_amdgcn_ds_bpermute(((lane + 1) & 63) * 4, row);
+    const int next_row = lane + 1 < n ? nxt_lane : row_after;
+    int word = 0;
+    if (lane < n && next_row != row) {
+      const int first = (row != row0 || first0) ? 2 : 0;
+      const int last = j == t->count(b) - 1 ? 4 : 0;
+      word = 1 | first | last | (row << 3);
+    }
+    n_r = row;
+    n_w = word;
+    n_j = -1;  // logical page of the entry, -1 when it attends nothing
+    n_raw = -1;
+    if (lane < n) {
+      const int L = t->len[b];
+      const int np = L > 0 ? (L + kPage - 1) / kPage : 0;
+      if (sel == nullptr) {
+        if (j < np) {
+          n_j = j;
+          n_raw = page_indices[t->base[b] + j];
+        }
+      } else {
+        // two dependent levels: the list entry (j < c_b <= k), then its
+        // table entry; entries past the row's count attend nothing
+        const int act = min(min(sel_count[row], k), np);
+        const int jl = sel[(size_t)row * k + j];
+        if (j < act && jl >= 0 && jl < np) {
+          n_j = jl;
+          n_raw = page_indices[t->base[b] + jl];
+        }
+      }
+    }
+  }
+
+  // Validate the raw next batch into the current one.
+  __device__ __forceinline__ void take() {
+    c_n = n_n;
+    i = 0;
+    const int b = n_r / Hkv;
+    const int h = n_r - b * Hkv;
+    const int L = t->len[b];
+    const int jl = n_j;
+    const bool ok = lane < c_n && jl >= 0 && n_raw >= 0 && n_raw < num_phys;
+    c_p = ok ? n_raw * Hkv + h : 0;
+    c_v = ok ? min(kPage, L - kPage * jl) : 0;
+    c_r = n_r;
+    c_w = lane < c_n ? n_w : 0;
+    fill();
+  }
+
+  __device__ __forceinline__ void next(int* p, int* valid) {
+    if (i == c_n) {
+      if (n_n <= 0) {
+        *p = 0;
+        *valid = -1;
+        segw = 0;
+        return;
+      }
+      take();
+    }
+    *p = __builtin_amdgcn_readlane(c_p, i);
+    *valid = __builtin_amdgcn_readlane(c_v, i);
+    segw = __builtin_amdgcn_readlane(c_w, i);
+    const int row = __builtin_amdgcn_readlane(c_r, i);
+    if (row != cur_row) {  // entering a row: its query, for the hook to swap in
+      cur_row = row;
+      load_q(row);
+    }
+    ++i;
+  }
+  __device__ __forceinline__ int seg() const { return segw; }
+
+  __device__ __forceinline__ void load_q(int row) {
+    const int c16 = lane & 15;
+    const int grp = lane >> 4;
+    const char* qr = q + (size_t)row * G * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qn[ks] = c16 < G ? ld16(qr + c16 * kRowBytes + (8 * grp + 32 * ks) * 2) : make_uint4(0, 0, 0, 0);
+  }
+};
+
+template <int G>
+struct StreamHook {
+  static constexpr bool kActive = true;
+  StreamSrc* src;
+  float* part_o;
+  float* part_ml;
+  int* row_slots;
+  int w, lane;
+  __device__ __forceinline__ void operator()(WaveAttnMfma<G>& wa, int word) const {
+    const int r = word >> 3;
+    const size_t slot = (size_t)w + r;
+    wa.store(part_o + slot * G * WaveAttnMfma<G>::D, part_ml + slot * G * 2, lane);
+    if (lane == 0) {
+      if (word & 2) row_slots[2 * r] = w;
+      if (word & 4) row_slots[2 * r + 1] = w;
+    }
+    wa.restart(src->qn);
+  }
+};
+
+template <int G>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+decode_stream_kernel(
+    const bf16s* __restrict__ q, const bf16s* __restrict__ k_pool, const bf16s* __restrict__ v_pool,
+    int num_phys, int B, int Hkv, const int* __restrict__ page_indptr,
+    const int* __restrict__ page_indices, const int* __restrict__ seq_lens,
+    const int* __restrict__ sel, const int* __restrict__ sel_count, int k, float scale_log2,
+    int nwaves, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int* __restrict__ row_slots) {
+  using WA = WaveAttnMfma<G>;
+  __shared__ StreamTables tab;
+  __shared__ alignas(16) char vl[4][WA::kLdsBytes];
+  __shared__ long long wtot[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- per-sequence tables: lengths, table bases, prefix of the counts
+  constexpr int kPer = kStreamMaxB / 256;
+  const int b0 = tid * kPer;
+  int cnt[kPer];
+  long long local = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int b = b0 + e;
+    cnt[e] = 0;
+    if (b < B) {
+      const int L = seq_lens[b];
+      tab.len[b] = L;
+      tab.base[b] = page_indptr[b];
+      const int np = L > 0 ? (L + kPage - 1) / kPage : 0;
+      const int c = sel != nullptr ? min(k, np) : np;
+      cnt[e] = c > 1 ? c : 1;
+      local += cnt[e];
+    }
+  }
+  long long incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  long long excl = incl - local;
+  for (int w2 = 0; w2 < wave; ++w2) excl += wtot[w2];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int b = b0 + e;
+    if (b < B) tab.pre[b] = excl;
+    excl += cnt[e];
+  }
+  if (tid == 0) tab.pre[B] = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+  __syncthreads();
+
+  // ---- this wave's share
+  const long long T = (long long)Hkv * tab.pre[B];
+  const int w = blockIdx.x * 4 + wave;
+  const long long e0 = (long long)w * T / nwaves;
+  const long long e1 = (long long)(w + 1) * T / nwaves;
+  if (e0 >= e1) return;
+  int lo = 0, hi = B;  // largest b with Hkv * pre[b] <= e0
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((long long)Hkv * tab.pre[mid] <= e0)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const long long off = e0 - (long long)Hkv * tab.pre[lo];
+  const int c0 = tab.count(lo);
+  const int h0 = (int)(off / c0);
+  const int j0 = (int)(off - (long long)h0 * c0);
+
+  StreamSrc src;
+  src.t = &tab;
+  src.q = reinterpret_cast<const char*>(q);
+  src.page_indices = page_indices;
+  src.sel = sel;
+  src.sel_count = sel_count;
+  src.Hkv = Hkv;
+  src.G = G;
+  src.k = k;
+  src.num_phys = num_phys;
+  src.lane = lane;
+  src.e_next = e0;
+  src.e_end = e1;
+  src.fb = lo;
+  src.fh = h0;
+  src.fj = j0;
+  src.row0 = lo * Hkv + h0;
+  src.first0 = j0 == 0;
+  src.cur_row = src.row0;
+  src.fill();
+
+  WA wa;
+  wa.init(reinterpret_cast<const char*>(q) + (size_t)src.row0 * G * kRowBytes, lane);
+  StreamHook<G> hook{&src, part_o, part_ml, row_slots, w, lane};
+  wa.run(src, reinterpret_cast<const char*>(k_pool), reinterpret_cast<const char*>(v_pool),
+         (size_t)kTileBytes, scale_log2, vl[wave], lane, hook);
+}
+
 // One wave per (b, hq): log-sum-exp merge of the unit partials (and of the
 // shared-prefix partials for the cascade), then normalisation. The partials
 // are loaded without waiting for the row's unit count (every slot the row can
@@ -177,8 +468,8 @@ __global__ void __launch_bounds__(256) merge_kernel(
     int B, int Hkv, int G, const int* __restrict__ seq_lens, const int* __restrict__ sel_count,
     int k_stride, int chunk, int max_units, const float* __restrict__ part_o,
     const float* __restrict__ part_ml, const float* __restrict__ pre_o,
-    const float* __restrict__ pre_ml, int n_pre, float* __restrict__ out,
-    float* __restrict__ lse) {
+    const float* __restrict__ pre_ml, int n_pre, const int* __restrict__ row_slots, int nwaves,
+    float* __restrict__ out, float* __restrict__ lse) {
   constexpr int PER = D / 64;
   constexpr int kBatch = 16;  // partial slots loaded per round (a cascade row has 8 prefix splits + suffix units)
   const int lane = threadIdx.x & 63;
@@ -193,13 +484,23 @@ __global__ void __launch_bounds__(256) merge_kernel(
   const size_t pre_row = (size_t)b * G + hh;
   const int L = seq_lens[b];
   const int cnt_sel = sel_count != nullptr ? sel_count[row] : 0;
-  const int slots = max_units + n_pre;
+  // the row's unit slots: ucap of them from ubase (stream split: the slots of
+  // its first to last wave, known once row_slots is read; units: every slot
+  // the row can own, loaded before its unit count is known)
+  int ubase = (int)(row * max_units), ucap = max_units, units = -1;
+  if (row_slots != nullptr) {
+    const int f = min(max(row_slots[2 * row], 0), nwaves - 1);
+    const int l = min(max(row_slots[2 * row + 1], f), nwaves - 1);
+    ubase = f + (int)row;
+    ucap = l - f + 1;
+    units = ucap;
+  }
+  const int slots = ucap + n_pre;
 
   float M = -__builtin_inff(), lsum = 0.0f;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  int units = -1;
   for (int base = 0; base < slots; base += kBatch) {
     float m[kBatch], l[kBatch], v[kBatch][PER];
 #pragma unroll
@@ -207,12 +508,12 @@ __global__ void __launch_bounds__(256) merge_kernel(
       const int i = min(base + t, slots - 1);
       const float* po;
       const float* pml;
-      if (i < max_units) {
-        const size_t un = row * max_units + i;
+      if (i < ucap) {
+        const size_t un = (size_t)ubase + i;
         po = part_o + (un * G + hh) * D;
         pml = part_ml + (un * G + hh) * 2;
       } else {
-        const size_t pr = ((size_t)h * n_pre + (i - max_units)) * ((size_t)B * G) + pre_row;
+        const size_t pr = ((size_t)h * n_pre + (i - ucap)) * ((size_t)B * G) + pre_row;
         po = pre_o + pr * D;
         pml = pre_ml + pr * 2;
       }
@@ -236,7 +537,7 @@ __global__ void __launch_bounds__(256) merge_kernel(
     for (int t = 0; t < kBatch; ++t) {
       const int i = base + t;
       // slots past the row's units (and past the list) hold stale values
-      const bool use = i < slots && (i < units || i >= max_units);
+      const bool use = i < slots && (i < units || i >= ucap);
       if (!use || m[t] == -__builtin_inff()) continue;
       if (m[t] > M) {
         const float a = (M == -__builtin_inff()) ? 0.0f : fast_exp2(M - m[t]);
@@ -271,8 +572,28 @@ hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
   // only long rows have the high units.
   dim3 grid(c.Hkv, c.B, plan.max_units);
   const T* qq = static_cast<const T*>(q);
+  if constexpr (IsBf16<T>::value) {
+    if (plan.stream) {
+      const bf16s* kb = static_cast<const bf16s*>(c.k_pool);
+      const bf16s* vb = static_cast<const bf16s*>(c.v_pool);
+#define QSA_STREAM_CASE(GG)                                                                      \
+  case GG:                                                                                       \
+    hipLaunchKernelGGL((decode_stream_kernel<GG>), dim3(plan.waves / 4), dim3(256), 0, stream, qq, \
+                       kb, vb, c.num_phys, c.B, c.Hkv, c.page_indptr, c.page_indices, c.seq_lens,  \
+                       sel, sel_count, k, scale_log2, plan.waves, part.o, part.ml, part.row_slots); \
+    break;
+      switch (c.G) {
+        QSA_STREAM_CASE(4)
+        QSA_STREAM_CASE(8)
+        default:
+          return hipErrorInvalidValue;
+      }
+#undef QSA_STREAM_CASE
+    }
+  }
   const T* kk = static_cast<const T*>(c.k_pool);
   const T* vv = static_cast<const T*>(c.v_pool);
+  if (!plan.stream) {
 #define QSA_DECODE_CASE(GG)                                                                     \
   case GG:                                                                                      \
     hipLaunchKernelGGL((decode_split_kernel<T, GG>), grid, dim3(256), 0, stream, qq, kk, vv,    \
@@ -288,6 +609,7 @@ hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
       return hipErrorInvalidValue;
   }
 #undef QSA_DECODE_CASE
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 mgrid((c.B * c.Hq + 3) / 4);
@@ -295,11 +617,11 @@ hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
   if (c.D == 128) {
     hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, stream, c.B, c.Hkv, c.G, c.seq_lens,
                        sc, k, plan.chunk, plan.max_units, part.o, part.ml, prefix.o, prefix.ml,
-                       n_prefix, out, lse);
+                       n_prefix, plan.stream ? part.row_slots : nullptr, plan.waves, out, lse);
   } else {
     hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(256), 0, stream, c.B, c.Hkv, c.G, c.seq_lens,
                        sc, k, plan.chunk, plan.max_units, part.o, part.ml, prefix.o, prefix.ml,
-                       n_prefix, out, lse);
+                       n_prefix, plan.stream ? part.row_slots : nullptr, plan.waves, out, lse);
   }
   return hipGetLastError();
 }

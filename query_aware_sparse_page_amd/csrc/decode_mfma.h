@@ -43,6 +43,13 @@ __device__ __forceinline__ mf_f32x4_t mfma_k16(const uint2& a, const uint2& b, m
 }
 typedef __bf16 mf_bf16x2_t __attribute__((ext_vector_type(2)));
 
+// The default segment hook: a page list within one (b, h) row.
+struct NoSegments {
+  static constexpr bool kActive = false;
+  template <class WA>
+  __device__ __forceinline__ void operator()(WA&, int) const {}
+};
+
 // Two page buffers (one page in flight while one is computed) measured
 // faster than three or four.
 template <int G, int kStagesArg = 2>
@@ -78,18 +85,38 @@ struct WaveAttnMfma {
     l_run = 0.0f;
   }
 
-  // Pages as in WaveAttn::run. vlds: this wave's kLdsBytes of LDS.
-  template <class Src>
+  // A new (b, h) row: its query rows (B operand layout, as init loads them)
+  // and an empty state.
+  __device__ __forceinline__ void restart(const uint4 (&q)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = q[ks];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[dt] = mf_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run = -__builtin_inff();
+    l_run = 0.0f;
+  }
+
+  // Pages as in WaveAttn::run. vlds: this wave's kLdsBytes of LDS. A source
+  // whose page list spans several (b, h) rows reports, with each page, a
+  // nonzero segment word when the page is the last of its row's run
+  // (src.seg()); after that page is processed, hook(*this, word) takes the
+  // row's result and resets the state for the next row.
+  template <class Src, class Hook = NoSegments>
   __device__ __forceinline__ void run(Src& src, const char* kbase, const char* vbase,
-                                      size_t page_stride, float scale_log2, char* vlds, int lane) {
+                                      size_t page_stride, float scale_log2, char* vlds, int lane,
+                                      Hook hook = Hook{}) {
     const int c16 = lane & 15;
     const int grp = lane >> 4;
 
     // K tile in the A layout of S^T (lane: key c16, dims 8 grp + 32 ks),
     // V tile linear (lane: chunk c16 of rows grp + 4 r). Branch-free.
-    auto issue = [&](uint4 (&kA)[4], uint4 (&vB)[4]) -> int {
+    auto issue = [&](uint4 (&kA)[4], uint4 (&vB)[4], int& segw) -> int {
       int p, valid;
       src.next(&p, &valid);
+      if constexpr (Hook::kActive)
+        segw = src.seg();
+      else
+        segw = 0;
       const char* kt = kbase + (size_t)p * page_stride;
       const char* vt = vbase + (size_t)p * page_stride;
 #pragma unroll
@@ -182,19 +209,20 @@ struct WaveAttnMfma {
     // pages are in flight while one page is processed.
     if (src.empty()) return;
     uint4 kA[kStages][4], vB[kStages][4];
-    int vld[kStages];
+    int vld[kStages], segw[kStages];
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s) {
-      vld[s] = issue(kA[s], vB[s]);
+      vld[s] = issue(kA[s], vB[s], segw[s]);
       __builtin_amdgcn_sched_barrier(0);
     }
     int sp = 0;
     while (true) {
 #pragma unroll
       for (int r = 0; r < kStages; ++r) {
-        vld[(r + kStages - 1) % kStages] =
-            issue(kA[(r + kStages - 1) % kStages], vB[(r + kStages - 1) % kStages]);
+        const int nx = (r + kStages - 1) % kStages;
+        vld[nx] = issue(kA[nx], vB[nx], segw[nx]);
         process(sp, vld[r], kA[r], vB[r]);
+        if (Hook::kActive && segw[r] != 0) hook(*this, segw[r]);
         ++sp;
       }
       bool more = false;

@@ -22,15 +22,21 @@ struct LaunchCommon {
 // Split-K decode work split: `chunk` pages per work unit (a multiple of 4,
 // one quarter per wave), `max_units` units for the longest (b, h) row.
 struct DecodePlan {
-  int chunk = 4;
-  int max_units = 0;
+  int chunk = 4;       // units: pages per unit; stream: pages per wave (rounded up)
+  int max_units = 0;   // units: most units of one row; stream: most partial slots of one row
+  bool stream = false; // the stream split (decode_stream_kernel)
+  int waves = 0;       // stream: waves in the launch (a multiple of 4)
 };
+
+// Sequences whose per-sequence tables the stream split keeps in LDS.
+constexpr int kStreamMaxB = 1024;
 
 // Per-unit partial results: part_o [units, G, D] (unnormalised, relative to
 // the unit's running max), part_ml [units, G, 2] = (max in log2 units, sum).
 struct Partials {
   float* o = nullptr;
   float* ml = nullptr;
+  int* row_slots = nullptr;  // stream split: [rows][2] first and last wave of each row
 };
 
 hipError_t launch_build_meta(const LaunchCommon& c, int max_pages, int tail_pages, void* meta,

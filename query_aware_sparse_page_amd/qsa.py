@@ -67,7 +67,7 @@ def lib():
             "qsa_topk_workspace_size": (sz, [D, i32, i32]),
             "qsa_decode_workspace_size": (sz, [D, _i32p, i32]),
             "qsa_cascade_workspace_size": (sz, [D, i32, _i32p, i32]),
-            "qsa_decode_plan": (i32, [D, _i32p, i32, _i32p, _i32p]),
+            "qsa_decode_plan": (i32, [D, _i32p, i32, _i32p, _i32p, _i32p]),
             "qsa_budget_pages": (i32, [i32, i32]),
             "qsa_status_string": (ctypes.c_char_p, [i32]),
             "qsa_last_error": (ctypes.c_char_p, []),
@@ -260,12 +260,13 @@ def decode_workspace_size(kv: PagedKV, num_q_heads: int, k: int = 0) -> int:
     return int(lib().qsa_decode_workspace_size(ctypes.byref(d), ctypes.cast(kv._host_arr, _i32p), k))
 
 
-def decode_plan(kv: PagedKV, num_q_heads: int, k: int = 0) -> Tuple[int, int]:
+def decode_plan(kv: PagedKV, num_q_heads: int, k: int = 0) -> Tuple[int, int, bool]:
+    """(pages per unit or per wave, most partials of one row, stream split?)."""
     d = kv.dims(num_q_heads)
-    c, m = ctypes.c_int32(), ctypes.c_int32()
+    c, m, st = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _check(lib().qsa_decode_plan(ctypes.byref(d), ctypes.cast(kv._host_arr, _i32p), k, ctypes.byref(c),
-                                 ctypes.byref(m)))
-    return c.value, m.value
+                                 ctypes.byref(m), ctypes.byref(st)))
+    return c.value, m.value, bool(st.value)
 
 
 def paged_decode(q: torch.Tensor, kv: PagedKV, sel: Optional[torch.Tensor] = None,

@@ -88,18 +88,38 @@ def test_validation_errors_return_before_any_device_work(L):
 
 
 def test_decode_plan_and_workspace(L):
-    d = _dims(B=16)
-    lens = _lens([8192] * 16)
     c, m = ctypes.c_int32(), ctypes.c_int32()
-    assert L.qsa_decode_plan(ctypes.byref(d), lens, 153, ctypes.byref(c), ctypes.byref(m)) == 0
+    # units split (fp32 pools): a row of n pages has ceil(n / chunk) units
+    d = _dims(B=16, D=64, dt=qsa.QSA_F32)
+    lens = _lens([8192] * 16)
+    assert L.qsa_decode_plan(ctypes.byref(d), lens, 153, ctypes.byref(c), ctypes.byref(m), None) == 0
     assert c.value % 4 == 0 and 4 <= c.value <= 256
     assert m.value == -(-153 // c.value)
     ws = L.qsa_decode_workspace_size(ctypes.byref(d), lens, 153)
     units = 16 * 8 * m.value
-    assert ws >= units * 4 * 128 * 4 + units * 4 * 2 * 4
-    # dense: every page counts
-    assert L.qsa_decode_plan(ctypes.byref(d), lens, 0, ctypes.byref(c), ctypes.byref(m)) == 0
+    assert ws >= units * 4 * 64 * 4 + units * 4 * 2 * 4
+    assert L.qsa_decode_plan(ctypes.byref(d), lens, 0, ctypes.byref(c), ctypes.byref(m), None) == 0
     assert m.value == -(-512 // c.value)
+    # bf16, 4 heads per group, 16 rows of 8192 tokens: the units fit one
+    # round (the host reports 256 CUs when it has no GPU), so units again
+    d = _dims(B=16)
+    st = ctypes.c_int32(-1)
+    assert L.qsa_decode_plan(ctypes.byref(d), lens, 153, ctypes.byref(c), ctypes.byref(m), ctypes.byref(st)) == 0
+    assert st.value == 0
+    assert c.value % 4 == 0 and m.value == -(-153 // c.value)
+    # 64 dense rows of 8192 tokens would take several rounds of units: the
+    # stream split, equal shares of the 64 * 8 * 512 pages, one partial per
+    # (wave, row) segment
+    d = _dims(B=64)
+    lens = _lens([8192] * 64)
+    st = ctypes.c_int32(-1)
+    assert L.qsa_decode_plan(ctypes.byref(d), lens, 0, ctypes.byref(c), ctypes.byref(m), ctypes.byref(st)) == 0
+    assert st.value == 1
+    share = c.value
+    assert 1 <= share <= 512 and m.value >= -(-512 // share)
+    waves = -(-64 * 8 * 512 // share)
+    ws = L.qsa_decode_workspace_size(ctypes.byref(d), lens, 0)
+    assert ws >= (waves + 64 * 8) * 4 * (128 + 2) * 4
     assert L.qsa_decode_workspace_size(ctypes.byref(_dims(Hq=30)), lens, 0) == 0
     cw = L.qsa_cascade_workspace_size(ctypes.byref(d), 4096, lens, 0)
     assert cw > L.qsa_decode_workspace_size(ctypes.byref(d), lens, 0)
@@ -110,10 +130,10 @@ def test_sequence_count_limit(L):
     d = _dims(B=65536)
     lens = _lens([16] * 65536)
     c, m = ctypes.c_int32(), ctypes.c_int32()
-    assert L.qsa_decode_plan(ctypes.byref(d), lens, 0, ctypes.byref(c), ctypes.byref(m)) == qsa.QSA_ERR_UNSUPPORTED
+    assert L.qsa_decode_plan(ctypes.byref(d), lens, 0, ctypes.byref(c), ctypes.byref(m), None) == qsa.QSA_ERR_UNSUPPORTED
     d = _dims(B=65535)
     lens = _lens([16] * 65535)
-    assert L.qsa_decode_plan(ctypes.byref(d), lens, 0, ctypes.byref(c), ctypes.byref(m)) == 0
+    assert L.qsa_decode_plan(ctypes.byref(d), lens, 0, ctypes.byref(c), ctypes.byref(m), None) == 0
 
 
 def test_topk_workspace_query(L):
