@@ -7,9 +7,10 @@
 //
 // Workgroup = 8 waves. Phases, separated by workgroup barriers:
 //  1. Score: the row's metadata is one contiguous stream of 512-byte [m | M]
-//     records (logical page order). 16 lanes per page, 4 pages per wave-step,
-//     32 pages per workgroup-step; records are loaded four steps ahead
-//     (double-buffered batches). The score arithmetic is the same as
+//     records (logical page order). 16 lanes per page, 4 pages per wave-step;
+//     a wave scores chunks of 8 consecutive pages with two chunks of records
+//     in flight (8 KiB per wave: smaller and fewer chunks in flight measured
+//     faster than 16-page ones). The score arithmetic is the same as
 //     score_kernel's (q split by sign, v_dot2 / fma, DPP sum, group max), so
 //     both paths produce bit-identical group scores. With refresh_tail set the
 //     wave owning the tail page rebuilds its min/max from the keys first and
@@ -37,7 +38,7 @@ constexpr int kRowWaves = 8;
 constexpr int kRowThreads = kRowWaves * kWave;
 static_assert(kRowThreads >= 256, "the radix histogram is cleared by 256 threads");
 constexpr int kKeysPerThread = (kRowMaxPages + kRowThreads - 1) / kRowThreads;
-constexpr int kChunkSteps = 4;                 // score steps per chunk (4 pages a step)
+constexpr int kChunkSteps = 2;                 // score steps per chunk (4 pages a step)
 constexpr int kChunkPages = 4 * kChunkSteps;    // consecutive pages scored by one wave
 constexpr int kScoreBufs = 2;                   // chunks of records in flight per wave
 

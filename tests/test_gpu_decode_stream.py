@@ -24,6 +24,8 @@ CASES = [
     ("short_rows_k2", [1, 16, 17, 33] + _rng.integers(1, 65, 92).tolist(), 32, 8, 2),
     ("long_rows_g8", [9000, 1, 13999] + _rng.integers(9000, 14001, 7).tolist(), 64, 8, 0),
     ("long_rows_g4_k300", [9001, 16000, 700] + _rng.integers(9000, 16001, 9).tolist(), 32, 8, 300),
+    ("hkv2_g8_many_rows", [1, 15, 16, 17] + _rng.integers(1, 48, 296).tolist(), 16, 2, 0),
+    ("hkv1_g4_k3", [1, 33] + _rng.integers(1, 96, 598).tolist(), 4, 1, 3),
 ]
 
 
