@@ -125,6 +125,16 @@ def test_decode_plan_and_workspace(L):
     assert cw > L.qsa_decode_workspace_size(ctypes.byref(d), lens, 0)
 
 
+def test_stream_split_sequence_limit(L):
+    # the stream split keeps per-sequence tables for at most 1024 sequences
+    c, m, st = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(-1)
+    for B, want in ((1024, 1), (1025, 0)):
+        d = _dims(B=B, Hq=4, Hkv=1)
+        assert L.qsa_decode_plan(ctypes.byref(d), _lens([20] * B), 0, ctypes.byref(c), ctypes.byref(m),
+                                 ctypes.byref(st)) == 0
+        assert st.value == want
+
+
 def test_sequence_count_limit(L):
     # the sequence index is a launch grid dimension: at most 65535
     d = _dims(B=65536)

@@ -98,6 +98,24 @@ def test_stream_rows_with_fewer_selected_than_planned():
     assert_close_out(out.cpu().numpy(), lse.cpu().numpy(), oo, ol)
 
 
+def test_stream_at_the_sequence_table_limit():
+    # 1024 sequences fill the stream kernel's per-sequence LDS tables; one
+    # more takes the units split. Both against the oracle.
+    lens = [1 + (37 * i) % 40 for i in range(1025)]
+    for B in (1024, 1025):
+        c = workloads.build_case(f"seqs{B}", B, 4, 1, 128, lens[:B], "bf16", 31, n_sentinel=3)
+        print(f"[case] sequence table limit B={B}", flush=True)
+        d = case_np(c)
+        g = c.to(DEV)
+        kv = qsa.PagedKV.from_case(g)
+        assert qsa.decode_plan(kv, 4, 0)[2] == (B <= 1024)
+        out, lse = qsa.paged_decode(g.q, kv, sm_scale=c.sm_scale)
+        torch.cuda.synchronize()
+        oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], "bf16", d["page_indptr"], d["page_indices"],
+                                d["seq_lens"], c.sm_scale)
+        assert_close_out(out.cpu().numpy(), lse.cpu().numpy(), oo, ol)
+
+
 @pytest.mark.parametrize("k", [None, 2])
 def test_stream_cascade_suffix(k):
     B, Hq, Hkv, prefix_len, suffix_len = 80, 32, 8, 256, 48
