@@ -96,9 +96,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the decode path shards over "
-                          "sequences and KV heads without any exchange, and no multi-GPU run is made; "
-                          "use --gpus 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU: the decode path would shard over "
+                          "sequences and KV heads without any exchange, so one GPU's share is the "
+                          "measured unit; use --gpus 1"}))
         sys.exit(2)
 
     import torch
