@@ -45,6 +45,13 @@ MEASURED_TRAFFIC = {
         "sha256_16": "28e95b6f9e5cbe07",
         "profile": "profiles/sparse_row_kernel_c2_sparse.md",
     },
+    # the decode stage: decode_stream_kernel + merge_kernel
+    ("c3_dense", "dense", "bound"): {
+        "bytes": 5143009266,
+        "sources": ["decode.hip", "decode_mfma.h", "decode_wave.h", "qsa_device.h", "qsa_internal.h", "api.hip"],
+        "sha256_16": "dfb34fc4c9451f13",
+        "profile": "profiles/decode_stream_kernel_c3_dense.md",
+    },
 }
 
 
@@ -282,8 +289,9 @@ def main():
         mt = accounting.meta_bytes(lens, Hkv, D, elem, tail_pages=1, rows_per_record=rows) if k else {"total": 0}
         step_bytes = dec["total"] + sc["total"] + tk["total"] + mt["total"]
         dom_name, dom_bytes = "decode", dec["total"]
-        dom_kernel = ("cascade prefix (MFMA) + split-K suffix decode + LSE merge" if cascade
-                      else "decode_split_kernel + merge_kernel (split-K paged decode, LSE merge)")
+        split = "decode_stream_kernel" if qsa.decode_plan(kvs[0], Hq, k or 0)[2] else "decode_split_kernel"
+        dom_kernel = (f"cascade prefix (MFMA) + split-K suffix decode ({split}) + LSE merge" if cascade
+                      else f"{split} + merge_kernel (split-K paged decode, LSE merge)")
     qps = B / (ms_step / 1e3)
     dom_ms = stage_ms[dom_name]["mean"]
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
@@ -325,7 +333,7 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": measured_traffic(args.config, path, args.scorer),
+            "traffic": measured_traffic(args.config, path or ("cascade" if cascade else "dense"), args.scorer),
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": round(dom_ms, 5),
         },
