@@ -117,14 +117,15 @@ int device_cus() {
   return cus[dev];
 }
 
-// Work units wanted per launch: two 4-wave units per CU, i.e. two waves per
-// SIMD, so that every SIMD gets the same number of pages in one round.
+// 4-wave workgroups that run at once: two per CU (two waves per SIMD).
 int target_units() { return 2 * device_cus(); }
 
 // Pages per unit: a multiple of 4 (one quarter per wave) sized so that the
-// rows' pages fill about target_units() equal units; counts per (b, h) row are
-// min(k, n_b) (every page when k <= 0). Capped at 192 (48 pages per wave; the
-// kernel takes up to 256).
+// rows' pages fill about one unit per CU; counts per (b, h) row are min(k,
+// n_b) (every page when k <= 0). Capped at 192 (48 pages per wave; the
+// kernel takes up to 256). (One unit per CU measured faster than two on the
+// short lists where units fit one round: 53.6 vs 54.6 us for the 8K-token,
+// top-153 step's split path; one per two CUs was slower, 57.8 us.)
 qsa::DecodePlan make_plan(const qsa_dims* d, const int32_t* lens, int32_t k) {
   qsa::DecodePlan plan;
   long long total = 0;
@@ -135,7 +136,7 @@ qsa::DecodePlan make_plan(const qsa_dims* d, const int32_t* lens, int32_t k) {
     maxc = std::max(maxc, c);
     total += (long long)d->num_kv_heads * c;
   }
-  const long long per = (total + target_units() - 1) / target_units();
+  const long long per = (total + device_cus() - 1) / device_cus();
   // (long rows: 192-256 pages per unit measured fastest; each unit start
   // and end costs a few microseconds, which smaller units pay more often,
   // while larger ones leave a longer tail in the last round)

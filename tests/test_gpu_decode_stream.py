@@ -1,8 +1,9 @@
 """The stream split of the decode (decode_stream_kernel: every wave takes an
 equal share of all rows' page lists, writing one partial per row segment)
-against the oracle, on shapes where the planner picks it: more rows than the
-work units that run at once, and long rows cut into many units. Each case
-first checks that the plan is the stream split."""
+against the oracle, on shapes where the planner picks it: more work units
+than run at once (more rows than two per CU here, each row spread over
+several waves' shares). Each case first checks that the plan is the stream
+split; the full-size dense test covers long rows cut into many units."""
 import numpy as np
 import pytest
 import torch
@@ -22,8 +23,8 @@ CASES = [
     # (label, lens, Hq, Hkv, k): k = 0 is dense
     ("short_rows_dense", [1, 16, 17, 33] + _rng.integers(1, 65, 92).tolist(), 32, 8, 0),
     ("short_rows_k2", [1, 16, 17, 33] + _rng.integers(1, 65, 92).tolist(), 32, 8, 2),
-    ("long_rows_g8", [9000, 1, 13999] + _rng.integers(9000, 14001, 7).tolist(), 64, 8, 0),
-    ("long_rows_g4_k300", [9001, 16000, 700] + _rng.integers(9000, 16001, 9).tolist(), 32, 8, 300),
+    ("rows_g8_several_waves", [1, 2000, 1999] + _rng.integers(500, 2001, 69).tolist(), 64, 8, 0),
+    ("rows_g4_k40", [700, 1500, 17] + _rng.integers(700, 1501, 67).tolist(), 32, 8, 40),
     ("hkv2_g8_many_rows", [1, 15, 16, 17] + _rng.integers(1, 48, 296).tolist(), 16, 2, 0),
     ("hkv1_g4_k3", [1, 33] + _rng.integers(1, 96, 598).tolist(), 4, 1, 3),
 ]
