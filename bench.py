@@ -288,10 +288,18 @@ def main():
         tk = accounting.topk_bytes(lens, Hkv, k) if k else {"total": 0}
         mt = accounting.meta_bytes(lens, Hkv, D, elem, tail_pages=1, rows_per_record=rows) if k else {"total": 0}
         step_bytes = dec["total"] + sc["total"] + tk["total"] + mt["total"]
-        dom_name, dom_bytes = "decode", dec["total"]
         split = "decode_stream_kernel" if qsa.decode_plan(kvs[0], Hq, k or 0)[2] else "decode_split_kernel"
-        dom_kernel = (f"cascade prefix (MFMA) + split-K suffix decode ({split}) + LSE merge" if cascade
-                      else f"{split} + merge_kernel (split-K paged decode, LSE merge)")
+        # the stage that takes the most time is the one the roofline reports
+        labels = {
+            "score+meta_tail": ("score_kernel (bound scores with the tail-page refresh)", sc["total"] + mt["total"]),
+            "topk": ("topk kernel (per-row radix select)", tk["total"]),
+            "decode": ((f"cascade prefix (MFMA) + split-K suffix decode ({split}) + LSE merge" if cascade
+                        else f"{split} + merge_kernel (split-K paged decode, LSE merge)"), dec["total"]),
+        }
+        dom_name = max((n for n in stage_ms if n in labels), key=lambda n: stage_ms[n]["mean"])
+        dom_kernel, dom_bytes = labels[dom_name]
+        if centroid and dom_name == "score+meta_tail":
+            dom_kernel = "score_kernel (centroid scores with the tail-page refresh)"
     qps = B / (ms_step / 1e3)
     dom_ms = stage_ms[dom_name]["mean"]
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
