@@ -164,11 +164,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
   for (int qt = 0; qt < kQT; ++qt)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[qt][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run[kQT], l_part[kQT];
+  // The softmax denominators come from the matrix cores as well: a 16x16x16
+  // product of P^T with an A operand whose row 0 is all ones leaves row 0 of
+  // lacc (lanes 0..15, element 0) holding the sum of the bf16 weights of
+  // query c16, the same weights the O^T products use, accumulated in fp32.
+  const uint2 ones_a = c16 == 0 ? make_uint2(0x3F803F80u, 0x3F803F80u) : make_uint2(0u, 0u);
+  f32x4_t lacc[kQT];
+  float m_run[kQT];
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
     m_run[qt] = -__builtin_inff();
-    l_part[qt] = 0.0f;
+    lacc[qt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
   // Attention over the block staged in LDS buffer buf (keys from kb).
@@ -199,15 +205,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
       float s[8];
-      float mx = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = sacc[kt][qt][i] * scale_log2;
-          s[4 * kt + i] = (full || kb + 16 * kt + 4 * g4 + i < kend) ? v : -__builtin_inff();
-          mx = fmaxf(mx, s[4 * kt + i]);
-        }
+        for (int i = 0; i < 4; ++i) s[4 * kt + i] = sacc[kt][qt][i] * scale_log2;
+      if (!full) {  // (workgroup-uniform: only the split's last block)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kb + 16 * kt + 4 * g4 + i >= kend) s[4 * kt + i] = -__builtin_inff();
+      }
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, s[i]);
       // the lane's own keys decide whether the reference must move (the
       // ballot is the cross-lane OR); only then is the column max reduced
       if (__builtin_amdgcn_ballot_w64(mx > m_run[qt] + kCasTau) != 0) {
@@ -216,7 +227,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
         const float mn = fmaxf(m_run[qt], mx);
         const float al = (mn == -__builtin_inff()) ? 1.0f : fast_exp2(m_run[qt] - mn);
         m_run[qt] = mn;
-        l_part[qt] *= al;
+        lacc[qt] *= al;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) oacc[qt][dt] *= al;
       }
@@ -229,11 +240,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
         const bf16x2_t w = {(__bf16)fast_exp2(s[2 * e] - m_run[qt]),
                             (__bf16)fast_exp2(s[2 * e + 1] - m_run[qt])};
         pk[e] = __builtin_bit_cast(uint32_t, w);
-        // the denominator sums the same bf16-rounded weights the MFMA uses
-        l_part[qt] += __uint_as_float(pk[e] << 16) + __uint_as_float(pk[e] & 0xFFFF0000u);
       }
       pt[qt][0] = make_uint2(pk[0], pk[1]);
       pt[qt][1] = make_uint2(pk[2], pk[3]);
+      lacc[qt] = mfma16k16(ones_a, pt[qt][0], lacc[qt]);
+      lacc[qt] = mfma16k16(ones_a, pt[qt][1], lacc[qt]);
     }
     // ---- O^T += V^T . P^T, one 16x16x16 product per 16-key tile: A rows =
     // dims 16 dt + c16, keys 4 g4 .. +3 of the tile, read transposed
@@ -282,9 +293,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
   // ---- partial (o relative to m_run, m_run, l) per query row
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
-    float l = l_part[qt];
-    l += xshfl(l, 16);
-    l += xshfl(l, 32);
+    const float l = lacc[qt][0];  // meaningful in lanes 0..15 (g4 == 0), which store it
     const int r = row0 + qt * 16 + c16;
     if (r < R) {
       const size_t pr = ((size_t)h * n_splits + split) * (size_t)R + r;
