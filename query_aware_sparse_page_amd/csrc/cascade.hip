@@ -65,7 +65,6 @@ __device__ __forceinline__ f32x4_t mfma16k16(const uint2& a, const uint2& b, f32
 struct CascadeShared {
   alignas(16) uint16_t k[2][kKeyBlock][kKPitch];
   alignas(16) uint16_t v[2][kKeyBlock][kVPitch];
-  int pg[kMaxSplitPages];
 };
 
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(512 / kThreads))) cascade_prefix_kernel(
@@ -98,15 +97,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
   const int n_pre_pages = (prefix_len + kPage - 1) / kPage;
   const int pg0 = kbeg / kPage;
 
-  // the split's physical pages (-1: outside the prefix or out of range)
-  for (int i = tid; i < kMaxSplitPages; i += kThreads) {
+  // the split's physical pages in registers, entry i in lane i % 64 of
+  // pgr[i / 64] (-1: outside the prefix or out of range); a block's page is
+  // then one v_readlane away instead of an LDS round trip
+  int pgr[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int i = lane + 64 * half;
     const int pgi = pg0 + i;
     int p = -1;
-    if (pgi < n_pre_pages && pgi * kPage < kend) {
+    if (i < kMaxSplitPages && pgi < n_pre_pages && pgi * kPage < kend) {
       p = prefix_pages[pgi];
       p = (p >= 0 && p < num_phys) ? p : -1;
     }
-    sh.pg[i] = p;
+    pgr[half] = p;
   }
 
   // B operand of S^T: Q^T[dims 8g + 32ks .. +8][query c16] per query tile
@@ -122,7 +126,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
     for (int ks = 0; ks < 4; ++ks)
       qb[qt][ks] = ok ? ld16(qrow + (8 * g4 + 32 * ks) * 2) : make_uint4(0, 0, 0, 0);
   }
-  __syncthreads();  // page list
 
   const size_t page_stride = (size_t)Hkv * kTileBytes;
   const char* kbase = reinterpret_cast<const char*>(k_pool) + (size_t)h * kTileBytes;
@@ -135,25 +138,30 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
   // pages out of range, are staged as zeros.
   const int last_blk = nblk > 0 ? nblk - 1 : 0;
   const int last_pg = kend > kbeg ? (kend - 1) / kPage - pg0 : 0;  // the split's last page (relative)
-  const int toff = ((tid >> 4) & 15) * kRowBytes + (tid & 15) * 16;
+  const uint32_t toff = ((tid >> 4) & 15) * kRowBytes + (tid & 15) * 16;  // (unsigned: a 32-bit offset to a uniform base)
+  // A wave's 64 threads stage rows of one page (idx / 256 is the same for
+  // all of them), so the page and its tile address are wave-uniform.
   auto page_of = [&](int bi, int pg) -> int {  // physical page, -1 if out of range
-    return sh.pg[min(2 * min(bi, last_blk) + pg, last_pg)];
+    const int i = min(2 * min(bi, last_blk) + pg, last_pg);  // < kMaxSplitPages <= 128
+    return i < 64 ? __builtin_amdgcn_readlane(pgr[0], i) : __builtin_amdgcn_readlane(pgr[1], i - 64);
   };
-  auto issue = [&](int bi, uint4 (&kr)[kStageReps], uint4 (&vr)[kStageReps]) {
+  // pv: the staged page of each chunk, kept for stage() (-1: staged as zeros)
+  auto issue = [&](int bi, uint4 (&kr)[kStageReps], uint4 (&vr)[kStageReps], int (&pv)[kStageReps]) {
 #pragma unroll
     for (int rep = 0; rep < kStageReps; ++rep) {
-      const int idx = tid + kThreads * rep;
-      const size_t off = (size_t)max(page_of(bi, idx >> 8), 0) * page_stride + toff;
-      kr[rep] = ld16(kbase + off);
-      vr[rep] = ld16(vbase + off);
+      pv[rep] = page_of(bi, (wave * 64 + kThreads * rep) >> 8);  // = idx >> 8, wave-uniform
+      const size_t poff = (size_t)max(pv[rep], 0) * page_stride;
+      kr[rep] = ld16(kbase + poff + toff);
+      vr[rep] = ld16(vbase + poff + toff);
     }
   };
-  auto stage = [&](int bi, int buf, const uint4 (&kr)[kStageReps], const uint4 (&vr)[kStageReps]) {
+  auto stage = [&](int bi, int buf, const uint4 (&kr)[kStageReps], const uint4 (&vr)[kStageReps],
+                   const int (&pv)[kStageReps]) {
 #pragma unroll
     for (int rep = 0; rep < kStageReps; ++rep) {
       const int idx = tid + kThreads * rep;
       const int key = idx >> 4;
-      const bool ok = bi < nblk && kbeg + bi * kKeyBlock + key < kend && page_of(bi, idx >> 8) >= 0;
+      const bool ok = bi < nblk && kbeg + bi * kKeyBlock + key < kend && pv[rep] >= 0;
       *reinterpret_cast<uint4*>(&sh.k[buf][key][(idx & 15) * 8]) = ok ? kr[rep] : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(&sh.v[buf][key][(idx & 15) * 8]) = ok ? vr[rep] : make_uint4(0, 0, 0, 0);
     }
@@ -267,12 +275,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
   // bi is computed; buffers rotate through an unrolled loop (no copies)
   if (nblk > 0) {
     uint4 kr[kDepth][kStageReps], vr[kDepth][kStageReps];
+    int pv[kDepth][kStageReps];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
-      issue(d, kr[d], vr[d]);
+      issue(d, kr[d], vr[d], pv[d]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    stage(0, 0, kr[0], vr[0]);
+    stage(0, 0, kr[0], vr[0], pv[0]);
     __syncthreads();
     const int rounds = (nblk + kDepth - 1) / kDepth;
     int bi = 0;
@@ -280,10 +289,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
 #pragma unroll
       for (int r = 0; r < kDepth; ++r) {
         // slot r held block bi, staged in the previous step: reload it with bi + kDepth
-        issue(bi + kDepth, kr[r], vr[r]);
+        issue(bi + kDepth, kr[r], vr[r], pv[r]);
         __builtin_amdgcn_sched_barrier(0);
         compute(kbeg + bi * kKeyBlock, bi & 1);
-        stage(bi + 1, (bi + 1) & 1, kr[(r + 1) % kDepth], vr[(r + 1) % kDepth]);
+        stage(bi + 1, (bi + 1) & 1, kr[(r + 1) % kDepth], vr[(r + 1) % kDepth], pv[(r + 1) % kDepth]);
         __syncthreads();
         ++bi;
       }
