@@ -52,6 +52,14 @@ MEASURED_TRAFFIC = {
         "sha256_16": "91dd591e8539e0cd",
         "profile": "profiles/decode_stream_kernel_c3_dense.md",
     },
+    # the cascade call: cascade_prefix_kernel + decode_stream_kernel + merge_kernel
+    ("c5_cascade", "cascade", "bound"): {
+        "bytes": 270370674,
+        "sources": ["cascade.hip", "decode.hip", "decode_mfma.h", "decode_wave.h", "qsa_device.h",
+                    "qsa_internal.h", "api.hip"],
+        "sha256_16": "36a074fb36f3b36f",
+        "profile": "profiles/cascade_prefix_kernel_counters_c5_cascade.md",
+    },
 }
 
 
