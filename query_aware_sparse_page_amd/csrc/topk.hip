@@ -189,10 +189,14 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
   constexpr int kRadixBits = 13;
   constexpr int kBins = 1 << kRadixBits;
   constexpr int kBinsPerThread = kBins / kThreads;
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t wsum[kWaves];
+  // Histograms, scan sums and the picked digit alternate between two
+  // buffers by pass, so a pass needs two workgroup barriers: the next
+  // pass's histogram is cleared while this one is filled, and nothing is
+  // rewritten before every thread has passed the next barrier.
+  __shared__ uint32_t hist[2][kBins];
+  __shared__ uint32_t wsum[2][kWaves];
   __shared__ uint32_t wmin[kWaves], wmax[kWaves];
-  __shared__ uint32_t s_digit, s_krem, s_bin;
+  __shared__ uint32_t s_pick[2][3];  // digit, pages still needed, pages in the digit's bin
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -239,6 +243,12 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
       kmax = max(kmax, keys[i]);
     }
   }
+  // exact: digit width about log2(n) + 2 bits, so the histogram stays small
+  // for short rows and a pass splits a long row finely
+  const int width = kApprox ? digit_bits : min(kRadixBits, max(4, 34 - __builtin_clz((uint32_t)n)));
+  // the first pass's histogram (at most 2^width bins) is cleared before the
+  // min / max barrier
+  for (int i = tid; i < (1 << width); i += kThreads) hist[0][i] = 0u;
   kmin = wave_min_u(kmin);
   kmax = wave_max_u(kmax);
   if (lane == 0) {
@@ -260,9 +270,7 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
   int shift = 0;
   int passes = 0;
   const uint32_t diff = kmin ^ kmax;
-  // exact: digit width about log2(n) + 2 bits, so the histogram stays small
-  // for short rows and a pass splits a long row finely
-  const int width = kApprox ? digit_bits : min(kRadixBits, max(4, 34 - __builtin_clz((uint32_t)n)));
+  int pb = 0;  // this pass's buffers
   if (diff != 0u) {
     shift = 32 - __builtin_clz(diff);               // bits below `shift` still open
     prefix = (uint32_t)((uint64_t)kmin >> shift);
@@ -270,12 +278,15 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
       const int nb = shift < width ? shift : width;
       const int lo = shift - nb;
       const uint32_t nbins = 1u << nb;
-      for (int i = tid; i < (int)nbins; i += kThreads) hist[i] = 0u;
-      __syncthreads();
+      uint32_t* hcur = hist[pb];
 #pragma unroll
       for (int i = 0; i < kKeys; ++i) {
         if (j0 + i < n && (uint32_t)((uint64_t)keys[i] >> shift) == prefix)
-          atomicAdd(&hist[(keys[i] >> lo) & (nbins - 1u)], 1u);
+          atomicAdd(&hcur[(keys[i] >> lo) & (nbins - 1u)], 1u);
+      }
+      if (lo > 0) {  // the next pass's histogram
+        const int nb_next = lo < width ? lo : width;
+        for (int i = tid; i < (1 << nb_next); i += kThreads) hist[pb ^ 1][i] = 0u;
       }
       __syncthreads();
       // thread t scans digits nbins-1 - (t*B .. t*B+B-1), i.e. descending
@@ -284,29 +295,29 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
 #pragma unroll
       for (int i = 0; i < kBinsPerThread; ++i) {
         const int pos = tid * kBinsPerThread + i;
-        cnt[i] = pos < (int)nbins ? hist[nbins - 1 - pos] : 0u;
+        cnt[i] = pos < (int)nbins ? hcur[nbins - 1 - pos] : 0u;
         local += cnt[i];
       }
       uint32_t total;
-      uint32_t above = block_excl_scan<kWaves>(local, wsum, &total);
+      uint32_t above = block_excl_scan_once<kWaves>(local, wsum[pb], &total);
       if (above < krem && above + local >= krem) {
 #pragma unroll
         for (int i = 0; i < kBinsPerThread; ++i) {
           if (above < krem && above + cnt[i] >= krem) {
-            s_digit = nbins - 1u - (uint32_t)(tid * kBinsPerThread + i);
-            s_krem = krem - above;
-            s_bin = cnt[i];
+            s_pick[pb][0] = nbins - 1u - (uint32_t)(tid * kBinsPerThread + i);
+            s_pick[pb][1] = krem - above;
+            s_pick[pb][2] = cnt[i];
           }
           above += cnt[i];
         }
       }
       __syncthreads();
-      prefix = (prefix << nb) | s_digit;
-      krem = s_krem;
-      const uint32_t bin = s_bin;
+      prefix = (prefix << nb) | s_pick[pb][0];
+      krem = s_pick[pb][1];
+      const uint32_t bin = s_pick[pb][2];
       shift = lo;
       ++passes;
-      __syncthreads();
+      pb ^= 1;
       if (bin == krem) break;                          // the whole bin is taken
       if (kApprox && (uint32_t)keff - krem >= (uint32_t)min_confident) break;
     }
@@ -324,7 +335,7 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
     }
   }
   uint32_t total;
-  const uint32_t excl = block_excl_scan<kWaves>(gt_n | (eq_n << 16), wsum, &total);
+  const uint32_t excl = block_excl_scan_once<kWaves>(gt_n | (eq_n << 16), wsum[pb], &total);
   uint32_t gt_before = excl & 0xFFFFu;
   uint32_t eq_before = excl >> 16;
   const uint32_t c = total >> 16;                     // pages in the kept bin
