@@ -186,7 +186,8 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
     int* __restrict__ sel, int* __restrict__ sel_count, int* __restrict__ sel_phys,
     int* __restrict__ passes_out) {
   constexpr int kWaves = kThreads / 64;
-  constexpr int kRadixBits = 13;
+  constexpr int kRadixBits = 13;  // widest digit (the approximate select's digit_bits <= 13)
+  constexpr int kExactBits = 10;  // widest digit of the exact select
   constexpr int kBins = 1 << kRadixBits;
   constexpr int kBinsPerThread = kBins / kThreads;
   // Histograms, scan sums and the picked digit alternate between two
@@ -244,8 +245,11 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(
     }
   }
   // exact: digit width about log2(n) + 2 bits, so the histogram stays small
-  // for short rows and a pass splits a long row finely
-  const int width = kApprox ? digit_bits : min(kRadixBits, max(4, 34 - __builtin_clz((uint32_t)n)));
+  // for short rows, at most kExactBits: a pass over 1024 bins (one per
+  // thread) is cheaper than one over 8192, which more than pays for a third
+  // pass on rows of 8192 pages (13.5 against 14.4 us per launch for 10 and
+  // 13 bits)
+  const int width = kApprox ? digit_bits : min(kExactBits, max(4, 34 - __builtin_clz((uint32_t)n)));
   // the first pass's histogram (at most 2^width bins) is cleared before the
   // min / max barrier
   for (int i = tid; i < (1 << width); i += kThreads) hist[0][i] = 0u;
