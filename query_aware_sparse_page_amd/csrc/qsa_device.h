@@ -237,26 +237,6 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
   return before + incl - v;
 }
 
-// As block_excl_scan, without the closing barrier: wsum must not be written
-// again until every thread has passed another workgroup barrier.
-template <int kWaves>
-__device__ __forceinline__ uint32_t block_excl_scan_once(uint32_t v, uint32_t* wsum, uint32_t* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_scan_incl(v);
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t t = wsum[w];
-    before += (w < wave) ? t : 0u;
-    tot += t;
-  }
-  *total = tot;
-  return before + incl - v;
-}
-
 template <int kCtrl>
 __device__ __forceinline__ uint32_t dpp_full_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xF, 0xF, true);

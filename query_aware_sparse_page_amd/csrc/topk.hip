@@ -164,6 +164,26 @@ __global__ void __launch_bounds__(256) topk_wave_kernel(
   if (lane == 0) sel_count[row] = keff;
 }
 
+// As block_excl_scan, without the closing barrier: wsum must not be written
+// again until every thread has passed another workgroup barrier.
+template <int kWaves>
+__device__ __forceinline__ uint32_t block_excl_scan_once(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_scan_incl(v);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t t = wsum[w];
+    before += (w < wave) ? t : 0u;
+    tot += t;
+  }
+  *total = tot;
+  return before + incl - v;
+}
+
 // Block kernel (one workgroup per row). kApprox = false is the exact select;
 // kApprox = true is the approximate select of the Vortex digest
 // (optimisations: radix top-K that terminates early once it holds enough
