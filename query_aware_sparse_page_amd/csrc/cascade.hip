@@ -45,7 +45,7 @@ constexpr int kStageReps = 512 / kThreads;  // 16-byte K and V chunks a thread s
 static_assert(kStageReps >= 1 && kStageReps * kThreads == 512, "a block is 32 keys x 16 chunks");
 constexpr int kKeyBlock = 32;       // keys per block
 constexpr int kDepth = 2;           // blocks whose global loads are in flight
-constexpr int kKPitch = kCD + 8;    // LDS row of K in bf16 (256 B + 16 B pad)
+constexpr int kKPitch = kCD + 16;   // LDS row of K in bf16 (256 B + 32 B pad: no bank conflicts in the A-operand reads)
 constexpr int kVPitch = kCD + 16;   // LDS row of V in bf16 (256 B + 32 B pad)
 constexpr int kMaxSplitPages = 80;  // pages of one split (the host keeps splits <= 1056 tokens)
 constexpr float kCasTau = 8.0f;
