@@ -5,10 +5,10 @@
 // With B sequences sharing the prefix, the queries of one KV head form a
 // dense [R = B*g, D] block and the prefix a [D, prefix_len] block: a real
 // contraction, so it runs on the matrix cores (v_mfma_f32_16x16x32_bf16,
-// fp32 accumulate). Flash-attention style: a workgroup owns 128 query rows
-// (8 waves, one 16-column tile each) and one split of the prefix keys; it
-// walks the split in blocks of 32 keys (two pages), keeping an online
-// softmax per query.
+// fp32 accumulate). Flash-attention style: a workgroup owns 256 query rows
+// (8 waves, two 16-column tiles each, so every K and V read from LDS serves
+// 32 queries) and one split of the prefix keys; it walks the split in blocks
+// of 32 keys (two pages), keeping an online softmax per query.
 //
 // Orientation: the wave computes S^T = K . Q^T (rows = keys, cols = queries),
 // so the probabilities come out of the MFMA already in the layout of the B
@@ -20,13 +20,14 @@
 // group's lane s reads key row key0 + s/4, dims d0 + 4 (s%4) .. +3, and lane
 // s receives V[key0 .. key0+3][d0 + s]).
 //
-// MFMA operand layouts (lane l, g = l/16):
-//   16x16x32: A[i][k]: i = l%16, k = 8g .. 8g+7     B[k][j]: j = l%16, k = 8g .. 8g+7
-//   16x16x16: A[i][k]: i = l%16, k = 4g .. 4g+3     B[k][j]: j = l%16, k = 4g .. 4g+3
-//   both:     C[i][j]: j = l%16, i = 4g .. 4g+3
-// S^T (16x16x32 over the head dim) leaves lane l the logits of keys 4g .. 4g+3
-// of each 16-key tile: the k-slots of the B operand of that tile's
-// 16x16x16 product O^T += V^T . P^T.
+// MFMA operand layout (v_mfma_f32_16x16x32_bf16, lane l, g = l/16):
+//   A[i][k]: i = l%16, k = 8g .. 8g+7     B[k][j]: j = l%16, k = 8g .. 8g+7
+//   C[i][j]: j = l%16, i = 4g .. 4g+3
+// S^T (over the head dim) leaves lane l the logits of keys 4g .. 4g+3 of each
+// 16-key tile. O^T += V^T . P^T takes the block's 32 keys in one product with
+// its k-slots 8g .. 8g+7 holding keys 4g .. 4g+3 of tile 0 and then of tile 1
+// (any order works as long as A and B agree): the B operand is the lane's own
+// eight weights, and the A operand two transposing reads, one per tile.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -38,7 +39,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kCD = 128;            // head dim
 constexpr int kWaves = 8;           // waves per workgroup
-constexpr int kQT = 1;              // 16-query tiles per wave (one: 114 VGPRs, 4 waves per SIMD)
+constexpr int kQT = 2;              // 16-query tiles per wave (180 VGPRs: one workgroup per CU)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWG = kWaves * 16 * kQT;
 constexpr int kStageReps = 512 / kThreads;  // 16-byte K and V chunks a thread stages per block
@@ -55,12 +56,7 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ f32x4_t mfma16k16(const uint2& a, const uint2& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
-                                                   __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
-}
 
 struct CascadeShared {
   alignas(16) uint16_t k[2][kKeyBlock][kKPitch];
@@ -172,11 +168,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
   for (int qt = 0; qt < kQT; ++qt)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[qt][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  // The softmax denominators come from the matrix cores as well: a 16x16x16
-  // product of P^T with an A operand whose row 0 is all ones leaves row 0 of
+  // The softmax denominators come from the matrix cores as well: a product
+  // of P^T with an A operand whose row 0 is all ones leaves row 0 of
   // lacc (lanes 0..15, element 0) holding the sum of the bf16 weights of
   // query c16, the same weights the O^T products use, accumulated in fp32.
-  const uint2 ones_a = c16 == 0 ? make_uint2(0x3F803F80u, 0x3F803F80u) : make_uint2(0u, 0u);
+  const uint4 ones_a = c16 == 0 ? make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u)
+                                 : make_uint4(0u, 0u, 0u, 0u);
   f32x4_t lacc[kQT];
   float m_run[kQT];
 #pragma unroll
@@ -251,23 +248,24 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
       }
       pt[qt][0] = make_uint2(pk[0], pk[1]);
       pt[qt][1] = make_uint2(pk[2], pk[3]);
-      lacc[qt] = mfma16k16(ones_a, pt[qt][0], lacc[qt]);
-      lacc[qt] = mfma16k16(ones_a, pt[qt][1], lacc[qt]);
+      lacc[qt] = mfma16(ones_a, make_uint4(pt[qt][0].x, pt[qt][0].y, pt[qt][1].x, pt[qt][1].y), lacc[qt]);
     }
-    // ---- O^T += V^T . P^T, one 16x16x16 product per 16-key tile: A rows =
-    // dims 16 dt + c16, keys 4 g4 .. +3 of the tile, read transposed
+    // ---- O^T += V^T . P^T, one product per 16 dims over the block's 32
+    // keys: A rows = dims 16 dt + c16, keys 4 g4 .. +3 of tile 0 then of
+    // tile 1, each read transposed
     typedef short lds_v4i16 __attribute__((ext_vector_type(4)));
     const uint16_t* vsrc = &sh.v[buf][4 * g4 + (c16 >> 2)][4 * (c16 & 3)];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
+      uint2 a[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const lds_v4i16 a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) lds_v4i16*)(vsrc + 16 * kt * kVPitch + 16 * dt));
-        const uint2 a = __builtin_bit_cast(uint2, a4);
+      for (int kt = 0; kt < 2; ++kt)
+        a[kt] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) lds_v4i16*)(vsrc + 16 * kt * kVPitch + 16 * dt)));
+      const uint4 a8 = make_uint4(a[0].x, a[0].y, a[1].x, a[1].y);
 #pragma unroll
-        for (int qt = 0; qt < kQT; ++qt) oacc[qt][dt] = mfma16k16(a, pt[qt][kt], oacc[qt][dt]);
-      }
+      for (int qt = 0; qt < kQT; ++qt)
+        oacc[qt][dt] = mfma16(a8, make_uint4(pt[qt][0].x, pt[qt][0].y, pt[qt][1].x, pt[qt][1].y), oacc[qt][dt]);
     }
   };
 
