@@ -47,17 +47,17 @@ MEASURED_TRAFFIC = {
     },
     # the decode stage: decode_stream_kernel + merge_kernel
     ("c3_dense", "dense", "bound"): {
-        "bytes": 5143026988,
+        "bytes": 5142985564,
         "sources": ["decode.hip", "decode_mfma.h", "decode_wave.h", "qsa_device.h", "qsa_internal.h", "api.hip"],
-        "sha256_16": "91dd591e8539e0cd",
+        "sha256_16": "5c0d1a7ec84a1f17",
         "profile": "profiles/decode_stream_kernel_c3_dense.md",
     },
     # the cascade call: cascade_prefix_kernel + decode_stream_kernel + merge_kernel
     ("c5_cascade", "cascade", "bound"): {
-        "bytes": 269514162,
+        "bytes": 269486332,
         "sources": ["cascade.hip", "decode.hip", "decode_mfma.h", "decode_wave.h", "qsa_device.h",
                     "qsa_internal.h", "api.hip"],
-        "sha256_16": "48ec92689949a4ae",
+        "sha256_16": "72d810bb3088ca38",
         "profile": "profiles/cascade_prefix_kernel_counters_c5_cascade.md",
     },
 }
