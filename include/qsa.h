@@ -26,9 +26,14 @@
  *  - Supported shapes: page_size 16; (dtype, head_dim) = (QSA_BF16, 128) or
  *    (QSA_F32, 64) - both make one (page, KV head) tile 4 KiB; group size
  *    g = Hq / Hkv in {1, 2, 4, 8}. Other shapes return QSA_ERR_UNSUPPORTED.
- *  - Robustness: a logical page index outside [0, n_b) or a physical page id
- *    outside [0, num_phys_pages) is skipped (treated as holding no tokens),
- *    never dereferenced.
+ *  - Robustness: a logical page index outside [0, n_b), a physical page id
+ *    outside [0, num_phys_pages) or a sel_count outside [1, min(k, n_b)] is
+ *    never dereferenced or followed: the page is skipped (treated as holding
+ *    no tokens; a count is clamped). By default this is silent. In checked
+ *    mode (qsa_set_checked below) every kernel that skips such an entry
+ *    records it in a device error word, and the call then returns
+ *    QSA_ERR_DEVICE naming what was out of range (its outputs are those of
+ *    the skipping run).
  */
 #ifndef QSA_H_
 #define QSA_H_
@@ -201,7 +206,7 @@ qsa_status qsa_topk_pages_approx(const qsa_dims* dims, const qsa_paged_kv* kv,
  * results). z_t = sm_scale * q.k_t; out = sum_t e^{z_t} v_t / sum_t e^{z_t}
  * (fp32 [B, Hq, D]); lse = ln sum_t e^{z_t} (fp32 [B, Hq], or NULL).
  * sel: [B, Hkv, k] logical page indices; sel_count [B, Hkv] (each in
- * [1, k]); k is the row stride of sel. Pages are split into work units that
+ * [1, min(k, n_b)]); k is the row stride of sel. Pages are split into work units that
  * run in parallel and are merged by log-sum-exp. Workspace:
  * qsa_decode_workspace_size(dims, seq_lens_host, sel ? k : 0). */
 qsa_status qsa_paged_decode(const qsa_dims* dims, const void* q,
@@ -302,6 +307,21 @@ size_t qsa_sparse_decode_workspace_size(const qsa_dims* dims, const int32_t* seq
 qsa_status qsa_decode_plan(const qsa_dims* dims, const int32_t* seq_lens_host,
                            int32_t k, int32_t* chunk_pages, int32_t* max_units,
                            int32_t* stream);
+
+/* Checked mode (process-wide; off unless the environment holds QSA_CHECKED
+ * set to anything but "" or "0", or qsa_set_checked(1) is called). The
+ * range checks that keep a corrupted page table, selection or count from
+ * being dereferenced run in every call (see Robustness above); checked mode
+ * adds their report: each compute call clears a per-device error word on
+ * its stream, passes it to its kernels, then waits for the stream and
+ * returns QSA_ERR_DEVICE if any kernel skipped an out-of-range entry. The
+ * wait makes checked calls synchronous, so they are meant for debugging and
+ * tests, not for graph capture; concurrent checked calls on one device share
+ * the word, so a report may name another call's entry. The top-K calls read
+ * no pool and report nothing. (The CS336 lecture 10 page, §9.2: the block
+ * table is the indirection these checks guard.) */
+void qsa_set_checked(int32_t on);
+int32_t qsa_get_checked(void);
 
 /* floor(budget_tokens / page_size): a token budget in whole pages (>= 0). */
 int32_t qsa_budget_pages(int32_t budget_tokens, int32_t page_size);

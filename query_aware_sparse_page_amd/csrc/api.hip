@@ -1,16 +1,21 @@
 // The libqsa C ABI: argument validation, work planning and kernel launches on
 // the caller's stream. Declarations and contracts are in include/qsa.h.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
+#include <mutex>
 #include <string>
 
+#include "host.h"
 #include "qsa.h"
 #include "qsa_internal.h"
 
-namespace {
+namespace qsa {
+namespace host {
 
 thread_local std::string g_last_error;
 
@@ -33,9 +38,6 @@ qsa_status device_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(QSA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
-
-constexpr size_t kAlign = 256;
-size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int pages_of(int L) { return (L + 15) / 16; }
 
@@ -180,15 +182,6 @@ qsa_status check_plan(const qsa::DecodePlan& p) {
   return QSA_OK;
 }
 
-// Decode workspace: [partial outputs][partial (max, sum)][stream split: the
-// rows' (first, last) waves], each region 256-byte aligned. Partial slots:
-// rows x max_units (units), or waves + rows (stream: slot w + r for the
-// segment of row r in wave w).
-struct DecodeWs {
-  size_t o_bytes = 0, ml_bytes = 0, rs_bytes = 0;
-  size_t total() const { return align_up(o_bytes) + align_up(ml_bytes) + align_up(rs_bytes); }
-};
-
 DecodeWs decode_ws(const qsa_dims* d, const qsa::DecodePlan& plan) {
   const size_t rows = (size_t)d->num_seqs * d->num_kv_heads;
   const size_t slots = plan.stream ? (size_t)plan.waves + rows : rows * plan.max_units;
@@ -255,11 +248,102 @@ SparseWs sparse_ws(const qsa_dims* d, const int32_t* lens, int stride, int k) {
   return w;
 }
 
+// ---- checked mode ----------------------------------------------------------
+// Every kernel that skips a page because a table or selection entry is out
+// of range can OR a bit into a device error word. In checked mode each entry
+// point clears the word before its launches (with a one-thread kernel),
+// passes it to them, then waits for the stream and reads it back: a set bit
+// turns the call's status into QSA_ERR_DEVICE. Unchecked (the default), the
+// kernels get no word and skip silently.
+
+namespace {
+
+// The error word: one per device (each GPU the library runs on holds its own
+// copy, at its own address).
+__device__ unsigned int g_err_word;
+
+__global__ void clear_word_kernel(unsigned int* w) {
+  if (threadIdx.x == 0) *w = 0u;
+}
+
+std::atomic<int> g_checked{-1};  // -1: not read from the environment yet
+
+constexpr int kMaxDevices = 64;
+std::mutex g_word_mu;
+unsigned int* g_word_ptr[kMaxDevices] = {nullptr};
+
 }  // namespace
+
+bool checked_mode() {
+  int v = g_checked.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = std::getenv("QSA_CHECKED");
+    v = (e != nullptr && *e != '\0' && std::strcmp(e, "0") != 0) ? 1 : 0;
+    int expect = -1;
+    g_checked.compare_exchange_strong(expect, v);
+    v = g_checked.load(std::memory_order_relaxed);
+  }
+  return v == 1;
+}
+
+void set_checked_mode(bool on) { g_checked.store(on ? 1 : 0); }
+
+qsa_status Checked::begin(qsa::LaunchCommon& c, hipStream_t stream) {
+  word_ = nullptr;
+  if (!checked_mode()) return QSA_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "checked mode: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QSA_ERR_UNSUPPORTED, "checked mode: device %d (at most %d devices)", dev, kMaxDevices);
+  {
+    std::lock_guard<std::mutex> lock(g_word_mu);
+    if (g_word_ptr[dev] == nullptr) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_err_word));
+      if (e != hipSuccess) return device_status(e, "checked mode: hipGetSymbolAddress");
+      g_word_ptr[dev] = static_cast<unsigned int*>(p);
+    }
+    word_ = g_word_ptr[dev];
+  }
+  hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, stream, word_);
+  e = hipGetLastError();
+  if (e != hipSuccess) {
+    word_ = nullptr;
+    return device_status(e, "checked mode: clearing the error word");
+  }
+  c.err = word_;
+  return QSA_OK;
+}
+
+qsa_status Checked::end(qsa_status s, hipStream_t stream) {
+  if (word_ == nullptr || s != QSA_OK) return s;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return device_status(e, "checked mode: hipStreamSynchronize");
+  unsigned int v = 0;
+  e = hipMemcpy(&v, word_, sizeof(v), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return device_status(e, "checked mode: reading the error word");
+  if (v == 0u) return ok();
+  std::string what;
+  if (v & qsa::kErrPhys) what += " a page table entry outside [0, num_phys_pages);";
+  if (v & qsa::kErrSel) what += " a selected logical page outside [0, n_b);";
+  if (v & qsa::kErrCount) what += " a sel_count entry outside [1, min(k, n_b)];";
+  return fail(QSA_ERR_DEVICE, "device range check (word 0x%x):%s the entries were skipped", v,
+              what.c_str());
+}
+
+}  // namespace host
+}  // namespace qsa
+
+using namespace qsa::host;
 
 extern "C" {
 
 int32_t qsa_version(void) { return 1; }
+
+void qsa_set_checked(int32_t on) { set_checked_mode(on != 0); }
+
+int32_t qsa_get_checked(void) { return checked_mode() ? 1 : 0; }
 
 const char* qsa_status_string(qsa_status s) {
   switch (s) {
@@ -290,9 +374,12 @@ qsa_status qsa_build_page_meta(const qsa_dims* dims, const qsa_paged_kv* kv, int
   if (stride < max_pages)
     return fail(QSA_ERR_INVALID_ARG, "stride %d < longest sequence's page count %d", stride,
                 max_pages);
-  return device_status(
-      qsa::launch_build_meta(common(dims, kv), max_pages, tail_pages, meta, stride, stream),
-      "build_page_meta launch");
+  qsa::LaunchCommon c = common(dims, kv);
+  Checked chk;
+  if ((s = chk.begin(c, stream)) != QSA_OK) return s;
+  return chk.end(device_status(qsa::launch_build_meta(c, max_pages, tail_pages, meta, stride, stream),
+                               "build_page_meta launch"),
+                 stream);
 }
 
 qsa_status qsa_score_pages(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv, void* meta,
@@ -309,9 +396,13 @@ qsa_status qsa_score_pages(const qsa_dims* dims, const void* q, const qsa_paged_
                 max_pages);
   if (refresh_tail != 0 && refresh_tail != 1)
     return fail(QSA_ERR_INVALID_ARG, "refresh_tail %d (0 or 1)", refresh_tail);
-  return device_status(qsa::launch_score(common(dims, kv), q, meta, refresh_tail, group_scores,
-                                         head_scores, stride, stream),
-                       "score_pages launch");
+  qsa::LaunchCommon c = common(dims, kv);
+  Checked chk;
+  if ((s = chk.begin(c, stream)) != QSA_OK) return s;
+  return chk.end(device_status(qsa::launch_score(c, q, meta, refresh_tail, group_scores, head_scores,
+                                                 stride, stream),
+                               "score_pages launch"),
+                 stream);
 }
 
 qsa_status qsa_build_page_centroids(const qsa_dims* dims, const qsa_paged_kv* kv,
@@ -326,9 +417,13 @@ qsa_status qsa_build_page_centroids(const qsa_dims* dims, const qsa_paged_kv* kv
   if (stride < max_pages)
     return fail(QSA_ERR_INVALID_ARG, "stride %d < longest sequence's page count %d", stride,
                 max_pages);
-  return device_status(
-      qsa::launch_build_centroids(common(dims, kv), max_pages, tail_pages, cent, stride, stream),
-      "build_page_centroids launch");
+  qsa::LaunchCommon c = common(dims, kv);
+  Checked chk;
+  if ((s = chk.begin(c, stream)) != QSA_OK) return s;
+  return chk.end(
+      device_status(qsa::launch_build_centroids(c, max_pages, tail_pages, cent, stride, stream),
+                    "build_page_centroids launch"),
+      stream);
 }
 
 qsa_status qsa_score_pages_centroid(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv,
@@ -345,9 +440,13 @@ qsa_status qsa_score_pages_centroid(const qsa_dims* dims, const void* q, const q
                 max_pages);
   if (refresh_tail != 0 && refresh_tail != 1)
     return fail(QSA_ERR_INVALID_ARG, "refresh_tail %d (0 or 1)", refresh_tail);
-  return device_status(qsa::launch_score_centroid(common(dims, kv), q, cent, refresh_tail,
-                                                  group_scores, head_scores, stride, stream),
-                       "score_pages_centroid launch");
+  qsa::LaunchCommon c = common(dims, kv);
+  Checked chk;
+  if ((s = chk.begin(c, stream)) != QSA_OK) return s;
+  return chk.end(device_status(qsa::launch_score_centroid(c, q, cent, refresh_tail, group_scores,
+                                                          head_scores, stride, stream),
+                               "score_pages_centroid launch"),
+                 stream);
 }
 
 size_t qsa_topk_workspace_size(const qsa_dims* dims, int32_t max_pages, int32_t k) {
@@ -448,11 +547,14 @@ qsa_status qsa_paged_decode(const qsa_dims* dims, const void* q, const qsa_paged
   if (ws_bytes < w.total() || (w.total() > 0 && ws == nullptr))
     return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, w.total());
   const qsa::Partials part = carve(ws, w);
-  const qsa::LaunchCommon c = common(dims, kv);
+  qsa::LaunchCommon c = common(dims, kv);
+  Checked chk;
+  if ((s = chk.begin(c, stream)) != QSA_OK) return s;
   const float scale_log2 = sm_scale * 1.4426950408889634f;
-  return device_status(qsa::launch_decode(c, q, sel, sel_count, kk, scale_log2, plan, part,
-                                          qsa::Partials{}, 0, out, lse, stream),
-                       "paged_decode launch");
+  return chk.end(device_status(qsa::launch_decode(c, q, sel, sel_count, kk, scale_log2, plan, part,
+                                                  qsa::Partials{}, 0, out, lse, stream),
+                               "paged_decode launch"),
+                 stream);
 }
 
 size_t qsa_cascade_workspace_size(const qsa_dims* dims, int32_t prefix_len,
@@ -495,14 +597,16 @@ qsa_status qsa_cascade_decode(const qsa_dims* dims, const void* q, const int32_t
   qsa::Partials pre;
   pre.o = reinterpret_cast<float*>(base + w.total());
   pre.ml = reinterpret_cast<float*>(base + w.total() + align_up(rows * dims->head_dim * sizeof(float)));
-  const qsa::LaunchCommon c = common(dims, kv);
+  qsa::LaunchCommon c = common(dims, kv);
+  Checked chk;
+  if ((s = chk.begin(c, stream)) != QSA_OK) return s;
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   hipError_t e = qsa::launch_cascade_prefix(c, q, prefix_pages, prefix_len, nsplit, scale_log2, pre,
                                             stream);
   if (e != hipSuccess) return device_status(e, "cascade prefix launch");
   e = qsa::launch_decode(c, q, sel, sel_count, kk, scale_log2, plan, part, pre, nsplit, out, lse,
                          stream);
-  return device_status(e, "cascade suffix launch");
+  return chk.end(device_status(e, "cascade suffix launch"), stream);
 }
 
 qsa_status qsa_sparse_decode_path(const qsa_dims* dims, const int32_t* seq_lens_host,
@@ -563,21 +667,25 @@ qsa_status sparse_decode_impl(const qsa_dims* dims, const void* q, const qsa_pag
   qsa_path chosen;
   if ((s = qsa_sparse_decode_path(dims, kv->seq_lens_host, stride, k, path, &chosen)) != QSA_OK)
     return s;
-  const qsa::LaunchCommon c = common(dims, kv);
+  qsa::LaunchCommon c = common(dims, kv);
   const float scale_log2 = sm_scale * 1.4426950408889634f;
+  Checked chk;
   if (chosen == QSA_PATH_FUSED) {
     // fewer rows than CUs: two workgroups per row, each attending for half
     // of the group's query heads
     const int rows = dims->num_seqs * dims->num_kv_heads;
     const int head_split = (c.G >= 2 && rows < device_cus()) ? 2 : 1;
-    return device_status(qsa::launch_sparse_row(c, q, meta, stride, refresh_tail, k, scale_log2,
-                                                 head_split, centroid, out, lse, group_scores, sel,
-                                                 sel_count, stream),
-                         "sparse_decode (fused) launch");
+    if ((s = chk.begin(c, stream)) != QSA_OK) return s;
+    return chk.end(device_status(qsa::launch_sparse_row(c, q, meta, stride, refresh_tail, k,
+                                                        scale_log2, head_split, centroid, out, lse,
+                                                        group_scores, sel, sel_count, stream),
+                                 "sparse_decode (fused) launch"),
+                   stream);
   }
   const SparseWs w = sparse_ws(dims, kv->seq_lens_host, stride, k);
   if (ws_bytes < w.total() || ws == nullptr)
     return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, w.total());
+  if ((s = chk.begin(c, stream)) != QSA_OK) return s;
   char* base = static_cast<char*>(ws);
   float* gs = reinterpret_cast<float*>(base);
   base += align_up(w.gs);
@@ -596,9 +704,10 @@ qsa_status sparse_decode_impl(const qsa_dims* dims, const void* q, const qsa_pag
   if (e != hipSuccess) return device_status(e, "sparse_decode top-K launch");
   const qsa::DecodePlan plan = make_plan(dims, kv->seq_lens_host, k);
   const qsa::Partials part = carve(base, w.dec);
-  return device_status(qsa::launch_decode(c, q, sl, cn, k, scale_log2, plan, part, qsa::Partials{},
-                                          0, out, lse, stream),
-                       "sparse_decode decode launch");
+  return chk.end(device_status(qsa::launch_decode(c, q, sl, cn, k, scale_log2, plan, part,
+                                                  qsa::Partials{}, 0, out, lse, stream),
+                               "sparse_decode decode launch"),
+                 stream);
 }
 
 }  // namespace

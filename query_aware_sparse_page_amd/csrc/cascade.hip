@@ -67,7 +67,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, int num_phys, int B, int Hkv, int G,
     const int* __restrict__ prefix_pages, int prefix_len, int split_tokens, int n_splits,
-    float scale_log2, float* __restrict__ pre_o, float* __restrict__ pre_ml) {
+    float scale_log2, float* __restrict__ pre_o, float* __restrict__ pre_ml,
+    unsigned int* __restrict__ err) {
   __shared__ CascadeShared sh;
 
   const int tid = threadIdx.x;
@@ -104,7 +105,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
     int p = -1;
     if (i < kMaxSplitPages && pgi < n_pre_pages && pgi * kPage < kend) {
       p = prefix_pages[pgi];
-      p = (p >= 0 && p < num_phys) ? p : -1;
+      if (p < 0 || p >= num_phys) {
+        if (rt == 0 && wave == 0) report_bad(err, kErrPhys);
+        p = -1;
+      }
     }
     pgr[half] = p;
   }
@@ -204,8 +208,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
         for (int kt = 0; kt < 2; ++kt) sacc[kt][qt] = mfma16(a[kt], qb[qt][ks], sacc[kt][qt]);
     }
     // ---- online softmax over this block, per query column c16 of each tile
-    // (only a split's last block can hold keys past its end)
-    const bool full = kb + kKeyBlock <= kend;
+    // (only a split's last block can hold keys past its end; a key tile on
+    // a page out of range, staged as zeros, is masked like keys past the end)
+    const int bi = (kb - kbeg) / kKeyBlock;
+    const bool bad0 = page_of(bi, 0) < 0;
+    const bool bad1 = page_of(bi, 1) < 0;
+    const bool full = kb + kKeyBlock <= kend && !bad0 && !bad1;
     uint2 pt[kQT][2];  // B operands: P^T of key tile 0 and 1 (keys 4g .. 4g+3)
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
@@ -214,12 +222,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[4 * kt + i] = sacc[kt][qt][i] * scale_log2;
-      if (!full) {  // (workgroup-uniform: only the split's last block)
+      if (!full) {  // (workgroup-uniform: the split's last block, or a page out of range)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (kb + 16 * kt + 4 * g4 + i >= kend) s[4 * kt + i] = -__builtin_inff();
+            if (kb + 16 * kt + 4 * g4 + i >= kend || (kt == 0 ? bad0 : bad1))
+              s[4 * kt + i] = -__builtin_inff();
       }
       float mx = -__builtin_inff();
 #pragma unroll
@@ -236,14 +245,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) oacc[qt][dt] *= al;
       }
-      // m_run is finite from the first block on (its first key lies inside
-      // the split, so every column has a finite logit there and the
-      // reference moves); bf16 weights, rounded to nearest even in hardware
+      // m_run is finite once a block with a key on a page in range has
+      // been seen; before that every logit is -inf and its weight must be 0
+      // (exp2(-inf - 0)), not exp2(-inf + inf). bf16 weights, rounded to
+      // nearest even in hardware.
+      const float mref = m_run[qt] == -__builtin_inff() ? 0.0f : m_run[qt];
       uint32_t pk[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bf16x2_t w = {(__bf16)fast_exp2(s[2 * e] - m_run[qt]),
-                            (__bf16)fast_exp2(s[2 * e + 1] - m_run[qt])};
+        const bf16x2_t w = {(__bf16)fast_exp2(s[2 * e] - mref),
+                            (__bf16)fast_exp2(s[2 * e + 1] - mref)};
         pk[e] = __builtin_bit_cast(uint32_t, w);
       }
       pt[qt][0] = make_uint2(pk[0], pk[1]);
@@ -333,7 +344,7 @@ hipError_t launch_cascade_prefix(const LaunchCommon& c, const void* q, const int
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(c.k_pool),
                      static_cast<const uint16_t*>(c.v_pool), c.num_phys, c.B, c.Hkv, c.G,
                      prefix_pages, prefix_len, split_tokens, n_splits, scale_log2, prefix.o,
-                     prefix.ml);
+                     prefix.ml, c.err);
   return hipGetLastError();
 }
 

@@ -63,7 +63,7 @@ decode_split_kernel(
     const int* __restrict__ page_indices, const int* __restrict__ seq_lens,
     const int* __restrict__ sel, const int* __restrict__ sel_count, int k_stride,
     float scale_log2, int chunk, int max_units, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, unsigned int* __restrict__ err) {
   using WA = WaveAttn<T, G>;
   constexpr int EPC = WA::EPC;
   constexpr int D = WA::D;
@@ -94,6 +94,8 @@ decode_split_kernel(
     count = count < n ? count : n;  // a row selects distinct pages of the sequence
     count = count > 0 ? count : 0;
   }
+  if (sel != nullptr && u == 0 && tid == 0 && (cnt_sel < 1 || cnt_sel > min(k_stride, n)))
+    report_bad(err, kErrCount);
   int units = (count + chunk - 1) / chunk;
   units = units < 1 ? 1 : (units < max_units ? units : max_units);
   if (u >= units) return;  // whole workgroup: nothing in this unit
@@ -109,7 +111,11 @@ decode_split_kernel(
       if (p >= 0 && p < num_phys) {
         my_p = p;
         my_valid = min(kPage, L - kPage * j);
+      } else {
+        report_bad(err, kErrPhys);
       }
+    } else {
+      report_bad(err, kErrSel);
     }
   }
 
@@ -200,6 +206,7 @@ struct StreamSrc {
   const int* page_indices;
   const int* sel;
   const int* sel_count;
+  unsigned int* err;
   int Hkv, G, k, num_phys, lane;
   long long e_next, e_end;  // next entry to fetch; end of the share
   int fb, fh, fj;           // (b, h, j) of entry e_next
@@ -279,12 +286,16 @@ struct StreamSrc {
       } else {
         // two dependent levels: the list entry (j < c_b <= k), then its
         // table entry; entries past the row's count attend nothing
-        const int act = min(min(sel_count[row], k), np);
+        const int cnt = sel_count[row];
+        const int act = min(min(cnt, k), np);
         const int jl = sel[(size_t)row * k + j];
         if (j < act && jl >= 0 && jl < np) {
           n_j = jl;
           n_raw = page_indices[t->base[b] + jl];
+        } else if (j < act) {
+          report_bad(err, kErrSel);
         }
+        if (j == 0 && (cnt < 1 || cnt > min(k, np))) report_bad(err, kErrCount);
       }
     }
   }
@@ -298,6 +309,7 @@ struct StreamSrc {
     const int L = t->len[b];
     const int jl = n_j;
     const bool ok = lane < c_n && jl >= 0 && n_raw >= 0 && n_raw < num_phys;
+    if (lane < c_n && jl >= 0 && !ok) report_bad(err, kErrPhys);
     c_p = ok ? n_raw * Hkv + h : 0;
     c_v = ok ? min(kPage, L - kPage * jl) : 0;
     c_r = n_r;
@@ -365,7 +377,7 @@ decode_stream_kernel(
     const int* __restrict__ page_indices, const int* __restrict__ seq_lens,
     const int* __restrict__ sel, const int* __restrict__ sel_count, int k, float scale_log2,
     int nwaves, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int* __restrict__ row_slots) {
+    int* __restrict__ row_slots, unsigned int* __restrict__ err) {
   using WA = WaveAttnMfma<G>;
   __shared__ StreamTables tab;
   __shared__ alignas(16) char vl[4][WA::kLdsBytes];
@@ -437,6 +449,7 @@ decode_stream_kernel(
   src.page_indices = page_indices;
   src.sel = sel;
   src.sel_count = sel_count;
+  src.err = err;
   src.Hkv = Hkv;
   src.G = G;
   src.k = k;
@@ -584,7 +597,8 @@ hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
   case GG:                                                                                       \
     hipLaunchKernelGGL((decode_stream_kernel<GG>), dim3(plan.waves / 4), dim3(256), 0, stream, qq, \
                        kb, vb, c.num_phys, c.B, c.Hkv, c.page_indptr, c.page_indices, c.seq_lens,  \
-                       sel, sel_count, k, scale_log2, plan.waves, part.o, part.ml, part.row_slots); \
+                       sel, sel_count, k, scale_log2, plan.waves, part.o, part.ml, part.row_slots, \
+                       c.err);                                                                    \
     break;
       switch (c.G) {
         QSA_STREAM_CASE(4)
@@ -602,7 +616,8 @@ hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
   case GG:                                                                                      \
     hipLaunchKernelGGL((decode_split_kernel<T, GG>), grid, dim3(256), 0, stream, qq, kk, vv,    \
                        c.num_phys, c.Hkv, c.page_indptr, c.page_indices, c.seq_lens, sel,       \
-                       sel_count, k, scale_log2, plan.chunk, plan.max_units, part.o, part.ml); \
+                       sel_count, k, scale_log2, plan.chunk, plan.max_units, part.o, part.ml,  \
+                       c.err);                                                                 \
     break;
   switch (c.G) {
     QSA_DECODE_CASE(1)

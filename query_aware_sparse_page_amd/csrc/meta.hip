@@ -22,7 +22,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) build_meta_kernel(
     const T* __restrict__ k_pool, int num_phys, int Hkv, const int* __restrict__ page_indptr,
     const int* __restrict__ page_indices, const int* __restrict__ seq_lens, int tail_pages,
-    T* __restrict__ meta, int stride) {
+    T* __restrict__ meta, int stride, unsigned int* __restrict__ err) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int b = blockIdx.y;
@@ -35,7 +35,10 @@ __global__ void __launch_bounds__(256) build_meta_kernel(
   const int h = tile - (tile / Hkv) * Hkv;
   if (j >= n) return;
   const int p = page_indices[page_indptr[b] + j];
-  if (p < 0 || p >= num_phys) return;
+  if (p < 0 || p >= num_phys) {
+    report_bad(err, kErrPhys);
+    return;
+  }
   const int valid = min(kPage, L - kPage * j);
   const int chunk = lane & 15;
   const char* src = reinterpret_cast<const char*>(k_pool) + ((size_t)p * Hkv + h) * kTileBytes;
@@ -58,7 +61,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) build_centroid_kernel(
     const T* __restrict__ k_pool, int num_phys, int Hkv, const int* __restrict__ page_indptr,
     const int* __restrict__ page_indices, const int* __restrict__ seq_lens, int tail_pages,
-    T* __restrict__ cent, int stride) {
+    T* __restrict__ cent, int stride, unsigned int* __restrict__ err) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int b = blockIdx.y;
@@ -71,7 +74,10 @@ __global__ void __launch_bounds__(256) build_centroid_kernel(
   const int h = tile - (tile / Hkv) * Hkv;
   if (j >= n) return;
   const int p = page_indices[page_indptr[b] + j];
-  if (p < 0 || p >= num_phys) return;
+  if (p < 0 || p >= num_phys) {
+    report_bad(err, kErrPhys);
+    return;
+  }
   const int valid = min(kPage, L - kPage * j);
   const char* src = reinterpret_cast<const char*>(k_pool) + ((size_t)p * Hkv + h) * kTileBytes;
   const uint4 mean = tile_mean<T>(src, valid, lane);
@@ -90,11 +96,11 @@ hipError_t launch_build_centroids(const LaunchCommon& c, int max_pages, int tail
   if (c.bf16) {
     hipLaunchKernelGGL(build_centroid_kernel<bf16s>, grid, dim3(256), 0, stream,
                        static_cast<const bf16s*>(c.k_pool), c.num_phys, c.Hkv, c.page_indptr,
-                       c.page_indices, c.seq_lens, tail_pages, static_cast<bf16s*>(cent), stride);
+                       c.page_indices, c.seq_lens, tail_pages, static_cast<bf16s*>(cent), stride, c.err);
   } else {
     hipLaunchKernelGGL(build_centroid_kernel<float>, grid, dim3(256), 0, stream,
                        static_cast<const float*>(c.k_pool), c.num_phys, c.Hkv, c.page_indptr,
-                       c.page_indices, c.seq_lens, tail_pages, static_cast<float*>(cent), stride);
+                       c.page_indices, c.seq_lens, tail_pages, static_cast<float*>(cent), stride, c.err);
   }
   return hipGetLastError();
 }
@@ -106,11 +112,11 @@ hipError_t launch_build_meta(const LaunchCommon& c, int max_pages, int tail_page
   if (c.bf16) {
     hipLaunchKernelGGL(build_meta_kernel<bf16s>, grid, dim3(256), 0, stream,
                        static_cast<const bf16s*>(c.k_pool), c.num_phys, c.Hkv, c.page_indptr,
-                       c.page_indices, c.seq_lens, tail_pages, static_cast<bf16s*>(meta), stride);
+                       c.page_indices, c.seq_lens, tail_pages, static_cast<bf16s*>(meta), stride, c.err);
   } else {
     hipLaunchKernelGGL(build_meta_kernel<float>, grid, dim3(256), 0, stream,
                        static_cast<const float*>(c.k_pool), c.num_phys, c.Hkv, c.page_indptr,
-                       c.page_indices, c.seq_lens, tail_pages, static_cast<float*>(meta), stride);
+                       c.page_indices, c.seq_lens, tail_pages, static_cast<float*>(meta), stride, c.err);
   }
   return hipGetLastError();
 }

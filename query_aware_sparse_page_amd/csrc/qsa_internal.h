@@ -17,7 +17,22 @@ struct LaunchCommon {
   const int* page_indptr = nullptr;
   const int* page_indices = nullptr;
   const int* seq_lens = nullptr;
+  // Device error word (checked mode) or NULL: kernels that skip a page
+  // because a table or selection entry is out of range OR one of the
+  // kErr* bits into it (see report_bad below).
+  unsigned int* err = nullptr;
 };
+
+// Bits of the device error word.
+constexpr unsigned int kErrPhys = 1u;   // a physical page id outside [0, num_phys_pages)
+constexpr unsigned int kErrSel = 2u;    // a selected logical page outside [0, n_b)
+constexpr unsigned int kErrCount = 4u;  // a sel_count entry outside [1, k]
+
+// Records a skipped out-of-range entry in the error word (one lane per call
+// site is enough; every lane may call it). A vector atomic to global memory.
+__device__ __forceinline__ void report_bad(unsigned int* err, unsigned int bit) {
+  if (err != nullptr) __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Split-K decode work split: `chunk` pages per work unit (a multiple of 4,
 // one quarter per wave), `max_units` units for the longest (b, h) row.

@@ -35,7 +35,8 @@ __global__ void __launch_bounds__(256) score_kernel(
     const T* __restrict__ q, T* __restrict__ meta, int Hkv, const int* __restrict__ seq_lens,
     const int* __restrict__ page_indptr, const int* __restrict__ page_indices,
     const T* __restrict__ k_pool, int num_phys, int refresh_tail,
-    float* __restrict__ group_scores, float* __restrict__ head_scores, int stride) {
+    float* __restrict__ group_scores, float* __restrict__ head_scores, int stride,
+    unsigned int* __restrict__ err) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.y;
@@ -82,6 +83,7 @@ __global__ void __launch_bounds__(256) score_kernel(
     const int off = jt - base_j;
     if (off >= 0 && off < kScorePagesPerBlock && ((off & 15) >> 2) == wave) {
       const int p = page_indices[page_indptr[b] + jt];
+      if (p < 0 || p >= num_phys) report_bad(err, kErrPhys);  // the stored record is scored
       if (p >= 0 && p < num_phys) {
         const int valid = min(kPage, L - kPage * jt);
         const char* src = reinterpret_cast<const char*>(k_pool) + ((size_t)p * Hkv + h) * kTileBytes;
@@ -145,7 +147,7 @@ hipError_t launch_score_t(const LaunchCommon& c, const void* q, void* meta, int 
   case GG:                                                                                       \
     hipLaunchKernelGGL((score_kernel<T, GG, kCentroid>), grid, dim3(256), 0, stream, qq, mm,    \
                        c.Hkv, c.seq_lens, c.page_indptr, c.page_indices, kp, c.num_phys,        \
-                       refresh_tail, gs, hs, stride);                                            \
+                       refresh_tail, gs, hs, stride, c.err);                                     \
     break;
   switch (c.G) {
     QSA_SCORE_CASE(1)

@@ -84,7 +84,7 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     const int* __restrict__ page_indptr, const int* __restrict__ page_indices,
     const int* __restrict__ seq_lens, int refresh_tail, int k, float scale_log2,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ group_scores,
-    int* __restrict__ sel, int* __restrict__ sel_count) {
+    int* __restrict__ sel, int* __restrict__ sel_count, unsigned int* __restrict__ err) {
   constexpr int GW = G / S;  // query heads attended by this workgroup
   using WA = typename RowShared<T, GW>::WA;
   constexpr int EPC = WA::EPC;
@@ -186,6 +186,7 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   if (refresh_tail && n > 0) {
     tail_p = page_indices[tbase + jt];
     tail_ok = tail_p >= 0 && tail_p < num_phys;  // else the stored record is scored unchanged
+    if (!tail_ok && tid == 0) report_bad(err, kErrPhys);
   }
   auto score_page = [&](const uint4& m, const uint4& M) -> float {
     float gmax = -__builtin_inff();
@@ -378,7 +379,9 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
         if (pos < (uint32_t)keff) {
           const int pp = sh.u.s.phys[j];
           sh.list[pos] = j;
-          sh.plist[pos] = (pp >= 0 && pp < num_phys) ? pp : -1;
+          const bool pok = pp >= 0 && pp < num_phys;
+          sh.plist[pos] = pok ? pp : -1;
+          if (!pok && part == 0) report_bad(err, kErrPhys);
           if (sel != nullptr) sel[row * k + pos] = j;
         }
       }
@@ -459,7 +462,7 @@ void launch_row(const LaunchCommon& c, const void* q, void* meta, int stride, in
                      static_cast<const T*>(q), static_cast<T*>(meta), stride,
                      static_cast<const T*>(c.k_pool), static_cast<const T*>(c.v_pool), c.num_phys,
                      c.Hkv, rows, c.page_indptr, c.page_indices, c.seq_lens, refresh_tail, k,
-                     scale_log2, out, lse, group_scores, sel, sel_count);
+                     scale_log2, out, lse, group_scores, sel, sel_count, c.err);
 }
 
 template <typename T, bool kCen>

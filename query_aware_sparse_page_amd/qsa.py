@@ -69,6 +69,8 @@ def lib():
             "qsa_cascade_workspace_size": (sz, [D, i32, _i32p, i32]),
             "qsa_decode_plan": (i32, [D, _i32p, i32, _i32p, _i32p, _i32p]),
             "qsa_budget_pages": (i32, [i32, i32]),
+            "qsa_set_checked": (None, [i32]),
+            "qsa_get_checked": (i32, []),
             "qsa_status_string": (ctypes.c_char_p, [i32]),
             "qsa_last_error": (ctypes.c_char_p, []),
             "qsa_version": (i32, []),
@@ -353,6 +355,16 @@ def sparse_decode(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, k: int, sm_s
               _ptr(sel_count), PATHS[path], _ptr(workspace),
               0 if workspace is None else workspace.numel(), _stream()))
     return o, lse
+
+
+def set_checked(on: bool) -> None:
+    """Checked mode (qsa_set_checked): calls report skipped out-of-range page
+    ids, selections and counts as QSA_ERR_DEVICE, and wait for their stream."""
+    lib().qsa_set_checked(1 if on else 0)
+
+
+def get_checked() -> bool:
+    return bool(lib().qsa_get_checked())
 
 
 def budget_pages(budget_tokens: int, page_size: int = 16) -> int:

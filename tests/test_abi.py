@@ -244,3 +244,35 @@ def test_centroid_validation(L):
     assert st == qsa.QSA_ERR_INVALID_ARG and b"refresh_tail" in L.qsa_last_error()
     st = L.qsa_score_pages_centroid(ctypes.byref(_dims(D=96)), 1, ctypes.byref(kv), 1, 1, None, 8, 0, None)
     assert st == qsa.QSA_ERR_UNSUPPORTED
+
+
+def test_checked_mode_switch_is_host_only(L):
+    # QSA_CHECKED is read once; the setter overrides it either way
+    was = L.qsa_get_checked()
+    try:
+        L.qsa_set_checked(1)
+        assert L.qsa_get_checked() == 1
+        assert qsa.get_checked() is True
+        L.qsa_set_checked(0)
+        assert L.qsa_get_checked() == 0
+        L.qsa_set_checked(7)            # any nonzero value turns it on
+        assert L.qsa_get_checked() == 1
+        # argument errors still return before any device work in checked mode
+        st = L.qsa_paged_decode(None, None, None, None, None, 0, ctypes.c_float(1.0), None, None, None, 0,
+                                None)
+        assert st == qsa.QSA_ERR_INVALID_ARG
+    finally:
+        L.qsa_set_checked(was)
+
+
+def test_checked_mode_from_environment():
+    # a fresh process reads QSA_CHECKED at its first query
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); from query_aware_sparse_page_amd import qsa; "
+            "print(int(qsa.get_checked()))" % ROOT)
+    for val, want in (("1", "1"), ("0", "0"), ("", "0"), ("yes", "1")):
+        env = dict(os.environ, QSA_CHECKED=val)
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+        assert r.returncode == 0, r.stderr
+        assert r.stdout.strip().splitlines()[-1] == want, (val, r.stdout)

@@ -24,6 +24,7 @@ import dataclasses
 import math
 from typing import List, Optional
 
+import numpy as np
 import torch
 
 PAGE_SIZE = 16
@@ -81,6 +82,26 @@ def n_pages(L: int) -> int:
 def _cast(x: torch.Tensor, dtype: str) -> torch.Tensor:
     # fp32 draws cast with round-to-nearest-even (torch's conversion).
     return x.to(_DT[dtype])
+
+
+def _ar1_walk(mu0: torch.Tensor, eps: torch.Tensor, rho: float, sigma: float) -> torch.Tensor:
+    """mu[0] = mu0, mu[j] = rho * mu[j-1] + sigma * eps[j] (j >= 1), element-wise
+    over the trailing dimensions, in fp32 with each product and the sum
+    rounded separately (the rounding of two scalar multiplies and an add,
+    wherever they run). The walk is sequential in j, so it runs on the host
+    over whole [B, Hkv, D] slices: one copy of the draws instead of one
+    device launch per step."""
+    e = eps.detach().to("cpu", torch.float32).numpy()
+    out = np.empty(e.shape, dtype=np.float32)
+    out[0] = mu0.detach().to("cpu", torch.float32).numpy()
+    r = np.float32(rho)
+    s = np.float32(sigma)
+    tmp = np.empty(e.shape[1:], dtype=np.float32)
+    for j in range(1, e.shape[0]):
+        np.multiply(out[j - 1], r, out=out[j])
+        np.multiply(e[j], s, out=tmp)
+        np.add(out[j], tmp, out=out[j])
+    return torch.from_numpy(out)
 
 
 def _fill_nan_tails(pool: torch.Tensor, phys_last: torch.Tensor, valid_last: torch.Tensor) -> None:
@@ -165,12 +186,10 @@ def build_case(
     if drift is not None:
         rho, sigma = drift
         maxn = max(nps)
-        mu = torch.empty(maxn, B, Hkv, D, device=device, dtype=torch.float32)
-        mu[0] = torch.randn(B, Hkv, D, generator=g, device=device) * (sigma / math.sqrt(1.0 - rho * rho))
+        mu0 = torch.randn(B, Hkv, D, generator=g, device=device) * (sigma / math.sqrt(1.0 - rho * rho))
         eps = torch.randn(maxn, B, Hkv, D, generator=g, device=device)
-        for j in range(1, maxn):
-            mu[j] = rho * mu[j - 1] + sigma * eps[j]
-        del eps
+        mu = _ar1_walk(mu0, eps, rho, sigma).to(device)
+        del eps, mu0
         for b in range(B):
             s0 = int(indptr[b])
             phys = page_indices[s0:s0 + nps[b]].to(torch.int64)
