@@ -27,7 +27,9 @@
 // 16-key tile. O^T += V^T . P^T takes the block's 32 keys in one product with
 // its k-slots 8g .. 8g+7 holding keys 4g .. 4g+3 of tile 0 and then of tile 1
 // (any order works as long as A and B agree): the B operand is the lane's own
-// eight weights, and the A operand two transposing reads, one per tile.
+// eight weights, and the A operand two transposing reads, one per tile. The
+// weights enter as bf16 high and low parts, one product each, so the output
+// carries no bf16 rounding of them.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -172,18 +174,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
   for (int qt = 0; qt < kQT; ++qt)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[qt][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  // The softmax denominators come from the matrix cores as well: a product
-  // of P^T with an A operand whose row 0 is all ones leaves row 0 of
-  // lacc (lanes 0..15, element 0) holding the sum of the bf16 weights of
-  // query c16, the same weights the O^T products use, accumulated in fp32.
-  const uint4 ones_a = c16 == 0 ? make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u)
-                                 : make_uint4(0u, 0u, 0u, 0u);
-  f32x4_t lacc[kQT];
+  // Softmax state per query column: the reference max, and this lane's
+  // share of the sum of the fp32 weights (its keys 4 g4 .. +3 of each
+  // tile; the four lane groups are added at the end).
+  float l_run[kQT];
   float m_run[kQT];
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
     m_run[qt] = -__builtin_inff();
-    lacc[qt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    l_run[qt] = 0.0f;
   }
 
   // Attention over the block staged in LDS buffer buf (keys from kb).
@@ -214,7 +213,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
     const bool bad0 = page_of(bi, 0) < 0;
     const bool bad1 = page_of(bi, 1) < 0;
     const bool full = kb + kKeyBlock <= kend && !bad0 && !bad1;
-    uint2 pt[kQT][2];  // B operands: P^T of key tile 0 and 1 (keys 4g .. 4g+3)
+    uint4 phi[kQT], plo[kQT];  // B operands: P^T (keys 4g .. 4g+3 of tile 0, then of tile 1), hi and lo
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
       float s[8];
@@ -241,25 +240,31 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
         const float mn = fmaxf(m_run[qt], mx);
         const float al = (mn == -__builtin_inff()) ? 1.0f : fast_exp2(m_run[qt] - mn);
         m_run[qt] = mn;
-        lacc[qt] *= al;
+        l_run[qt] *= al;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) oacc[qt][dt] *= al;
       }
       // m_run is finite once a block with a key on a page in range has
       // been seen; before that every logit is -inf and its weight must be 0
-      // (exp2(-inf - 0)), not exp2(-inf + inf). bf16 weights, rounded to
-      // nearest even in hardware.
+      // (exp2(-inf - 0)), not exp2(-inf + inf). The fp32 weights go into the
+      // sum; the products take them as bf16 high and low parts (p = hi + lo
+      // to about 2^-17; the conversions round to nearest even in hardware),
+      // so the output carries no bf16 rounding of the weights.
       const float mref = m_run[qt] == -__builtin_inff() ? 0.0f : m_run[qt];
-      uint32_t pk[4];
+      uint32_t hi[4], lo[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bf16x2_t w = {(__bf16)fast_exp2(s[2 * e] - mref),
-                            (__bf16)fast_exp2(s[2 * e + 1] - mref)};
-        pk[e] = __builtin_bit_cast(uint32_t, w);
+        const float w0 = fast_exp2(s[2 * e] - mref);
+        const float w1 = fast_exp2(s[2 * e + 1] - mref);
+        l_run[qt] += w0 + w1;
+        const bf16x2_t wh = {(__bf16)w0, (__bf16)w1};
+        hi[e] = __builtin_bit_cast(uint32_t, wh);
+        const bf16x2_t wl = {(__bf16)(w0 - __uint_as_float(hi[e] << 16)),
+                             (__bf16)(w1 - __uint_as_float(hi[e] & 0xFFFF0000u))};
+        lo[e] = __builtin_bit_cast(uint32_t, wl);
       }
-      pt[qt][0] = make_uint2(pk[0], pk[1]);
-      pt[qt][1] = make_uint2(pk[2], pk[3]);
-      lacc[qt] = mfma16(ones_a, make_uint4(pt[qt][0].x, pt[qt][0].y, pt[qt][1].x, pt[qt][1].y), lacc[qt]);
+      phi[qt] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      plo[qt] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
     // ---- O^T += V^T . P^T, one product per 16 dims over the block's 32
     // keys: A rows = dims 16 dt + c16, keys 4 g4 .. +3 of tile 0 then of
@@ -275,8 +280,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
             (__attribute__((address_space(3))) lds_v4i16*)(vsrc + 16 * kt * kVPitch + 16 * dt)));
       const uint4 a8 = make_uint4(a[0].x, a[0].y, a[1].x, a[1].y);
 #pragma unroll
-      for (int qt = 0; qt < kQT; ++qt)
-        oacc[qt][dt] = mfma16(a8, make_uint4(pt[qt][0].x, pt[qt][0].y, pt[qt][1].x, pt[qt][1].y), oacc[qt][dt]);
+      for (int qt = 0; qt < kQT; ++qt) {
+        oacc[qt][dt] = mfma16(a8, phi[qt], oacc[qt][dt]);
+        oacc[qt][dt] = mfma16(a8, plo[qt], oacc[qt][dt]);
+      }
     }
   };
 
@@ -311,7 +318,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5
   // ---- partial (o relative to m_run, m_run, l) per query row
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
-    const float l = lacc[qt][0];  // meaningful in lanes 0..15 (g4 == 0), which store it
+    float l = l_run[qt];
+    l += xshfl(l, 16);
+    l += xshfl(l, 32);  // the column's sum in every lane group (lanes 0..15 store it)
     const int r = row0 + qt * 16 + c16;
     if (r < R) {
       const size_t pr = ((size_t)h * n_splits + split) * (size_t)R + r;

@@ -24,3 +24,20 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    out = os.environ.get("QSA_MARGINS_OUT")
+    if not out:
+        return
+    try:
+        from tests import gpu_helpers
+    except Exception:  # pragma: no cover
+        return
+    import json
+    rows = {k: {"max_abs_d_out": v[0], "max_abs_d_lse": v[1], "comparisons": v[2]}
+            for k, v in sorted(gpu_helpers.MARGINS.items())}
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    with open(out, "w") as f:
+        json.dump({"tolerance": gpu_helpers.OUT_TOL, "margins": rows, "recall": gpu_helpers.RECALL}, f,
+                  indent=1)

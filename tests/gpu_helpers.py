@@ -44,12 +44,35 @@ def meta_bits(meta: torch.Tensor) -> np.ndarray:
     return np_store(meta)
 
 
-def assert_close_out(out_gpu, lse_gpu, out_ora, lse_ora, tol=OUT_TOL):
+# Largest |delta| seen per label over the session: label -> [max |dO|,
+# max |dLSE|, comparisons]. conftest.py writes it out when QSA_MARGINS_OUT
+# names a file, so the headroom to OUT_TOL of each path is on record.
+MARGINS = {}
+# Recall of the library's selections per label (tests/test_gpu_recall.py),
+# written out with the margins.
+RECALL = {}
+
+
+def record_margin(label, d_o, d_l):
+    m = MARGINS.setdefault(label, [0.0, 0.0, 0])
+    m[0] = max(m[0], float(d_o))
+    m[1] = max(m[1], float(d_l))
+    m[2] += 1
+
+
+def assert_close_out(out_gpu, lse_gpu, out_ora, lse_ora, tol=OUT_TOL, label=None):
     og = np.asarray(out_gpu, dtype=np.float64)
     lg = np.asarray(lse_gpu, dtype=np.float64)
     assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
     d_o = np.max(np.abs(og - out_ora)) if og.size else 0.0
     d_l = np.max(np.abs(lg - lse_ora)) if lg.size else 0.0
+    if label is not None:
+        record_margin(label, d_o, d_l)
     assert d_o <= tol, f"max |out delta| = {d_o:.3e}"
     assert d_l <= tol, f"max |lse delta| = {d_l:.3e}"
     return d_o, d_l
+
+
+def selection_rows(sel, cnt):
+    """GPU selection tensors -> (sel [B, Hkv, k] int32, counts) for the oracle."""
+    return sel.cpu().numpy().astype(np.int32), cnt.cpu().numpy().astype(np.int32)

@@ -93,14 +93,22 @@ def test_centroids_scores_selection_and_decode(label, lens, Hq, Hkv, dtype, k):
     oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], dtype, d["page_indptr"], d["page_indices"],
                             d["seq_lens"], c.sm_scale, sel=osel, sel_count=ocnt)
     o_n, l_n = out.cpu().numpy(), lse.cpu().numpy()
+    same = True
     for b, L in enumerate(d["seq_lens"]):
         n = O.num_pages(L)
         table = d["page_indices"][d["page_indptr"][b]:d["page_indptr"][b + 1]]
         for h in range(Hkv):
             got, want = check_selection_row(sel_n[b, h], cnt_n[b, h], phys_n[b, h], ogroup[b, h], n, k, table)
-            if set(got) == set(want):
-                hs_ = slice(h * G, (h + 1) * G)
-                assert_close_out(o_n[b, hs_], l_n[b, hs_], oo[b, hs_], ol[b, hs_])
+            same &= set(got) == set(want)
+    if not same:
+        # a swap inside the threshold band: the oracle attends over the
+        # GPU's own (valid) selection
+        oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], dtype, d["page_indptr"], d["page_indices"],
+                                d["seq_lens"], c.sm_scale, sel=sel_n, sel_count=cnt_n)
+    for b in range(c.B):
+        for h in range(Hkv):
+            hs_ = slice(h * G, (h + 1) * G)
+            assert_close_out(o_n[b, hs_], l_n[b, hs_], oo[b, hs_], ol[b, hs_], label="small/split/centroid")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -177,11 +185,19 @@ def test_centroid_sparse_decode_fused_and_split(label, lens, Hq, Hkv, dtype, k):
                             d["seq_lens"], c.sm_scale, sel=osel, sel_count=ocnt)
     sel_n, cnt_n, o_n, l_n = sf.cpu().numpy(), nf.cpu().numpy(), of.cpu().numpy(), lf.cpu().numpy()
     G = Hq // Hkv
+    same = True
     for b, L in enumerate(d["seq_lens"]):
         n = O.num_pages(L)
         table = d["page_indices"][d["page_indptr"][b]:d["page_indptr"][b + 1]]
         for h in range(Hkv):
             got, want = check_selection_row(sel_n[b, h], cnt_n[b, h], None, ogroup[b, h], n, k, table)
-            if set(got) == set(want):
-                hs_ = slice(h * G, (h + 1) * G)
-                assert_close_out(o_n[b, hs_], l_n[b, hs_], oo[b, hs_], ol[b, hs_])
+            same &= set(got) == set(want)
+    if not same:
+        # a swap inside the threshold band: the oracle attends over the
+        # GPU's own (valid) selection
+        oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], dtype, d["page_indptr"], d["page_indices"],
+                                d["seq_lens"], c.sm_scale, sel=sel_n, sel_count=cnt_n)
+    for b in range(c.B):
+        for h in range(Hkv):
+            hs_ = slice(h * G, (h + 1) * G)
+            assert_close_out(o_n[b, hs_], l_n[b, hs_], oo[b, hs_], ol[b, hs_], label="small/fused/centroid")

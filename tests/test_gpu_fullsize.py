@@ -92,7 +92,7 @@ def check_sparse_rows(case, kv, seqs, heads_check=None):
                             d["seq_lens"], case.sm_scale, sel=osel, sel_count=ocnt)
     o_n, l_n = out2.cpu().numpy(), lse2.cpu().numpy()
     for si, b in enumerate(seqs):
-        assert_close_out(o_n[b], l_n[b], oo[si], ol[si])
+        assert_close_out(o_n[b], l_n[b], oo[si], ol[si], label=f"{case.name}/split-calls/bound")
     assert np.all(np.isfinite(out.cpu().numpy()))
 
 
@@ -103,11 +103,144 @@ def test_c2_sparse_full_size_sampled():
     check_sparse_rows(case, kv, [0, 9, 15])
 
 
-def test_c4_long_full_size_sampled():
-    print("[case] c4 long full size: B=8 GQA 32/8 131072 tokens K=128", flush=True)
+def subcase_head(case, b, h):
+    """Oracle inputs for KV head h of sequence b alone: the sequence's pages
+    gathered to a compact host pool that keeps only head h, and the group's
+    query heads (input marshalling only; the oracle then runs with Hkv = 1)."""
+    indptr = case.page_indptr.cpu().numpy()
+    phys = case.page_indices.cpu().numpy()[indptr[b]:indptr[b + 1]].astype(np.int64)
+    idx = torch.from_numpy(phys).to(case.k_pool.device)
+    G = case.group
+    return dict(
+        q=np_store(case.q[b:b + 1, h * G:(h + 1) * G]),
+        k_pool=np_store(case.k_pool[idx, h:h + 1]), v_pool=np_store(case.v_pool[idx, h:h + 1]),
+        page_indptr=np.array([0, len(phys)], dtype=np.int32), page_indices=np.arange(len(phys), dtype=np.int32),
+        seq_lens=case.seq_lens.cpu().numpy()[b:b + 1].astype(np.int32), dtype=case.dtype,
+    )
+
+
+def _stale_tails(meta, lens):
+    """A copy of the metadata whose tail-page records hold a wrong value, so
+    that only a refresh inside the step can restore them."""
+    m = meta.clone()
+    for b, L in enumerate(lens):
+        m[b, :, -(-L // 16) - 1] = 3.0
+    return m
+
+
+def _oracle_row(case, d, scorer, k):
+    """Oracle metadata (or centroids), group scores and selection of a
+    one-KV-head subcase."""
+    dt = case.dtype
+    args = (d["page_indptr"], d["page_indices"], d["seq_lens"])
+    if scorer == "bound":
+        rec = O.build_page_meta(d["k_pool"], dt, *args)
+        head, group = O.score_pages(d["q"], dt, rec, dt, *args, 1)
+    else:
+        rec = O.build_page_centroids(d["k_pool"], dt, *args)
+        head, group = O.centroid_scores(d["q"], dt, rec, dt, *args, 1)
+    osel, ocnt = O.topk_pages(group, d["seq_lens"], k)
+    return rec, head, group, osel, ocnt
+
+
+def _check_step_row(case, scorer, path, b, h, meta_after, gs, sel, cnt, out, lse, check_out=True):
+    """One (sequence, KV head) row of a one-call sparse step against the
+    oracle: records bit-exact (the tail page's rebuilt by the step), every
+    page's group score within the fp32 accumulation bound, the selection
+    within the threshold band, and the attention output on the GPU's own
+    selection within the output tolerance."""
+    d = subcase_head(case, b, h)
+    k = case.k_pages
+    rec, head, group, osel, ocnt = _oracle_row(case, d, scorer, k)
+    n = O.num_pages(int(d["seq_lens"][0]))
+    got = np_store(meta_after[b, h])                      # [stride, 2, D] or [stride, D]
+    for j in range(n):
+        assert np.array_equal(got[j].view(np.uint8), rec[j, 0].view(np.uint8)), (b, h, j)
+    qv = O.values_f64(d["q"], case.dtype)[0]
+    rv = O.values_f64(rec, case.dtype)
+    gs_n = gs[b, h].cpu().numpy()
+    D = qv.shape[-1]
+    for j in range(n):
+        if scorer == "bound":
+            tol = max(score_tol(qv[i], rv[j, 0, 0], rv[j, 0, 1]) for i in range(case.group))
+        else:
+            tol = max((D + 2) * 2.0 ** -24 * float(np.sum(np.abs(qv[i]) * np.abs(rv[j, 0])))
+                      for i in range(case.group)) + 1e-30
+        assert abs(float(gs_n[j]) - float(group[0, 0, j])) <= tol, (b, h, j)
+    table = case.page_indices.cpu().numpy()[case.page_indptr[b].item():case.page_indptr[b + 1].item()]
+    got_sel, ref_sel = check_selection_row(sel[b, h].cpu().numpy(), cnt[b, h].cpu().numpy(), None,
+                                           group[0, 0], n, k, table)
+    exact = set(got_sel) == set(int(x) for x in ref_sel)
+    if not (check_out or not exact):
+        return exact
+    s1 = np.full((1, 1, k), -1, dtype=np.int32)
+    s1[0, 0, :len(got_sel)] = got_sel
+    c1 = np.array([[len(got_sel)]], dtype=np.int32)
+    oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], case.dtype, d["page_indptr"], d["page_indices"],
+                            d["seq_lens"], case.sm_scale, sel=s1, sel_count=c1)
+    G = case.group
+    assert_close_out(out[b, h * G:(h + 1) * G].cpu().numpy(), lse[b, h * G:(h + 1) * G].cpu().numpy(),
+                     oo[0], ol[0], label=f"{case.name}/{path}/{scorer}")
+    return exact
+
+
+def _one_call_step(case, kv, scorer, path):
+    """The benchmarked launch: one qsa_sparse_decode call (tail refresh,
+    scores, top-K, attention, merge) on stale tail records; returns its
+    outputs, and checks that the call without the optional outputs gives
+    the same bits."""
+    lens = case.seq_lens_list()
+    build = qsa.build_page_centroids if scorer == "centroid" else qsa.build_page_meta
+    meta0 = _stale_tails(build(kv), lens)
+    B, Hkv, k = case.B, case.Hkv, case.k_pages
+    stride = int(meta0.shape[2])
+    gs = torch.empty(B, Hkv, stride, dtype=torch.float32, device=DEV)
+    sel = torch.empty(B, Hkv, k, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(B, Hkv, dtype=torch.int32, device=DEV)
+    meta = meta0.clone()
+    out, lse = qsa.sparse_decode(case.q, kv, meta, k, sm_scale=case.sm_scale, refresh_tail=True, path=path,
+                                 group_scores=gs, sel=sel, sel_count=cnt, scorer=scorer)
+    o2, l2 = qsa.sparse_decode(case.q, kv, meta0.clone(), k, sm_scale=case.sm_scale, refresh_tail=True,
+                               path=path, scorer=scorer)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+    assert np.all(np.isfinite(out.cpu().numpy()))
+    return meta, gs, sel, cnt, out, lse
+
+
+@pytest.mark.parametrize("scorer", ["bound", "centroid"])
+def test_c2_fused_full_size(scorer):
+    """The headline launch at its benchmarked shape: 128 (sequence, KV head)
+    rows of 512 pages, top-153, two workgroups per row."""
+    print(f"[case] c2 sparse full size, fused one-call step, scorer={scorer}", flush=True)
+    case = workloads.c2_sparse(device=DEV, n_sentinel=64)
+    kv = qsa.PagedKV.from_case(case)
+    assert qsa.sparse_decode_path(kv, case.Hq, 512, case.k_pages) == "fused"
+    meta, gs, sel, cnt, out, lse = _one_call_step(case, kv, scorer, "fused")
+    same = 0
+    rows = [(b, h) for b in range(case.B) for h in range(case.Hkv)]
+    # every row's scores and selection; outputs of a spread of rows
+    for i, (b, h) in enumerate(rows):
+        # outputs: every third row, and every row whose page set differs
+        # from the oracle's inside the threshold band
+        same += _check_step_row(case, scorer, "fused", b, h, meta, gs, sel, cnt, out, lse,
+                                check_out=(i % 3 == 0))
+    print(f"[c2 fused {scorer}] rows with the oracle's exact page set: {same}/{len(rows)}", flush=True)
+
+
+def test_c4_long_full_size_every_sequence():
+    """The long-context step as benchmarked (one qsa_sparse_decode call; the
+    library takes the split path for 8192-page rows), every sequence checked
+    on two of its KV heads."""
+    print("[case] c4 long full size: B=8 GQA 32/8 131072 tokens K=128, one-call split step", flush=True)
     case = workloads.c4_long(device=DEV)
     kv = qsa.PagedKV.from_case(case)
-    check_sparse_rows(case, kv, [5], heads_check=[0, 7])
+    assert qsa.sparse_decode_path(kv, case.Hq, 8192, case.k_pages) == "split"
+    meta, gs, sel, cnt, out, lse = _one_call_step(case, kv, "bound", "auto")
+    for b in range(case.B):
+        for h in (b % case.Hkv, (b + 5) % case.Hkv):
+            _check_step_row(case, "bound", "split", b, h, meta, gs, sel, cnt, out, lse)
+        print(f"[c4] sequence {b} checked", flush=True)
 
 
 def test_c3_dense_full_size_sampled():
@@ -123,7 +256,7 @@ def test_c3_dense_full_size_sampled():
                             d["seq_lens"], case.sm_scale)
     o_n, l_n = out.cpu().numpy(), lse.cpu().numpy()
     for si, b in enumerate(seqs):
-        assert_close_out(o_n[b], l_n[b], oo[si], ol[si])
+        assert_close_out(o_n[b], l_n[b], oo[si], ol[si], label="c3_dense/decode (stream split)")
     assert np.all(np.isfinite(o_n))
     # every page selected through the sparse entry: bit-identical
     K = max(-(-L // 16) for L in lens)
@@ -172,5 +305,6 @@ def test_c5_cascade_full_size_sampled(selective):
                               sel=osel, sel_count=ocnt)
     o_n, l_n = out.cpu().numpy(), lse.cpu().numpy()
     for si, b in enumerate(seqs):
-        assert_close_out(o_n[b], l_n[b], oo[si], ol[si])
+        assert_close_out(o_n[b], l_n[b], oo[si], ol[si],
+                         label=f"c5_cascade/{'pass B (suffix top-9)' if selective else 'pass A (all suffix)'}")
     assert np.all(np.isfinite(o_n))

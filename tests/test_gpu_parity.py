@@ -248,7 +248,30 @@ def test_end_to_end_pipeline_tiny_config():
     assert set(int(x) for x in c.planted[0]) <= set(int(x) for x in sel.cpu().numpy()[0, 0])
     oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], "f32", d["page_indptr"], d["page_indices"],
                             d["seq_lens"], c.sm_scale, sel=osel, sel_count=ocnt)
-    assert_close_out(out.cpu().numpy(), lse.cpu().numpy(), oo, ol)
+    assert_close_out(out.cpu().numpy(), lse.cpu().numpy(), oo, ol, label="c1_tiny/split-calls")
+
+
+@pytest.mark.parametrize("seed", [workloads.SEED_BASE + 1 + i for i in range(6)])
+def test_end_to_end_tiny_config_unit_vector_shift(seed):
+    # The tiny config with the planted shift read as the unit vector
+    # (+1.5 q/||q||_2): the planted pages no longer always stand out, so the
+    # selection is checked within the threshold band and the attention on
+    # the GPU's own selection against the oracle.
+    c = workloads.c1_tiny(seed=seed, plant_dir="unit")
+    d = case_np(c)
+    g, kv = _kv(c)
+    meta = qsa.build_page_meta(kv)
+    gs, _ = qsa.score_pages(g.q, kv, meta)
+    sel, cnt, phys = qsa.topk_pages(gs, kv, c.k_pages, num_q_heads=c.Hq)
+    out, lse = qsa.paged_decode(g.q, kv, sel=sel, sel_count=cnt, sm_scale=c.sm_scale)
+    torch.cuda.synchronize()
+    _, _, ogroup = _oracle_scores(c, d, 64)
+    table = d["page_indices"][:64]
+    check_selection_row(sel.cpu().numpy()[0, 0], cnt.cpu().numpy()[0, 0], phys.cpu().numpy()[0, 0], ogroup[0, 0],
+                        64, c.k_pages, table)
+    oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], "f32", d["page_indptr"], d["page_indices"],
+                            d["seq_lens"], c.sm_scale, sel=sel.cpu().numpy(), sel_count=cnt.cpu().numpy())
+    assert_close_out(out.cpu().numpy(), lse.cpu().numpy(), oo, ol, label="c1_tiny_unit_shift/split-calls")
 
 
 @pytest.mark.parametrize("prefix_len,suffix_len,B,Hq,Hkv,k", [
@@ -272,7 +295,7 @@ def test_cascade(prefix_len, suffix_len, B, Hq, Hkv, k):
     oo, ol = O.cascade_decode(d["q"], d["k_pool"], d["v_pool"], "bf16", d["prefix_pages"], prefix_len,
                               d["page_indptr"], d["page_indices"], d["seq_lens"], c.sm_scale,
                               sel=osel, sel_count=ocnt)
-    assert_close_out(out.cpu().numpy(), lse.cpu().numpy(), oo, ol)
+    assert_close_out(out.cpu().numpy(), lse.cpu().numpy(), oo, ol, label="small/cascade")
 
 
 def test_error_paths_raise():

@@ -185,6 +185,39 @@ def test_planted_hot_pages_in_top8():
     assert all(hits), hits
 
 
+def _planted_hit_rate(plant_dir, seeds):
+    """Over seeds of the tiny config: the share of planted pages in the
+    oracle's top 8, and the share of seeds with all 4 of them there."""
+    per_page, all_four = [], []
+    for s in seeds:
+        c = workloads.c1_tiny(seed=s, plant_dir=plant_dir)
+        d = case_np(c)
+        meta = O.build_page_meta(d["k_pool"], "f32", d["page_indptr"], d["page_indices"], d["seq_lens"])
+        _, group = O.score_pages(d["q"], "f32", meta, "f32", d["page_indptr"], d["page_indices"], d["seq_lens"], 1)
+        sel, cnt = O.topk_pages(group, d["seq_lens"], 8)
+        n_hit = len(set(int(x) for x in c.planted[0]) & set(int(x) for x in sel[0, 0, :cnt[0, 0]]))
+        per_page.append(n_hit / 4)
+        all_four.append(n_hit == 4)
+    return float(np.mean(per_page)), float(np.mean(all_four))
+
+
+def test_planted_hit_rate_under_both_readings_of_the_shift():
+    # The tiny config's "+1.5 q/|q|" read two ways, over 100 seeds: |q|
+    # element-wise (+1.5 sign(q_i) per dimension, the reading the workloads
+    # use) puts every planted page in the top 8 on every seed; |q| as the
+    # Euclidean norm (a shift of length 1.5 along q) puts about 90% of them
+    # there and all four on about 2 seeds in 3, so the config's "the true top
+    # pages are known" holds only under the first. Rates measured with these
+    # seeds: sign 1.0 / 1.0, unit 0.880 / 0.63 (200 seeds: 0.904 / 0.68).
+    seeds = range(workloads.SEED_BASE + 1, workloads.SEED_BASE + 101)
+    sign_page, sign_all = _planted_hit_rate("sign", seeds)
+    unit_page, unit_all = _planted_hit_rate("unit", seeds)
+    print(f"[P-C] planted pages in the top 8: sign {sign_page:.3f} (all four {sign_all:.2f}), "
+          f"unit {unit_page:.3f} (all four {unit_all:.2f})")
+    assert sign_page == 1.0 and sign_all == 1.0
+    assert 0.85 <= unit_page < 0.95 and 0.55 <= unit_all <= 0.8
+
+
 # ---------------------------------------------------------------- O5 top-K
 
 def test_topk_golden():

@@ -127,6 +127,7 @@ def build_case(
     drift: Optional[tuple] = None,
     nan_fill: bool = True,
     chunk_pages: int = 4096,
+    plant_dir: str = "sign",
 ) -> PagedCase:
     """Generic paged-decode input.
 
@@ -135,9 +136,11 @@ def build_case(
     chunks); then the optional structure:
       plant_pages: per sequence, that many logical pages (distinct, uniform)
         get +plant_scale * qbar_h/|qbar_h| added to every key of KV head h,
-        qbar_h the fp32 mean of the group's (rounded) queries and |.| taken
-        element-wise, i.e. a shift of plant_scale * sign(qbar_h[i]) in every
-        dimension (this makes the planted pages the true top pages);
+        qbar_h the fp32 mean of the group's (rounded) queries. plant_dir
+        "sign" takes |.| element-wise, i.e. a shift of plant_scale *
+        sign(qbar_h[i]) in every dimension (this makes the planted pages the
+        true top pages); plant_dir "unit" takes the Euclidean norm, a shift
+        of length plant_scale along the unit vector qbar_h/||qbar_h||_2;
       drift=(rho, sigma): per (b, h, dim) an AR(1) page mean over logical
         pages, mu_0 ~ N(0, sigma^2/(1-rho^2)), mu_j = rho*mu_{j-1} + sigma*eps,
         added to every key of the page.
@@ -172,7 +175,12 @@ def build_case(
     planted = None
     if plant_pages > 0:
         qf = q.to(torch.float32).view(B, Hkv, G, D).mean(dim=2)          # [B,Hkv,D]
-        dirn = torch.sign(qf)
+        if plant_dir == "sign":
+            dirn = torch.sign(qf)
+        elif plant_dir == "unit":
+            dirn = qf / torch.linalg.vector_norm(qf, dim=-1, keepdim=True)
+        else:
+            raise ValueError(plant_dir)
         rows = []
         for b in range(B):
             sel = torch.randperm(nps[b], generator=g, device=device)[:min(plant_pages, nps[b])]
@@ -217,18 +225,31 @@ def build_case(
     )
 
 
+def peaked(case: PagedCase, q_scale: float = 2.0, v_scale: float = 16.0) -> PagedCase:
+    """The same case with the queries scaled by q_scale (then rounded back to
+    the key dtype) and the values by v_scale (a power of two: exact), so the
+    softmax concentrates on a few tokens whose values are large: the inputs
+    on which the rounding of the attention weights shows most."""
+    out = dataclasses.replace(case)
+    out.q = (case.q.to(torch.float32) * q_scale).to(case.q.dtype)
+    out.v_pool = case.v_pool * v_scale
+    return out
+
+
 # --------------------------------------------------------------------------
 # The five workloads. Sizes follow the pages' workloads; seeds are fixed.
 # --------------------------------------------------------------------------
 
-def c1_tiny(device="cpu", seed=SEED_BASE + 1, n_sentinel=8) -> PagedCase:
+def c1_tiny(device="cpu", seed=SEED_BASE + 1, n_sentinel=8, plant_dir="sign") -> PagedCase:
     """1 sequence, 1 query head / 1 KV head, D=64, fp32, 1024 tokens (64
     pages), top-K=8. Q,K,V ~ N(0,1); 4 hot pages (distinct, uniform) get
-    +1.5*q/|q| (element-wise: 1.5*sign(q_i)) on every key so the true top
-    pages are known; physical slots
-    randomly permuted (plus NaN sentinel slots)."""
+    +1.5*q/|q| on every key so the true top pages are known: plant_dir
+    "sign" (default) reads |q| element-wise (1.5*sign(q_i) per dimension),
+    "unit" as the Euclidean norm (a shift of length 1.5 along q's
+    direction); physical slots randomly permuted (plus NaN sentinel
+    slots)."""
     return build_case("c1_tiny", 1, 1, 1, 64, [1024], "f32", seed, device, k_pages=8,
-                      n_sentinel=n_sentinel, plant_pages=4)
+                      n_sentinel=n_sentinel, plant_pages=4, plant_dir=plant_dir)
 
 
 def c2_sparse(device="cpu", seed=SEED_BASE + 2, B=16, L=8192, Hq=32, Hkv=8, n_sentinel=0) -> PagedCase:
