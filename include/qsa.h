@@ -232,6 +232,26 @@ qsa_status qsa_cascade_decode(const qsa_dims* dims, const void* q,
                               float sm_scale, float* out, float* lse, void* ws,
                               size_t ws_bytes, hipStream_t stream);
 
+/* qsa_paged_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, contract, plan and kernels as
+ * qsa_paged_decode (so the results are bit-identical to it), minus the
+ * workspace. The split-K partials go to a static device array of
+ * QSA_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends; the call allocates nothing. A batch whose partials need more
+ * (qsa_decode_workspace_size above the limit) returns QSA_ERR_WORKSPACE
+ * before any device work. Every call on one GPU shares that GPU's array and
+ * leaves its contents behind (nothing needs clearing: every partial a call
+ * reads is written earlier in the same call); calls that overlap on one GPU
+ * (other streams, other threads) race on it and must be serialised by the
+ * caller. */
+#define QSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+qsa_status qsa_paged_decode_noalloc(const qsa_dims* dims, const void* q,
+                                    const qsa_paged_kv* kv, const int32_t* sel,
+                                    const int32_t* sel_count, int32_t k,
+                                    float sm_scale, float* out, float* lse,
+                                    hipStream_t stream);
+
 /* Steps 2-4 as one call: one decode step of the sparse path (TinyServe §3.2
  * fuses page scoring, top-K selection and the sparse attention into one
  * kernel, with the scores kept on chip). Computes exactly what

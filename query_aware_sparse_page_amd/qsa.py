@@ -57,6 +57,7 @@ def lib():
             "qsa_topk_pages": (i32, [D, KV, vp, i32, i32, vp, vp, vp, vp, sz, vp]),
             "qsa_topk_pages_approx": (i32, [D, KV, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
             "qsa_paged_decode": (i32, [D, vp, KV, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
+            "qsa_paged_decode_noalloc": (i32, [D, vp, KV, vp, vp, i32, f32, vp, vp, vp]),
             "qsa_cascade_decode": (i32, [D, vp, vp, i32, KV, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
             "qsa_sparse_decode": (i32, [D, vp, KV, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, i32, vp,
                                         sz, vp]),
@@ -286,6 +287,26 @@ def paged_decode(q: torch.Tensor, kv: PagedKV, sel: Optional[torch.Tensor] = Non
     _check(lib().qsa_paged_decode(ctypes.byref(d), _ptr(q), ctypes.byref(s), _ptr(sel), _ptr(sel_count), k,
                                   ctypes.c_float(sm_scale), _ptr(o), _ptr(lse), _ptr(workspace),
                                   workspace.numel(), _stream()))
+    return o, lse
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # QSA_NOALLOC_SCRATCH_BYTES
+
+
+def paged_decode_noalloc(q: torch.Tensor, kv: PagedKV, sel: Optional[torch.Tensor] = None,
+                         sel_count: Optional[torch.Tensor] = None, sm_scale: Optional[float] = None,
+                         with_lse: bool = True, out=None):
+    """paged_decode without a workspace (qsa_paged_decode_noalloc): the
+    partials go to the library's static per-GPU scratch array. Outputs are
+    allocated here unless `out` = (o, lse) is given."""
+    B, Hq, D = q.shape
+    k = int(sel.shape[-1]) if sel is not None else 0
+    sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
+    o = out[0] if out is not None else torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    lse = (out[1] if out is not None else torch.empty(B, Hq, dtype=torch.float32, device=q.device)) if with_lse else None
+    d, s = kv.dims(Hq), kv.struct()
+    _check(lib().qsa_paged_decode_noalloc(ctypes.byref(d), _ptr(q), ctypes.byref(s), _ptr(sel), _ptr(sel_count),
+                                          k, ctypes.c_float(sm_scale), _ptr(o), _ptr(lse), _stream()))
     return o, lse
 
 
