@@ -264,10 +264,11 @@ qsa_status qsa_paged_decode_noalloc(const qsa_dims* dims, const void* q,
  * Optional outputs (each may be NULL): group_scores [B, Hkv, stride] fp32,
  * sel [B, Hkv, k] int32 (ascending, -1 padded), sel_count [B, Hkv] int32.
  * path selects the kernels:
- *   QSA_PATH_FUSED - one workgroup per (b, h) row scores, selects, attends
- *     and merges in LDS (one launch, no workspace); rows of at most 4096
+ *   QSA_PATH_FUSED - one launch, no workspace: one workgroup per (b, h)
+ *     row scores, selects, attends and merges in LDS; rows of at most 4096
  *     pages (max_b n_b <= 4096) with min(k, max_b n_b) <= 512, else
- *     QSA_ERR_UNSUPPORTED;
+ *     QSA_ERR_UNSUPPORTED. Rows of at most 64 pages with bf16 groups of 4 or
+ *     8 heads and the bound scorer take one wave per row instead;
  *   QSA_PATH_SPLIT - the separate score, top-K and split-K decode kernels,
  *     which spread one row over many workgroups (long rows, few rows);
  *   QSA_PATH_AUTO - FUSED when supported and B * Hkv >= 64, else SPLIT.
@@ -301,6 +302,32 @@ qsa_status qsa_sparse_decode_centroid(const qsa_dims* dims, const void* q,
                                       int32_t* sel, int32_t* sel_count,
                                       qsa_path path, void* ws, size_t ws_bytes,
                                       hipStream_t stream);
+
+/* One decode step of the selective cascade (Quail page, join attention; the
+ * suffix selection of TinyServe §2.2-§2.3): computes exactly what
+ * qsa_score_pages(refresh_tail) -> qsa_topk_pages(k) on the suffix pages ->
+ * qsa_cascade_decode(sel) compute - the same group scores (a -0 score may
+ * come back as +0), the same selection, and out / lse within fp32 rounding
+ * of qsa_cascade_decode on that selection. The prefix (prefix_pages,
+ * prefix_len) is attended whole by every sequence on the matrix cores; kv,
+ * meta, stride, refresh_tail, k and the optional outputs (group_scores, sel,
+ * sel_count: each may be NULL) are those of qsa_sparse_decode for the
+ * suffix tables. Suffix rows of at most 64 pages with bf16 groups of 4 or 8
+ * heads run in two launches (the prefix, then one wave per (sequence, KV
+ * head) row that scores, selects, attends and merges the prefix partials by
+ * LSE); other shapes run the separate score, top-K and split-K kernels with
+ * the prefix partials folded into the merge. Requires bf16, head_dim 128.
+ * Workspace: qsa_cascade_sparse_decode_workspace_size(...). */
+qsa_status qsa_cascade_sparse_decode(const qsa_dims* dims, const void* q,
+                                     const int32_t* prefix_pages, int32_t prefix_len,
+                                     const qsa_paged_kv* kv, void* meta, int32_t stride,
+                                     int32_t refresh_tail, int32_t k, float sm_scale,
+                                     float* out, float* lse, float* group_scores,
+                                     int32_t* sel, int32_t* sel_count, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+size_t qsa_cascade_sparse_decode_workspace_size(const qsa_dims* dims, int32_t prefix_len,
+                                                const int32_t* suffix_lens_host,
+                                                int32_t stride, int32_t k);
 
 /* The kernels qsa_sparse_decode will run for these arguments (QSA_PATH_FUSED
  * or QSA_PATH_SPLIT), in *chosen. */

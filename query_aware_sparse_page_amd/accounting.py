@@ -98,3 +98,16 @@ def fused_step_bytes(seq_lens, Hq, Hkv, D, elem_bytes, k, page_size=16, with_lse
     table = n_tot * 4
     return {"meta": meta, "tail": tail, "kv": kv, "q": q, "out": o, "table": table,
             "total": meta + tail + kv + q + o + table}
+
+
+def cascade_step_bytes(suffix_lens, prefix_len, Hq, Hkv, D, elem_bytes, k, page_size=16, with_lse=True):
+    """One selective cascade step (suffix scores, selection and attention,
+    the shared prefix attended whole, merged): the fused suffix step's bytes
+    (records, tail refresh, selected K/V, Q, O, LSE, table) plus the prefix's
+    K and V, read once."""
+    f = fused_step_bytes(suffix_lens, Hq, Hkv, D, elem_bytes, k, page_size=page_size, with_lse=with_lse)
+    pre = prefix_len * Hkv * D * 2 * elem_bytes
+    f = dict(f)
+    f["prefix_kv"] = pre
+    f["total"] += pre
+    return f

@@ -224,6 +224,14 @@ bool fused_supported(int max_pages, int k) {
   return max_pages <= qsa::kRowMaxPages && std::min(k, max_pages) <= qsa::kRowMaxSelect;
 }
 
+// Rows the one-wave-per-row kernel takes (bf16 groups of 4 or 8 heads, the
+// bound scorer, at most 64 pages per row).
+bool short_rows_supported(const qsa_dims* d, int max_pages, bool centroid) {
+  const int g = d->num_q_heads / d->num_kv_heads;
+  return d->dtype == QSA_BF16 && d->head_dim == 128 && (g == 4 || g == 8) && !centroid &&
+         max_pages <= qsa::kShortMaxPages;
+}
+
 qsa_path choose_path(const qsa_dims* d, int max_pages, int k, qsa_path path) {
   if (path != QSA_PATH_AUTO) return path;
   const long long rows = (long long)d->num_seqs * d->num_kv_heads;
@@ -670,6 +678,15 @@ qsa_status sparse_decode_impl(const qsa_dims* dims, const void* q, const qsa_pag
   qsa::LaunchCommon c = common(dims, kv);
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   Checked chk;
+  if (chosen == QSA_PATH_FUSED && short_rows_supported(dims, max_pages, centroid)) {
+    // rows of at most 64 pages: one wave per row
+    if ((s = chk.begin(c, stream)) != QSA_OK) return s;
+    return chk.end(device_status(qsa::launch_short_rows(c, q, meta, stride, refresh_tail, k, scale_log2,
+                                                        qsa::Partials{}, 0, out, lse, group_scores, sel,
+                                                        sel_count, stream),
+                                 "sparse_decode (fused, short rows) launch"),
+                   stream);
+  }
   if (chosen == QSA_PATH_FUSED) {
     // fewer rows than CUs: two workgroups per row, each attending for half
     // of the group's query heads
@@ -730,6 +747,112 @@ qsa_status qsa_sparse_decode_centroid(const qsa_dims* dims, const void* q, const
                                       size_t ws_bytes, hipStream_t stream) {
   return sparse_decode_impl(dims, q, kv, cent, stride, refresh_tail, k, sm_scale, out, lse,
                             group_scores, sel, sel_count, path, ws, ws_bytes, true, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The prefix partials of a cascade at the start of `base`.
+qsa::Partials carve_prefix(char* base, const qsa_dims* d, int prefix_len) {
+  const size_t rows = (size_t)d->num_kv_heads * prefix_splits(prefix_len) * (d->num_q_heads / d->num_kv_heads) *
+                      d->num_seqs;
+  qsa::Partials pre;
+  pre.o = reinterpret_cast<float*>(base);
+  pre.ml = reinterpret_cast<float*>(base + align_up(rows * d->head_dim * sizeof(float)));
+  return pre;
+}
+
+// Workspace of qsa_cascade_sparse_decode: the prefix partials, then (rows
+// too long for one wave each) the split path's scores, selection and
+// decode partials.
+size_t cascade_sparse_ws(const qsa_dims* d, int prefix_len, const int32_t* lens, int max_pages, int stride,
+                         int k) {
+  const size_t pre = prefix_ws_bytes(d, prefix_len);
+  if (short_rows_supported(d, max_pages, false)) return pre;
+  return pre + sparse_ws(d, lens, stride, k).total();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qsa_cascade_sparse_decode_workspace_size(const qsa_dims* dims, int32_t prefix_len,
+                                                const int32_t* suffix_lens_host, int32_t stride, int32_t k) {
+  if (check_dims(dims) != QSA_OK || suffix_lens_host == nullptr || prefix_len < 1 || k < 1) return 0;
+  int max_pages = 0;
+  for (int b = 0; b < dims->num_seqs; ++b) {
+    if (suffix_lens_host[b] < 1) return 0;
+    max_pages = std::max(max_pages, pages_of(suffix_lens_host[b]));
+  }
+  if (stride < max_pages) return 0;
+  return cascade_sparse_ws(dims, prefix_len, suffix_lens_host, max_pages, stride, k);
+}
+
+qsa_status qsa_cascade_sparse_decode(const qsa_dims* dims, const void* q, const int32_t* prefix_pages,
+                                     int32_t prefix_len, const qsa_paged_kv* kv, void* meta, int32_t stride,
+                                     int32_t refresh_tail, int32_t k, float sm_scale, float* out, float* lse,
+                                     float* group_scores, int32_t* sel, int32_t* sel_count, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  qsa_status s = check_dims(dims);
+  if (s != QSA_OK) return s;
+  if (dims->dtype != QSA_BF16)
+    return fail(QSA_ERR_UNSUPPORTED, "cascade decode is built for bf16 / head_dim 128 only");
+  int max_pages = 0;
+  if ((s = check_kv(dims, kv, true, &max_pages)) != QSA_OK) return s;
+  if (q == nullptr || out == nullptr || prefix_pages == nullptr || meta == nullptr)
+    return fail(QSA_ERR_INVALID_ARG, "q/out/prefix_pages/meta is NULL");
+  if (prefix_len < 1) return fail(QSA_ERR_INVALID_ARG, "prefix_len %d < 1", prefix_len);
+  if (k < 1) return fail(QSA_ERR_INVALID_ARG, "k = %d (must be >= 1)", k);
+  if (refresh_tail != 0 && refresh_tail != 1)
+    return fail(QSA_ERR_INVALID_ARG, "refresh_tail %d (0 or 1)", refresh_tail);
+  if (!std::isfinite(sm_scale)) return fail(QSA_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (stride < max_pages)
+    return fail(QSA_ERR_INVALID_ARG, "stride %d < longest sequence's page count %d", stride, max_pages);
+  const bool short_rows = short_rows_supported(dims, max_pages, false);
+  if (!short_rows && stride > qsa::kTopkMaxPages)
+    return fail(QSA_ERR_UNSUPPORTED, "stride %d > %d pages per row", stride, qsa::kTopkMaxPages);
+  const size_t need = cascade_sparse_ws(dims, prefix_len, kv->seq_lens_host, max_pages, stride, k);
+  if (ws_bytes < need || ws == nullptr)
+    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  qsa::DecodePlan plan;
+  if (!short_rows) {
+    plan = make_plan(dims, kv->seq_lens_host, k);
+    if ((s = check_plan(plan)) != QSA_OK) return s;
+  }
+  char* base = static_cast<char*>(ws);
+  const qsa::Partials pre = carve_prefix(base, dims, prefix_len);
+  const int nsplit = prefix_splits(prefix_len);
+  qsa::LaunchCommon c = common(dims, kv);
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  Checked chk;
+  if ((s = chk.begin(c, stream)) != QSA_OK) return s;
+  hipError_t e = qsa::launch_cascade_prefix(c, q, prefix_pages, prefix_len, nsplit, scale_log2, pre, stream);
+  if (e != hipSuccess) return device_status(e, "cascade prefix launch");
+  if (short_rows) {
+    e = qsa::launch_short_rows(c, q, meta, stride, refresh_tail, k, scale_log2, pre, nsplit, out, lse,
+                               group_scores, sel, sel_count, stream);
+    return chk.end(device_status(e, "cascade suffix (short rows) launch"), stream);
+  }
+  // long suffix rows: the separate score, top-K and split-K kernels, with
+  // the prefix partials folded into the merge
+  const SparseWs w = sparse_ws(dims, kv->seq_lens_host, stride, k);
+  char* sb = base + prefix_ws_bytes(dims, prefix_len);
+  float* gs = reinterpret_cast<float*>(sb);
+  sb += align_up(w.gs);
+  int32_t* sl = reinterpret_cast<int32_t*>(sb);
+  sb += align_up(w.sel);
+  int32_t* cn = reinterpret_cast<int32_t*>(sb);
+  sb += align_up(w.cnt);
+  if (group_scores != nullptr) gs = group_scores;
+  if (sel != nullptr) sl = sel;
+  if (sel_count != nullptr) cn = sel_count;
+  e = qsa::launch_score(c, q, meta, refresh_tail, gs, nullptr, stride, stream);
+  if (e != hipSuccess) return device_status(e, "cascade suffix score launch");
+  e = qsa::launch_topk(c, gs, stride, k, sl, cn, nullptr, stream);
+  if (e != hipSuccess) return device_status(e, "cascade suffix top-K launch");
+  e = qsa::launch_decode(c, q, sl, cn, k, scale_log2, plan, carve(sb, w.dec), pre, nsplit, out, lse, stream);
+  return chk.end(device_status(e, "cascade suffix decode launch"), stream);
 }
 
 }  // extern "C"

@@ -104,6 +104,17 @@ hipError_t launch_sparse_row(const LaunchCommon& c, const void* q, void* meta, i
                              float* out, float* lse, float* group_scores, int* sel, int* sel_count,
                              hipStream_t stream);
 
+// Steps 2-4 for rows of at most kShortMaxPages pages, one wave per (b, h)
+// row (bf16, D = 128, G = 4 or 8, the bound scorer): scores with the
+// tail-page refresh, the top-k pages, attention over them, and the LSE merge
+// with n_prefix prefix partials per query row ([Hkv][n_prefix][B*G], as the
+// cascade prefix writes them; n_prefix = 0: none). Outputs as
+// launch_sparse_row's.
+constexpr int kShortMaxPages = 64;
+hipError_t launch_short_rows(const LaunchCommon& c, const void* q, void* meta, int stride, int refresh_tail,
+                             int k, float scale_log2, Partials prefix, int n_prefix, float* out, float* lse,
+                             float* group_scores, int* sel, int* sel_count, hipStream_t stream);
+
 // Cascade prefix on the matrix cores (bf16, D = 128): partials per
 // (KV head, split, query row).
 hipError_t launch_cascade_prefix(const LaunchCommon& c, const void* q, const int* prefix_pages,

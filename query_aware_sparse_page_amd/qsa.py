@@ -63,6 +63,9 @@ def lib():
                                         sz, vp]),
             "qsa_sparse_decode_centroid": (i32, [D, vp, KV, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, i32,
                                                  vp, sz, vp]),
+            "qsa_cascade_sparse_decode": (i32, [D, vp, vp, i32, KV, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp,
+                                                vp, sz, vp]),
+            "qsa_cascade_sparse_decode_workspace_size": (sz, [D, i32, _i32p, i32, i32]),
             "qsa_sparse_decode_path": (i32, [D, _i32p, i32, i32, i32, _i32p]),
             "qsa_sparse_decode_workspace_size": (sz, [D, _i32p, i32, i32, i32]),
             "qsa_topk_workspace_size": (sz, [D, i32, i32]),
@@ -331,6 +334,37 @@ def cascade_decode(q: torch.Tensor, prefix_pages: torch.Tensor, prefix_len: int,
     _check(lib().qsa_cascade_decode(ctypes.byref(d), _ptr(q), _ptr(prefix_pages), prefix_len, ctypes.byref(s),
                                     _ptr(sel), _ptr(sel_count), k, ctypes.c_float(sm_scale), _ptr(o), _ptr(lse),
                                     _ptr(workspace), workspace.numel(), _stream()))
+    return o, lse
+
+
+def cascade_sparse_decode_workspace_size(kv: PagedKV, num_q_heads: int, prefix_len: int, stride: int,
+                                         k: int) -> int:
+    d = kv.dims(num_q_heads)
+    return int(lib().qsa_cascade_sparse_decode_workspace_size(ctypes.byref(d), prefix_len,
+                                                              ctypes.cast(kv._host_arr, _i32p), stride, k))
+
+
+def cascade_sparse_decode(q: torch.Tensor, prefix_pages: torch.Tensor, prefix_len: int, kv: PagedKV,
+                          meta: torch.Tensor, k: int, sm_scale: Optional[float] = None, refresh_tail: bool = True,
+                          with_lse: bool = True, group_scores: Optional[torch.Tensor] = None,
+                          sel: Optional[torch.Tensor] = None, sel_count: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, out=None):
+    """One selective cascade step (qsa_cascade_sparse_decode): scores and
+    top-k on the suffix pages (meta: the suffix tables' [m | M] records),
+    the shared prefix attended whole, merged by LSE."""
+    B, Hq, D = q.shape
+    stride = int(meta.shape[2])
+    sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
+    o = out[0] if out is not None else torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    lse = (out[1] if out is not None else torch.empty(B, Hq, dtype=torch.float32, device=q.device)) if with_lse else None
+    need = cascade_sparse_decode_workspace_size(kv, Hq, prefix_len, stride, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    d, s = kv.dims(Hq), kv.struct()
+    _check(lib().qsa_cascade_sparse_decode(ctypes.byref(d), _ptr(q), _ptr(prefix_pages), prefix_len, ctypes.byref(s),
+                                           _ptr(meta), stride, int(refresh_tail), k, ctypes.c_float(sm_scale),
+                                           _ptr(o), _ptr(lse), _ptr(group_scores), _ptr(sel), _ptr(sel_count),
+                                           _ptr(workspace), workspace.numel(), _stream()))
     return o, lse
 
 
