@@ -284,7 +284,7 @@ qsa_status qsa_sparse_decode(const qsa_dims* dims, const void* q,
                              const qsa_paged_kv* kv, void* meta, int32_t stride,
                              int32_t refresh_tail, int32_t k, float sm_scale,
                              float* out, float* lse, float* group_scores,
-                             int32_t* sel, int32_t* sel_count, qsa_path path,
+                             int32_t* sel, int32_t* sel_count, int32_t path /* qsa_path */,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* qsa_sparse_decode with the centroid scorer (Vortex digest, Block Top-K's
@@ -300,7 +300,7 @@ qsa_status qsa_sparse_decode_centroid(const qsa_dims* dims, const void* q,
                                       int32_t k, float sm_scale, float* out,
                                       float* lse, float* group_scores,
                                       int32_t* sel, int32_t* sel_count,
-                                      qsa_path path, void* ws, size_t ws_bytes,
+                                      int32_t path /* qsa_path */, void* ws, size_t ws_bytes,
                                       hipStream_t stream);
 
 /* One decode step of the selective cascade (Quail page, join attention; the
@@ -332,7 +332,7 @@ size_t qsa_cascade_sparse_decode_workspace_size(const qsa_dims* dims, int32_t pr
 /* The kernels qsa_sparse_decode will run for these arguments (QSA_PATH_FUSED
  * or QSA_PATH_SPLIT), in *chosen. */
 qsa_status qsa_sparse_decode_path(const qsa_dims* dims, const int32_t* seq_lens_host,
-                                  int32_t stride, int32_t k, qsa_path path,
+                                  int32_t stride, int32_t k, int32_t path /* qsa_path */,
                                   qsa_path* chosen);
 
 /* Workspace sizes in bytes (0 on invalid arguments). k <= 0 means dense. */
@@ -341,7 +341,7 @@ size_t qsa_decode_workspace_size(const qsa_dims* dims, const int32_t* seq_lens_h
 size_t qsa_cascade_workspace_size(const qsa_dims* dims, int32_t prefix_len,
                                   const int32_t* suffix_lens_host, int32_t k);
 size_t qsa_sparse_decode_workspace_size(const qsa_dims* dims, const int32_t* seq_lens_host,
-                                        int32_t stride, int32_t k, qsa_path path);
+                                        int32_t stride, int32_t k, int32_t path /* qsa_path */);
 
 /* The decode work split the library will use. bf16 groups of 4 or more
  * query heads with at most 1024 sequences take the stream split: every wave
@@ -373,7 +373,11 @@ int32_t qsa_get_checked(void);
 /* floor(budget_tokens / page_size): a token budget in whole pages (>= 0). */
 int32_t qsa_budget_pages(int32_t budget_tokens, int32_t page_size);
 
-const char* qsa_status_string(qsa_status status);
+/* status: a qsa_status value (others give "unknown status"). Enumerated
+ * arguments (status, path, dims->dtype) are passed as int32_t, so a value
+ * outside the enumeration is an argument error rather than undefined
+ * behaviour of the library. */
+const char* qsa_status_string(int32_t status);
 const char* qsa_last_error(void);
 int32_t qsa_version(void);
 

@@ -19,14 +19,40 @@ HIPCC_FLAGS = [
 ]
 
 
+# A second build for checking the host code: the host half of every source
+# under AddressSanitizer and UndefinedBehaviorSanitizer (each -fsanitize
+# applies to the host compilation only; the device code is unchanged). It
+# needs the sanitizer runtime preloaded (sanitizer_runtime()).
+SAN_LIB = os.path.join(PKG, "_sanitized", "libqsa.so")
+SAN_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-shared-libsan", "-g",
+]
+
+
 def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
+def sanitizer_runtime() -> str:
+    """The ASan (+UBSan) runtime the sanitized build links against."""
+    clang = "/opt/rocm/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path):
+        raise RuntimeError("sanitizer runtime not found")
+    return path
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources()]
+    lib = SAN_LIB if sanitize else LIB
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
+    tmp = lib + ".tmp"
+    flags = HIPCC_FLAGS + (SAN_FLAGS if sanitize else [])
+    cmd = [hipcc, *flags, "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources()]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -36,8 +62,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -232,8 +232,8 @@ bool short_rows_supported(const qsa_dims* d, int max_pages, bool centroid) {
          max_pages <= qsa::kShortMaxPages;
 }
 
-qsa_path choose_path(const qsa_dims* d, int max_pages, int k, qsa_path path) {
-  if (path != QSA_PATH_AUTO) return path;
+qsa_path choose_path(const qsa_dims* d, int max_pages, int k, int32_t path) {
+  if (path != QSA_PATH_AUTO) return path == QSA_PATH_FUSED ? QSA_PATH_FUSED : QSA_PATH_SPLIT;
   const long long rows = (long long)d->num_seqs * d->num_kv_heads;
   return (fused_supported(max_pages, k) && rows >= kFusedMinRows) ? QSA_PATH_FUSED : QSA_PATH_SPLIT;
 }
@@ -353,7 +353,7 @@ void qsa_set_checked(int32_t on) { set_checked_mode(on != 0); }
 
 int32_t qsa_get_checked(void) { return checked_mode() ? 1 : 0; }
 
-const char* qsa_status_string(qsa_status s) {
+const char* qsa_status_string(int32_t s) {
   switch (s) {
     case QSA_OK: return "ok";
     case QSA_ERR_INVALID_ARG: return "invalid argument";
@@ -618,12 +618,12 @@ qsa_status qsa_cascade_decode(const qsa_dims* dims, const void* q, const int32_t
 }
 
 qsa_status qsa_sparse_decode_path(const qsa_dims* dims, const int32_t* seq_lens_host,
-                                  int32_t stride, int32_t k, qsa_path path, qsa_path* chosen) {
+                                  int32_t stride, int32_t k, int32_t path, qsa_path* chosen) {
   qsa_status s = check_dims(dims);
   if (s != QSA_OK) return s;
   if (seq_lens_host == nullptr || chosen == nullptr) return fail(QSA_ERR_INVALID_ARG, "NULL argument");
   if (path != QSA_PATH_AUTO && path != QSA_PATH_FUSED && path != QSA_PATH_SPLIT)
-    return fail(QSA_ERR_INVALID_ARG, "unknown path %d", (int)path);
+    return fail(QSA_ERR_INVALID_ARG, "unknown path %d", path);
   if (k < 1) return fail(QSA_ERR_INVALID_ARG, "k = %d (must be >= 1)", k);
   int max_pages = 0;
   for (int b = 0; b < dims->num_seqs; ++b) {
@@ -645,7 +645,7 @@ qsa_status qsa_sparse_decode_path(const qsa_dims* dims, const int32_t* seq_lens_
 }
 
 size_t qsa_sparse_decode_workspace_size(const qsa_dims* dims, const int32_t* seq_lens_host,
-                                        int32_t stride, int32_t k, qsa_path path) {
+                                        int32_t stride, int32_t k, int32_t path) {
   qsa_path chosen;
   if (qsa_sparse_decode_path(dims, seq_lens_host, stride, k, path, &chosen) != QSA_OK) return 0;
   if (chosen == QSA_PATH_FUSED) return 0;
@@ -661,7 +661,7 @@ namespace {
 qsa_status sparse_decode_impl(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv,
                               void* meta, int32_t stride, int32_t refresh_tail, int32_t k,
                               float sm_scale, float* out, float* lse, float* group_scores,
-                              int32_t* sel, int32_t* sel_count, qsa_path path, void* ws,
+                              int32_t* sel, int32_t* sel_count, int32_t path, void* ws,
                               size_t ws_bytes, bool centroid, hipStream_t stream) {
   qsa_status s = check_dims(dims);
   if (s != QSA_OK) return s;
@@ -734,7 +734,7 @@ extern "C" {
 qsa_status qsa_sparse_decode(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv, void* meta,
                              int32_t stride, int32_t refresh_tail, int32_t k, float sm_scale,
                              float* out, float* lse, float* group_scores, int32_t* sel,
-                             int32_t* sel_count, qsa_path path, void* ws, size_t ws_bytes,
+                             int32_t* sel_count, int32_t path, void* ws, size_t ws_bytes,
                              hipStream_t stream) {
   return sparse_decode_impl(dims, q, kv, meta, stride, refresh_tail, k, sm_scale, out, lse,
                             group_scores, sel, sel_count, path, ws, ws_bytes, false, stream);
@@ -743,7 +743,7 @@ qsa_status qsa_sparse_decode(const qsa_dims* dims, const void* q, const qsa_page
 qsa_status qsa_sparse_decode_centroid(const qsa_dims* dims, const void* q, const qsa_paged_kv* kv,
                                       void* cent, int32_t stride, int32_t refresh_tail, int32_t k,
                                       float sm_scale, float* out, float* lse, float* group_scores,
-                                      int32_t* sel, int32_t* sel_count, qsa_path path, void* ws,
+                                      int32_t* sel, int32_t* sel_count, int32_t path, void* ws,
                                       size_t ws_bytes, hipStream_t stream) {
   return sparse_decode_impl(dims, q, kv, cent, stride, refresh_tail, k, sm_scale, out, lse,
                             group_scores, sel, sel_count, path, ws, ws_bytes, true, stream);

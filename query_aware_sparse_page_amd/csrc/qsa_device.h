@@ -274,18 +274,23 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-// Element-wise min and max of the first `valid` key rows of one (page, KV
-// head) tile (16 rows x 256 B), exact (order keys, -0 < +0). Each load reads
-// 1 KiB contiguous: lane l holds chunk l%16 of rows {l/16, 4 + l/16, 8 + l/16,
-// 12 + l/16}; after the in-lane reduction lanes l, l^16, l^32, l^48 combine,
-// so on return every lane holds the tile's min / max of chunk l%16.
-template <typename T>
-__device__ __forceinline__ void tile_minmax(const char* tile, int valid, int lane, uint4& vmn,
-                                            uint4& vmx) {
-  using Ops = KeyOps<T>;
-  uint4 rows[4];
+// The rows of one (page, KV head) tile (16 rows x 256 B) as the tile
+// reductions below take them: four 16-byte loads per lane, each reading 1 KiB
+// contiguous; lane l holds chunk l%16 of rows {l/16, 4 + l/16, 8 + l/16,
+// 12 + l/16}.
+__device__ __forceinline__ void tile_load_rows(const char* tile, int lane, uint4 (&rows)[4]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) rows[r] = ld16(tile + r * 1024 + lane * 16);
+}
+
+// Element-wise min and max of the first `valid` key rows of one tile (rows
+// as tile_load_rows leaves them), exact (order keys, -0 < +0). After the
+// in-lane reduction lanes l, l^16, l^32, l^48 combine, so on return every
+// lane holds the tile's min / max of chunk l%16.
+template <typename T>
+__device__ __forceinline__ void tile_minmax_rows(const uint4 (&rows)[4], int valid, int lane, uint4& vmn,
+                                                 uint4& vmx) {
+  using Ops = KeyOps<T>;
   uint32_t mn[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
   uint32_t mx[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -311,6 +316,15 @@ __device__ __forceinline__ void tile_minmax(const char* tile, int valid, int lan
   vmx = make_uint4(Ops::unkey(mx[0]), Ops::unkey(mx[1]), Ops::unkey(mx[2]), Ops::unkey(mx[3]));
 }
 
+// tile_minmax_rows of the tile at `tile`.
+template <typename T>
+__device__ __forceinline__ void tile_minmax(const char* tile, int valid, int lane, uint4& vmn,
+                                            uint4& vmx) {
+  uint4 rows[4];
+  tile_load_rows(tile, lane, rows);
+  tile_minmax_rows<T>(rows, valid, lane, vmn, vmx);
+}
+
 // fp64 -> nearest bf16 (ties to even), as the bf16 bit pattern: the value is
 // rounded to 8 significant bits inside the fp64 encoding (a carry moves into
 // the exponent by itself), after which the conversion to fp32 is exact.
@@ -329,18 +343,15 @@ __device__ __forceinline__ double xshfl_d(double v, int mask) {
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
-// Mean of the valid rows of one (page, KV head) tile, element-wise, rounded
-// once to the element type: the row sums are taken in fp64 (the sum of up to
-// 16 bf16 values is exact there unless their magnitudes span more than about
-// 2^41), divided by `valid` in fp64 (correctly rounded), then rounded to bf16
-// (ties to even) or converted to fp32. Rows are distributed as in
-// tile_minmax; on return every lane holds the mean of chunk lane % 16.
+// Mean of the valid rows of one tile (rows as tile_load_rows leaves them),
+// element-wise, rounded once to the element type: the row sums are taken in
+// fp64 (the sum of up to 16 bf16 values is exact there unless their
+// magnitudes span more than about 2^41), divided by `valid` in fp64
+// (correctly rounded), then rounded to bf16 (ties to even) or converted to
+// fp32. On return every lane holds the mean of chunk lane % 16.
 template <typename T>
-__device__ __forceinline__ uint4 tile_mean(const char* tile, int valid, int lane) {
+__device__ __forceinline__ uint4 tile_mean_rows(const uint4 (&rows)[4], int valid, int lane) {
   constexpr int E = Elem<T>::kPerChunk;
-  uint4 rows[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) rows[r] = ld16(tile + r * 1024 + lane * 16);
   double acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0;
@@ -370,6 +381,14 @@ __device__ __forceinline__ uint4 tile_mean(const char* tile, int valid, int lane
     for (int e = 0; e < 4; ++e) w[e] = __float_as_uint((float)acc[e]);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// tile_mean_rows of the tile at `tile`.
+template <typename T>
+__device__ __forceinline__ uint4 tile_mean(const char* tile, int valid, int lane) {
+  uint4 rows[4];
+  tile_load_rows(tile, lane, rows);
+  return tile_mean_rows<T>(rows, valid, lane);
 }
 
 // Orders this wave's LDS accesses before and after the call point (all lanes

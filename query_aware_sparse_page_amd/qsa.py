@@ -11,7 +11,9 @@ from typing import Optional, Sequence, Tuple
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsa.so")
+# QSA_LIBRARY names another build of the same library (for example one with
+# the host code under sanitizers); by default the in-tree build is loaded.
+_LIB_PATH = os.environ.get("QSA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsa.so")
 _lib = None
 
 QSA_OK, QSA_ERR_INVALID_ARG, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_DEVICE = range(5)
