@@ -52,7 +52,28 @@ FUSED_SRC = ["sparse_row.hip", "decode_wave.h", "qsa_device.h", "qsa_internal.h"
 DECODE_SRC = ["decode.hip", "decode_mfma.h", "decode_wave.h", "qsa_device.h", "qsa_internal.h", "api.hip"]
 SPLIT_SRC = ["score.hip", "topk.hip"] + DECODE_SRC
 CASCADE_SRC = ["cascade.hip"] + DECODE_SRC
-MEASURED = {}
+SCORE_SRC = ["score.hip", "qsa_device.h", "qsa_internal.h"]
+CASCADE_SPARSE_SRC = ["cascade.hip", "short_row.hip", "decode_mfma.h", "decode_wave.h", "qsa_device.h",
+                      "qsa_internal.h"]
+PREFIX_SRC = ["cascade.hip", "qsa_device.h", "qsa_internal.h"]
+# kernel_us of a multi-kernel launch is the sum of its kernels' averages
+# (c2 dense and c3: split-K decode + merge; c5: prefix + short rows).
+MEASURED = {
+    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 45.47, "traffic": 197479888, "l2_hit": 0.5255,
+        "sources": FUSED_SRC, "sha256_16": "10a849ea10680d8f", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.56,
+        "sources": FUSED_SRC, "sha256_16": "10a849ea10680d8f", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 102.86, "traffic": 539293828,
+        "sources": DECODE_SRC, "sha256_16": "faa6501929e8bb7e", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
+    ('c3_dense', 'dense', 'bound'): {"kernel_us": 877.0, "traffic": 5143186925, "l2_hit": 0.0083,
+        "sources": DECODE_SRC, "sha256_16": "faa6501929e8bb7e", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
+    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 46.06, "traffic": 271420319,
+        "sources": SCORE_SRC, "sha256_16": "a0ac92e895ca5639", "profile": "profiles/split_pipeline_c4_long.md"},
+    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 86.79, "traffic": 305950889,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "bf765676c5b313e9", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 38.58,
+        "sources": PREFIX_SRC, "sha256_16": "8bfc88bf79cba8de", "profile": "profiles/cascade_prefix_kernel_counters_c5_cascade.md"},
+}
 
 
 def sources_sha(files):
