@@ -112,6 +112,8 @@ def test_short_rows_fused_matches_oracle_and_split(label, lens, Hq, Hkv, k):
     (256, 48, 5, 8, 2, 2), (100, 70, 3, 16, 2, 3), (1024 + 64, 160, 33, 8, 2, 4), (512, 200, 9, 8, 2, 20),
     (2048, 512, 20, 32, 8, 9), (4096, 1024, 4, 32, 8, 9),      # 64-page suffix rows
     (1000, 1200, 3, 8, 2, 9),                                  # 75-page suffix rows: the split fallback
+    (16, 40, 128, 32, 8, 2),                                   # a one-page prefix, 1024 suffix rows
+    (9000, 64, 64, 32, 8, 3),                                  # a long prefix (18 splits), ragged last split
 ])
 def test_cascade_sparse_decode_matches_oracle(prefix_len, suffix_len, B, Hq, Hkv, k):
     c = workloads.cascade_case("cas_sparse", B, Hq, Hkv, 128, prefix_len, suffix_len, "bf16", 89, n_sentinel=3)
