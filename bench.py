@@ -94,8 +94,11 @@ def measured(key, field):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # (defaults: about 50 ms of untimed warm-up and 50 ms timed on the default
+    # workload; 20 warm-up steps left the clocks short of steady state and
+    # the 200-step mean 5% above the steady per-step time)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", default="c2_sparse",
                     choices=["c2_sparse", "c3_dense", "c4_long", "c5_cascade"])
     ap.add_argument("--replicas", type=int, default=4, help="KV pool copies rotated over steps")
@@ -108,7 +111,7 @@ def parse():
                          "its selection is measured against")
     ap.add_argument("--no-others", action="store_true",
                     help="time only --config (no other_configs block)")
-    ap.add_argument("--other-steps", type=int, default=20, help="timed steps of each other config")
+    ap.add_argument("--other-steps", type=int, default=200, help="timed (and warm-up) steps of each other config")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
@@ -501,7 +504,7 @@ def main():
             if cfg == args.config:
                 continue
             torch.cuda.empty_cache()
-            r, c, _, _ = run_config(cfg, steps=args.other_steps, warmup=3, replicas=args.replicas,
+            r, c, _, _ = run_config(cfg, steps=args.other_steps, warmup=args.other_steps, replicas=args.replicas,
                                     path_arg="auto", scorer="bound", dense=False,
                                     graph_timing=not args.no_graph, cpu_seconds=0, log=log)
             del c
