@@ -1,7 +1,9 @@
 """The five workloads at their full sizes, in the launch configuration the
-benchmark uses: the GPU runs the whole batch; the oracle checks sampled
-sequences one by one (their pages are gathered into a compact pool, which is
-input marshalling only - the oracle sees generated inputs, never GPU output)."""
+benchmark uses: the GPU runs the whole batch; the oracle checks sequences
+one by one - every sequence on one or two of its KV heads, and sampled
+sequences on all of them (their pages are gathered into a compact pool, which
+is input marshalling only - the oracle sees generated inputs, never GPU
+output)."""
 import numpy as np
 import pytest
 import torch
@@ -269,6 +271,95 @@ def test_c3_dense_full_size_sampled():
     o2, l2 = qsa.paged_decode(case.q, kv, sel=sel.to(DEV), sel_count=cnt.to(DEV), sm_scale=case.sm_scale)
     torch.cuda.synchronize()
     assert torch.equal(o2, out) and torch.equal(l2, lse)
+
+
+def test_c3_dense_full_size_every_sequence():
+    """Every sequence of the dense batch (the benchmarked stream-split launch)
+    on one of its KV heads against the oracle."""
+    print("[case] c3 dense full size, every sequence on one KV head", flush=True)
+    case = workloads.c3_dense(device=DEV, n_sentinel=32)
+    kv = qsa.PagedKV.from_case(case)
+    out, lse = qsa.paged_decode(case.q, kv, sm_scale=case.sm_scale)
+    torch.cuda.synchronize()
+    G = case.group
+    o_n, l_n = out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(case.B):
+        h = b % case.Hkv
+        d = subcase_head(case, b, h)
+        oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], "bf16", d["page_indptr"], d["page_indices"],
+                                d["seq_lens"], case.sm_scale)
+        assert_close_out(o_n[b, h * G:(h + 1) * G], l_n[b, h * G:(h + 1) * G], oo[0], ol[0],
+                         label="c3_dense/decode (stream split)")
+        if b % 16 == 15:
+            print(f"[c3] sequences up to {b} checked", flush=True)
+
+
+def subcase_head_cascade(case, b, h):
+    """Oracle inputs for KV head h of sequence b of a cascade case: the shared
+    prefix's pages, then the sequence's suffix pages, gathered to a compact
+    host pool that keeps only head h (input marshalling only)."""
+    indptr = case.page_indptr.cpu().numpy()
+    suf = case.page_indices.cpu().numpy()[indptr[b]:indptr[b + 1]].astype(np.int64)
+    pre = case.prefix_pages.cpu().numpy().astype(np.int64)
+    idx = torch.from_numpy(np.concatenate([pre, suf])).to(case.k_pool.device)
+    G = case.group
+    return dict(
+        q=np_store(case.q[b:b + 1, h * G:(h + 1) * G]),
+        k_pool=np_store(case.k_pool[idx, h:h + 1]), v_pool=np_store(case.v_pool[idx, h:h + 1]),
+        prefix_pages=np.arange(len(pre), dtype=np.int32),
+        page_indptr=np.array([0, len(suf)], dtype=np.int32),
+        page_indices=np.arange(len(pre), len(pre) + len(suf), dtype=np.int32),
+        seq_lens=case.seq_lens.cpu().numpy()[b:b + 1].astype(np.int32),
+    )
+
+
+@pytest.mark.parametrize("selective", [False, True])
+def test_c5_cascade_full_size_every_sequence(selective):
+    """Every sequence of the shared-prefix batch on one of its KV heads, in
+    the benchmarked calls: qsa_cascade_decode over all suffix pages, or the
+    one-call selective step qsa_cascade_sparse_decode (its selection checked
+    within the threshold band, the output against the oracle's cascade on
+    the GPU's own selection)."""
+    print(f"[case] c5 cascade full size, every sequence on one KV head, selective={selective}", flush=True)
+    case = workloads.c5_cascade(device=DEV, selective=selective, n_sentinel=16)
+    kv = qsa.PagedKV.from_case(case)
+    B, Hkv, G, k = case.B, case.Hkv, case.group, case.k_pages
+    if selective:
+        meta = qsa.build_page_meta(kv)
+        stride = int(meta.shape[2])
+        gs = torch.empty(B, Hkv, stride, dtype=torch.float32, device=DEV)
+        sel = torch.empty(B, Hkv, k, dtype=torch.int32, device=DEV)
+        cnt = torch.empty(B, Hkv, dtype=torch.int32, device=DEV)
+        out, lse = qsa.cascade_sparse_decode(case.q, case.prefix_pages, case.prefix_len, kv, meta, k,
+                                             sm_scale=case.sm_scale, group_scores=gs, sel=sel, sel_count=cnt)
+        sel_n, cnt_n = sel.cpu().numpy(), cnt.cpu().numpy()
+    else:
+        out, lse = qsa.cascade_decode(case.q, case.prefix_pages, case.prefix_len, kv, sm_scale=case.sm_scale)
+    torch.cuda.synchronize()
+    o_n, l_n = out.cpu().numpy(), lse.cpu().numpy()
+    table = case.page_indices.cpu().numpy()
+    indptr = case.page_indptr.cpu().numpy()
+    for b in range(B):
+        h = b % Hkv
+        d = subcase_head_cascade(case, b, h)
+        s1 = c1 = None
+        if selective:
+            args = (d["page_indptr"], d["page_indices"], d["seq_lens"])
+            rec = O.build_page_meta(d["k_pool"], "bf16", *args)
+            _, group = O.score_pages(d["q"], "bf16", rec, "bf16", *args, 1)
+            n = O.num_pages(int(d["seq_lens"][0]))
+            got_sel, _ = check_selection_row(sel_n[b, h], cnt_n[b, h], None, group[0, 0], n, k,
+                                             table[indptr[b]:indptr[b + 1]])
+            s1 = np.full((1, 1, k), -1, dtype=np.int32)
+            s1[0, 0, :len(got_sel)] = got_sel
+            c1 = np.array([[len(got_sel)]], dtype=np.int32)
+        oo, ol = O.cascade_decode(d["q"], d["k_pool"], d["v_pool"], "bf16", d["prefix_pages"], case.prefix_len,
+                                  d["page_indptr"], d["page_indices"], d["seq_lens"], case.sm_scale,
+                                  sel=s1, sel_count=c1)
+        label = "c5_cascade/one-call selective step" if selective else "c5_cascade/pass A (all suffix)"
+        assert_close_out(o_n[b, h * G:(h + 1) * G], l_n[b, h * G:(h + 1) * G], oo[0], ol[0], label=label)
+        if b % 64 == 63:
+            print(f"[c5] sequences up to {b} checked", flush=True)
 
 
 @pytest.mark.parametrize("selective", [False, True])
