@@ -313,10 +313,13 @@ qsa_status qsa_sparse_decode_centroid(const qsa_dims* dims, const void* q,
  * meta, stride, refresh_tail, k and the optional outputs (group_scores, sel,
  * sel_count: each may be NULL) are those of qsa_sparse_decode for the
  * suffix tables. Suffix rows of at most 64 pages with bf16 groups of 4 or 8
- * heads run in two launches (the prefix, then one wave per (sequence, KV
- * head) row that scores, selects, attends and merges the prefix partials by
- * LSE); other shapes run the separate score, top-K and split-K kernels with
- * the prefix partials folded into the merge. Requires bf16, head_dim 128.
+ * heads run in two launches: one grid that interleaves the prefix's
+ * workgroups (1024-token splits on the matrix cores) with the suffix rows'
+ * (one wave per (sequence, KV head) row that scores, selects and attends),
+ * so that a CU runs one of each at once, then the log-sum-exp merge of the
+ * prefix and suffix partials. Other shapes run the prefix kernel and the
+ * separate score, top-K and split-K kernels with the prefix partials folded
+ * into the merge. Requires bf16, head_dim 128.
  * Workspace: qsa_cascade_sparse_decode_workspace_size(...). */
 qsa_status qsa_cascade_sparse_decode(const qsa_dims* dims, const void* q,
                                      const int32_t* prefix_pages, int32_t prefix_len,

@@ -203,13 +203,17 @@ qsa::Partials carve(void* ws, const DecodeWs& w) {
 }
 
 constexpr int kPrefixSplitTokens = 512;  // prefix tokens per cascade split
+// Splits of the one-launch selective cascade: its 4-wave prefix workgroups
+// share the CUs with the suffix rows, and the merge reads every split's
+// partials (512-token splits: c5 step 78.0 us; 1024: 71.6 us; 768: 78.4 us).
+constexpr int kOverlapSplitTokens = 1024;
 
-int prefix_splits(int prefix_len) {
-  return std::max(1, (prefix_len + kPrefixSplitTokens - 1) / kPrefixSplitTokens);
+int prefix_splits(int prefix_len, int tokens = kPrefixSplitTokens) {
+  return std::max(1, (prefix_len + tokens - 1) / tokens);
 }
 
-size_t prefix_ws_bytes(const qsa_dims* d, int prefix_len) {
-  const size_t rows = (size_t)d->num_kv_heads * prefix_splits(prefix_len) * d->num_q_heads /
+size_t prefix_ws_bytes(const qsa_dims* d, int prefix_len, int tokens = kPrefixSplitTokens) {
+  const size_t rows = (size_t)d->num_kv_heads * prefix_splits(prefix_len, tokens) * d->num_q_heads /
                       d->num_kv_heads * d->num_seqs;
   return align_up(rows * d->head_dim * sizeof(float)) + align_up(rows * 2 * sizeof(float));
 }
@@ -754,23 +758,34 @@ qsa_status qsa_sparse_decode_centroid(const qsa_dims* dims, const void* q, const
 namespace {
 
 // The prefix partials of a cascade at the start of `base`.
-qsa::Partials carve_prefix(char* base, const qsa_dims* d, int prefix_len) {
-  const size_t rows = (size_t)d->num_kv_heads * prefix_splits(prefix_len) * (d->num_q_heads / d->num_kv_heads) *
-                      d->num_seqs;
+qsa::Partials carve_prefix(char* base, const qsa_dims* d, int prefix_len, int tokens = kPrefixSplitTokens) {
+  const size_t rows = (size_t)d->num_kv_heads * prefix_splits(prefix_len, tokens) *
+                      (d->num_q_heads / d->num_kv_heads) * d->num_seqs;
   qsa::Partials pre;
   pre.o = reinterpret_cast<float*>(base);
   pre.ml = reinterpret_cast<float*>(base + align_up(rows * d->head_dim * sizeof(float)));
   return pre;
 }
 
-// Workspace of qsa_cascade_sparse_decode: the prefix partials, then (rows
-// too long for one wave each) the split path's scores, selection and
-// decode partials.
+// The suffix rows' unmerged partials of the one-launch form (one unit per
+// (sequence, KV head) row: o [rows][g][D], then (max, sum) [rows][g][2]).
+DecodeWs suffix_ws(const qsa_dims* d) {
+  const size_t rows = (size_t)d->num_seqs * d->num_kv_heads;
+  const int g = d->num_q_heads / d->num_kv_heads;
+  DecodeWs w;
+  w.o_bytes = rows * g * d->head_dim * sizeof(float);
+  w.ml_bytes = rows * g * 2 * sizeof(float);
+  return w;
+}
+
+// Workspace of qsa_cascade_sparse_decode: the prefix partials, then the
+// suffix rows' partials (rows of one wave each) or the split path's scores,
+// selection and decode partials.
 size_t cascade_sparse_ws(const qsa_dims* d, int prefix_len, const int32_t* lens, int max_pages, int stride,
                          int k) {
-  const size_t pre = prefix_ws_bytes(d, prefix_len);
-  if (short_rows_supported(d, max_pages, false)) return pre;
-  return pre + sparse_ws(d, lens, stride, k).total();
+  if (short_rows_supported(d, max_pages, false))
+    return prefix_ws_bytes(d, prefix_len, kOverlapSplitTokens) + suffix_ws(d).total();
+  return prefix_ws_bytes(d, prefix_len) + sparse_ws(d, lens, stride, k).total();
 }
 
 }  // namespace
@@ -821,19 +836,26 @@ qsa_status qsa_cascade_sparse_decode(const qsa_dims* dims, const void* q, const 
     if ((s = check_plan(plan)) != QSA_OK) return s;
   }
   char* base = static_cast<char*>(ws);
-  const qsa::Partials pre = carve_prefix(base, dims, prefix_len);
-  const int nsplit = prefix_splits(prefix_len);
+  const int tokens = short_rows ? kOverlapSplitTokens : kPrefixSplitTokens;
+  const qsa::Partials pre = carve_prefix(base, dims, prefix_len, tokens);
+  const int nsplit = prefix_splits(prefix_len, tokens);
   qsa::LaunchCommon c = common(dims, kv);
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   Checked chk;
   if ((s = chk.begin(c, stream)) != QSA_OK) return s;
+  if (short_rows) {
+    // the prefix and the suffix rows in one launch, then the merge
+    const qsa::Partials suf = carve(base + prefix_ws_bytes(dims, prefix_len, tokens), suffix_ws(dims));
+    hipError_t e = qsa::launch_cascade_overlap(c, q, prefix_pages, prefix_len, nsplit, scale_log2, pre, meta,
+                                               stride, refresh_tail, k, suf, group_scores, sel, sel_count,
+                                               device_cus() / 8, stream);
+    if (e != hipSuccess) return device_status(e, "cascade (prefix and suffix rows) launch");
+    return chk.end(device_status(qsa::launch_merge(c, suf, 1, 1 << 30, pre, nsplit, out, lse, stream),
+                                 "cascade merge launch"),
+                   stream);
+  }
   hipError_t e = qsa::launch_cascade_prefix(c, q, prefix_pages, prefix_len, nsplit, scale_log2, pre, stream);
   if (e != hipSuccess) return device_status(e, "cascade prefix launch");
-  if (short_rows) {
-    e = qsa::launch_short_rows(c, q, meta, stride, refresh_tail, k, scale_log2, pre, nsplit, out, lse,
-                               group_scores, sel, sel_count, stream);
-    return chk.end(device_status(e, "cascade suffix (short rows) launch"), stream);
-  }
   // long suffix rows: the separate score, top-K and split-K kernels, with
   // the prefix partials folded into the merge
   const SparseWs w = sparse_ws(dims, kv->seq_lens_host, stride, k);

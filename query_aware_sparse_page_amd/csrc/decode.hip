@@ -647,6 +647,15 @@ hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
 
 }  // namespace
 
+hipError_t launch_merge(const LaunchCommon& c, Partials part, int max_units, int chunk, Partials prefix,
+                        int n_prefix, float* out, float* lse, hipStream_t stream) {
+  if (c.D != 128) return hipErrorInvalidValue;
+  dim3 mgrid((c.B * c.Hq + 3) / 4);
+  hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, stream, c.B, c.Hkv, c.G, c.seq_lens, nullptr, 0,
+                     chunk, max_units, part.o, part.ml, prefix.o, prefix.ml, n_prefix, nullptr, 0, out, lse);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const LaunchCommon& c, const void* q, const int* sel, const int* sel_count,
                          int k, float scale_log2, const DecodePlan& plan, Partials part,
                          Partials prefix, int n_prefix, float* out, float* lse,

@@ -115,6 +115,26 @@ hipError_t launch_short_rows(const LaunchCommon& c, const void* q, void* meta, i
                              int k, float scale_log2, Partials prefix, int n_prefix, float* out, float* lse,
                              float* group_scores, int* sel, int* sel_count, hipStream_t stream);
 
+// The log-sum-exp merge alone: per query row, the row's split-K partials
+// (units of `chunk` pages over its seq_lens pages, at most max_units; the
+// layout of launch_decode's) and n_prefix prefix partials, into out / lse
+// (D = 128).
+hipError_t launch_merge(const LaunchCommon& c, Partials part, int max_units, int chunk, Partials prefix,
+                        int n_prefix, float* out, float* lse, hipStream_t stream);
+
+// A selective cascade step's two halves in one launch, ahead of
+// launch_merge: the cascade prefix's workgroups (4 waves each) interleaved
+// with the short-row workgroups of the suffix rows, whose unmerged partials
+// go to suffix (one unit per row: [rows][G][D] and [rows][G][2]). A CU holds
+// two of these workgroups, so the prefix's products and the suffix rows'
+// loads share it (cus_per_xcd: the device's CUs per XCD, which sets the
+// interleave). bf16, D = 128, G = 4 or 8, suffix rows of at most
+// kShortMaxPages pages.
+hipError_t launch_cascade_overlap(const LaunchCommon& c, const void* q, const int* prefix_pages, int prefix_len,
+                                  int n_splits, float scale_log2, Partials prefix, void* meta, int stride,
+                                  int refresh_tail, int k, Partials suffix, float* group_scores, int* sel,
+                                  int* sel_count, int cus_per_xcd, hipStream_t stream);
+
 // Cascade prefix on the matrix cores (bf16, D = 128): partials per
 // (KV head, split, query row).
 hipError_t launch_cascade_prefix(const LaunchCommon& c, const void* q, const int* prefix_pages,
