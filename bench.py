@@ -53,26 +53,29 @@ DECODE_SRC = ["decode.hip", "decode_mfma.h", "decode_wave.h", "qsa_device.h", "q
 SPLIT_SRC = ["score.hip", "topk.hip"] + DECODE_SRC
 CASCADE_SRC = ["cascade.hip"] + DECODE_SRC
 SCORE_SRC = ["score.hip", "qsa_device.h", "qsa_internal.h"]
-CASCADE_SPARSE_SRC = ["cascade.hip", "short_row.hip", "decode_mfma.h", "decode_wave.h", "qsa_device.h",
-                      "qsa_internal.h"]
-PREFIX_SRC = ["cascade.hip", "qsa_device.h", "qsa_internal.h"]
+CASCADE_SPARSE_SRC = ["cascade_overlap.hip", "cascade_prefix.h", "short_row.h", "decode.hip", "decode_mfma.h",
+                      "decode_wave.h", "qsa_device.h", "qsa_internal.h", "api.hip"]
+PREFIX_SRC = ["cascade.hip", "cascade_prefix.h", "qsa_device.h", "qsa_internal.h"]
 # kernel_us of a multi-kernel launch is the sum of its kernels' averages
-# (c2 dense and c3: split-K decode + merge; c5: prefix + short rows).
+# (c2 dense and c3: split-K decode + merge; c5: the interleaved prefix and
+# suffix-row kernel + merge; 'cascade_sparse:overlap' is that kernel alone).
 MEASURED = {
-    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 45.47, "traffic": 197479888, "l2_hit": 0.5255,
-        "sources": FUSED_SRC, "sha256_16": "10a849ea10680d8f", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.56,
-        "sources": FUSED_SRC, "sha256_16": "10a849ea10680d8f", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 102.86, "traffic": 539293828,
-        "sources": DECODE_SRC, "sha256_16": "faa6501929e8bb7e", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
-    ('c3_dense', 'dense', 'bound'): {"kernel_us": 877.0, "traffic": 5143186925, "l2_hit": 0.0083,
-        "sources": DECODE_SRC, "sha256_16": "faa6501929e8bb7e", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
-    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 46.06, "traffic": 271420319,
-        "sources": SCORE_SRC, "sha256_16": "a0ac92e895ca5639", "profile": "profiles/split_pipeline_c4_long.md"},
-    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 86.79, "traffic": 305950889,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "bf765676c5b313e9", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 38.58,
-        "sources": PREFIX_SRC, "sha256_16": "8bfc88bf79cba8de", "profile": "profiles/cascade_prefix_kernel_counters_c5_cascade.md"},
+    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 44.32, "traffic": 197443174, "l2_hit": 0.5255,
+        "sources": FUSED_SRC, "sha256_16": "2491021af04f0c03", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.43,
+        "sources": FUSED_SRC, "sha256_16": "2491021af04f0c03", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 102.74, "traffic": 539300214,
+        "sources": DECODE_SRC, "sha256_16": "5cb339f54a16e0cf", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
+    ('c3_dense', 'dense', 'bound'): {"kernel_us": 875.7, "traffic": 5142984059, "l2_hit": 0.0084,
+        "sources": DECODE_SRC, "sha256_16": "5cb339f54a16e0cf", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
+    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 46.47, "traffic": 271421361,
+        "sources": SCORE_SRC, "sha256_16": "9bfeb31cc939c874", "profile": "profiles/split_pipeline_c4_long.md"},
+    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 72.88, "traffic": 269536134, "l2_hit": 0.4294,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "d27a2a1fad519ae5", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 62.79,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "d27a2a1fad519ae5", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 36.57,
+        "sources": PREFIX_SRC, "sha256_16": "f9c47c1fcd818f58", "profile": "profiles/cascade_c5_cascade.md"},
 }
 
 
@@ -346,8 +349,8 @@ def run_config(config, *, steps, warmup, replicas, path_arg, scorer, dense, grap
         cz = accounting.cascade_step_bytes(lens, case.prefix_len, Hq, Hkv, D, elem, k)
         step_bytes = cz["total"]
         dom_name, dom_bytes = "cascade_sparse_decode", cz["total"]
-        dom_kernel = ("cascade_prefix_kernel (MFMA) + short_row_kernel (suffix scores, top-K, attention and "
-                      "the LSE merge with the prefix partials; one wave per row)")
+        dom_kernel = ("cascade_overlap_kernel (the prefix's workgroups on the matrix cores interleaved with the "
+                      "suffix rows' workgroups: scores, top-K, attention) + merge_kernel (LSE merge)")
         dom_key = (config, "cascade_sparse", scorer)
     else:
         rows = 1 if centroid else 2
@@ -424,10 +427,15 @@ def run_config(config, *, steps, warmup, replicas, path_arg, scorer, dense, grap
         "roofline": roofline,
     }
     if cascade:
-        pf = measured((config, "cascade:prefix", scorer), "kernel_us")
+        # the prefix's products: in their own kernel (split path), or sharing
+        # the interleaved kernel with the suffix rows (one-call step), whose
+        # whole duration then bounds their rate from below
+        shared = path == "cascade_sparse"
+        pf = measured((config, "cascade_sparse:overlap" if shared else "cascade:prefix", scorer), "kernel_us")
         flops = 4 * (B * (Hq // Hkv)) * case.prefix_len * D * Hkv
         res["cascade_prefix_mfma"] = {
-            "kernel": "cascade_prefix_kernel", "flop": flops,
+            "kernel": ("cascade_overlap_kernel (whole launch, suffix rows included)" if shared
+                       else "cascade_prefix_kernel"), "flop": flops,
             "rocprof_avg_launch_ms": None if pf is None else round(pf / 1e3, 5),
             "achieved_tflops": None if pf is None else round(flops / (pf / 1e6) / 1e12, 1),
             "peak_tflops": 2500.0,
