@@ -476,7 +476,14 @@ decode_stream_kernel(
 // shared-prefix partials for the cascade), then normalisation. The partials
 // are loaded without waiting for the row's unit count (every slot the row can
 // own is in bounds), so the merge costs one round of dependent loads.
-template <int D>
+// kBatch: partial slots loaded per round. A cascade row of 512-token prefix
+// splits over a 4096-token prefix has 8 prefix slots and usually one or two
+// suffix segments, so 10 take it in one round (16 loaded 6 unused slots and
+// measured 2.5 us slower on that merge; 12 in between); rows of at most 5
+// slots (units of a short list, or 4 prefix splits and one suffix partial)
+// take the 5-slot instance (10 loaded 5 unused slots: c5's one-call step
+// 71.1 against 67.9 us).
+template <int D, int kBatch>
 __global__ void __launch_bounds__(256) merge_kernel(
     int B, int Hkv, int G, const int* __restrict__ seq_lens, const int* __restrict__ sel_count,
     int k_stride, int chunk, int max_units, const float* __restrict__ part_o,
@@ -484,11 +491,6 @@ __global__ void __launch_bounds__(256) merge_kernel(
     const float* __restrict__ pre_ml, int n_pre, const int* __restrict__ row_slots, int nwaves,
     float* __restrict__ out, float* __restrict__ lse) {
   constexpr int PER = D / 64;
-  // Partial slots loaded per round: a cascade row of 512-token prefix splits
-  // over a 4096-token prefix has 8 prefix slots and usually one or two suffix
-  // segments, so 10 take it in one round (16 loaded 6 unused slots and
-  // measured 2.5 us slower on that merge; 12 in between).
-  constexpr int kBatch = 10;
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Hq = Hkv * G;
@@ -577,6 +579,33 @@ __global__ void __launch_bounds__(256) merge_kernel(
   }
 }
 
+constexpr int kMergeNarrow = 5;
+constexpr int kMergeWide = 10;
+
+hipError_t launch_merge_kernel(const LaunchCommon& c, int max_slots, const int* sel_count, int k, int chunk,
+                               int max_units, Partials part, Partials prefix, int n_prefix, const int* row_slots,
+                               int nwaves, float* out, float* lse, hipStream_t stream) {
+  dim3 mgrid((c.B * c.Hq + 3) / 4);
+  const bool narrow = max_slots <= kMergeNarrow;
+#define QSA_MERGE(DD, NB)                                                                                 \
+  hipLaunchKernelGGL((merge_kernel<DD, NB>), mgrid, dim3(256), 0, stream, c.B, c.Hkv, c.G, c.seq_lens,    \
+                     sel_count, k, chunk, max_units, part.o, part.ml, prefix.o, prefix.ml, n_prefix, row_slots, \
+                     nwaves, out, lse)
+  if (c.D == 128) {
+    if (narrow)
+      QSA_MERGE(128, kMergeNarrow);
+    else
+      QSA_MERGE(128, kMergeWide);
+  } else {
+    if (narrow)
+      QSA_MERGE(64, kMergeNarrow);
+    else
+      QSA_MERGE(64, kMergeWide);
+  }
+#undef QSA_MERGE
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
                            const int* sel_count, int k, float scale_log2, const DecodePlan& plan,
@@ -631,18 +660,11 @@ hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 mgrid((c.B * c.Hq + 3) / 4);
   const int* sc = sel != nullptr ? sel_count : nullptr;
-  if (c.D == 128) {
-    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, stream, c.B, c.Hkv, c.G, c.seq_lens,
-                       sc, k, plan.chunk, plan.max_units, part.o, part.ml, prefix.o, prefix.ml,
-                       n_prefix, plan.stream ? part.row_slots : nullptr, plan.waves, out, lse);
-  } else {
-    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(256), 0, stream, c.B, c.Hkv, c.G, c.seq_lens,
-                       sc, k, plan.chunk, plan.max_units, part.o, part.ml, prefix.o, prefix.ml,
-                       n_prefix, plan.stream ? part.row_slots : nullptr, plan.waves, out, lse);
-  }
-  return hipGetLastError();
+  // (the stream split's rows own a data-dependent number of slots)
+  const int max_slots = plan.stream ? kMergeWide + 1 : plan.max_units + n_prefix;
+  return launch_merge_kernel(c, max_slots, sc, k, plan.chunk, plan.max_units, part, prefix, n_prefix,
+                             plan.stream ? part.row_slots : nullptr, plan.waves, out, lse, stream);
 }
 
 }  // namespace
@@ -650,10 +672,8 @@ hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
 hipError_t launch_merge(const LaunchCommon& c, Partials part, int max_units, int chunk, Partials prefix,
                         int n_prefix, float* out, float* lse, hipStream_t stream) {
   if (c.D != 128) return hipErrorInvalidValue;
-  dim3 mgrid((c.B * c.Hq + 3) / 4);
-  hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, stream, c.B, c.Hkv, c.G, c.seq_lens, nullptr, 0,
-                     chunk, max_units, part.o, part.ml, prefix.o, prefix.ml, n_prefix, nullptr, 0, out, lse);
-  return hipGetLastError();
+  return launch_merge_kernel(c, max_units + n_prefix, nullptr, 0, chunk, max_units, part, prefix, n_prefix, nullptr,
+                             0, out, lse, stream);
 }
 
 hipError_t launch_decode(const LaunchCommon& c, const void* q, const int* sel, const int* sel_count,
