@@ -233,6 +233,42 @@ def test_cascade_prefix_skips_bad_pages(selective):
         assert "page table entry" in msg
 
 
+def test_cascade_sparse_one_call_skips_bad_prefix_pages():
+    """The one-call selective cascade (prefix and suffix-row workgroups in one
+    grid, then the merge) with out-of-range prefix page ids: those pages are
+    skipped (the oracle's cascade without them, on the GPU's own selection),
+    and checked mode reports them."""
+    prefix_len, suffix_len, k = 1000, 200, 5               # 63 prefix pages, 13 suffix pages
+    c = workloads.cascade_case("cas_bad1", 6, 8, 2, 128, prefix_len, suffix_len, "bf16", 47, n_sentinel=3)
+    print("[case] one-call selective cascade with bad prefix pages", flush=True)
+    d = case_np(c)
+    g = c.to(DEV)
+    kv = qsa.PagedKV.from_case(g)
+    P = c.num_phys_pages
+    pre = d["prefix_pages"]
+    n_pre = O.num_pages(prefix_len)
+    meta = qsa.build_page_meta(kv)
+    for bad_idx in ([5], list(range(40, n_pre))):
+        print(f"[case] bad prefix pages {bad_idx[0]}..{bad_idx[-1]}", flush=True)
+        bad_pre = g.prefix_pages.clone()
+        for i in bad_idx:
+            bad_pre[i] = P + 2 if i % 2 else -1
+        sel = torch.empty(c.B, c.Hkv, k, dtype=torch.int32, device=DEV)
+        cnt = torch.empty(c.B, c.Hkv, dtype=torch.int32, device=DEV)
+        out, lse = qsa.cascade_sparse_decode(g.q, bad_pre, prefix_len, kv, meta.clone(), k, sm_scale=c.sm_scale,
+                                             sel=sel, sel_count=cnt)
+        torch.cuda.synchronize()
+        keep = [int(pre[i]) for i in range(n_pre) if i not in bad_idx]
+        removed = sum(O.valid_tokens(prefix_len, i) for i in bad_idx)
+        oo, ol = O.cascade_decode(d["q"], d["k_pool"], d["v_pool"], "bf16", np.array(keep, dtype=np.int32),
+                                  prefix_len - removed, d["page_indptr"], d["page_indices"], d["seq_lens"],
+                                  c.sm_scale, sel=sel.cpu().numpy(), sel_count=cnt.cpu().numpy())
+        assert_close_out(out.cpu().numpy(), lse.cpu().numpy(), oo, ol)
+        msg = _checked_error(lambda: qsa.cascade_sparse_decode(g.q, bad_pre, prefix_len, kv, meta.clone(), k,
+                                                               sm_scale=c.sm_scale))
+        assert "page table entry" in msg
+
+
 def test_meta_build_and_tail_refresh_skip_bad_ids():
     lens = [1000, 1537, 33]
     c = _case("meta_bad", lens, 8, 2, "bf16", seed=47)
