@@ -60,20 +60,20 @@ PREFIX_SRC = ["cascade.hip", "cascade_prefix.h", "qsa_device.h", "qsa_internal.h
 # (c2 dense and c3: split-K decode + merge; c5: the interleaved prefix and
 # suffix-row kernel + merge; 'cascade_sparse:overlap' is that kernel alone).
 MEASURED = {
-    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 44.32, "traffic": 197443174, "l2_hit": 0.5255,
+    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 44.84, "traffic": 197437909, "l2_hit": 0.5258,
         "sources": FUSED_SRC, "sha256_16": "2491021af04f0c03", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.43,
+    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.00,
         "sources": FUSED_SRC, "sha256_16": "2491021af04f0c03", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 102.74, "traffic": 539300214,
-        "sources": DECODE_SRC, "sha256_16": "5cb339f54a16e0cf", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
-    ('c3_dense', 'dense', 'bound'): {"kernel_us": 875.7, "traffic": 5142984059, "l2_hit": 0.0084,
-        "sources": DECODE_SRC, "sha256_16": "5cb339f54a16e0cf", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
-    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 46.47, "traffic": 271421361,
+    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 102.25, "traffic": 539257047,
+        "sources": DECODE_SRC, "sha256_16": "1a419d764862d998", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
+    ('c3_dense', 'dense', 'bound'): {"kernel_us": 874.39, "traffic": 5142956248, "l2_hit": 0.0083,
+        "sources": DECODE_SRC, "sha256_16": "1a419d764862d998", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
+    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 46.22, "traffic": 271421128,
         "sources": SCORE_SRC, "sha256_16": "9bfeb31cc939c874", "profile": "profiles/split_pipeline_c4_long.md"},
-    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 72.88, "traffic": 269536134, "l2_hit": 0.4294,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "d27a2a1fad519ae5", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 62.79,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "d27a2a1fad519ae5", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 69.85, "traffic": 269410928, "l2_hit": 0.4265,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "c8516abc57e5ebf1", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 62.17,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "c8516abc57e5ebf1", "profile": "profiles/cascade_c5_cascade.md"},
     ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 36.57,
         "sources": PREFIX_SRC, "sha256_16": "f9c47c1fcd818f58", "profile": "profiles/cascade_c5_cascade.md"},
 }
