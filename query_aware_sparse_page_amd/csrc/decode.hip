@@ -579,14 +579,144 @@ __global__ void __launch_bounds__(256) merge_kernel(
   }
 }
 
+// The same merge with one wave per (b, h_kv) row for all G query heads of its
+// group. A slot's partials of the group's heads are contiguous (G D floats;
+// so are the group's outputs), so lane l merges the E = G D / 64
+// consecutive floats at l E (of head l / (64 / G)) with 16-byte loads and
+// stores: a quarter of the waves and of the load instructions of the kernel
+// above, and per head the same arithmetic in the same order.
+template <int D, int G, int kBatch>
+__global__ void __launch_bounds__(256) merge_group_kernel(
+    int B, int Hkv, const int* __restrict__ seq_lens, const int* __restrict__ sel_count, int k_stride, int chunk,
+    int max_units, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const float* __restrict__ pre_o, const float* __restrict__ pre_ml, int n_pre,
+    const int* __restrict__ row_slots, int nwaves, float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int E = G * D / 64;  // floats per lane
+  constexpr int LPH = 64 / G;    // lanes per head
+  static_assert(E % 4 == 0 && LPH * E == D, "16-byte pieces within one head");
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (gw >= B * Hkv) return;
+  const int b = gw / Hkv;
+  const int h = gw - b * Hkv;
+  const int hh = lane / LPH;
+  const int off = lane * E;  // = hh D + (lane % LPH) E
+  const size_t row = (size_t)gw;
+  const int Hq = Hkv * G;
+  const int L = seq_lens[b];
+  const int cnt_sel = sel_count != nullptr ? sel_count[row] : 0;
+  int ubase = (int)(row * max_units), ucap = max_units, units = -1;
+  if (row_slots != nullptr) {
+    const int f = min(max(row_slots[2 * row], 0), nwaves - 1);
+    const int l = min(max(row_slots[2 * row + 1], f), nwaves - 1);
+    ubase = f + (int)row;
+    ucap = l - f + 1;
+    units = ucap;
+  }
+  const int slots = ucap + n_pre;
+
+  float M = -__builtin_inff(), lsum = 0.0f;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  for (int base = 0; base < slots; base += kBatch) {
+    float m[kBatch], l[kBatch];
+    float4 v[kBatch][E / 4];
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int i = min(base + t, slots - 1);
+      const float* po;
+      const float* pml;
+      if (i < ucap) {
+        const size_t un = (size_t)ubase + i;
+        po = part_o + un * G * D + off;
+        pml = part_ml + (un * G + hh) * 2;
+      } else {
+        const size_t pr = ((size_t)h * n_pre + (i - ucap)) * ((size_t)B * G) + (size_t)b * G;
+        po = pre_o + pr * D + off;
+        pml = pre_ml + (pr + hh) * 2;
+      }
+      const float2 ml = *reinterpret_cast<const float2*>(pml);
+      m[t] = ml.x;
+      l[t] = ml.y;
+#pragma unroll
+      for (int e = 0; e < E / 4; ++e) v[t][e] = reinterpret_cast<const float4*>(po)[e];
+    }
+    if (units < 0) {
+      const int n = L > 0 ? (L + kPage - 1) / kPage : 0;
+      int count = n;
+      if (sel_count != nullptr) {
+        count = cnt_sel < k_stride ? cnt_sel : k_stride;
+        count = count < n ? count : n;
+        count = count > 0 ? count : 0;
+      }
+      units = (count + chunk - 1) / chunk;
+      units = units < max_units ? units : max_units;
+    }
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int i = base + t;
+      // slots past the row's units (and past the list) hold stale values
+      const bool use = i < slots && (i < units || i >= ucap);
+      if (!use || m[t] == -__builtin_inff()) continue;
+      if (m[t] > M) {
+        const float a = (M == -__builtin_inff()) ? 0.0f : fast_exp2(M - m[t]);
+        lsum *= a;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] *= a;
+        M = m[t];
+      }
+      const float w = fast_exp2(m[t] - M);
+      lsum = __builtin_fmaf(w, l[t], lsum);
+#pragma unroll
+      for (int e = 0; e < E / 4; ++e) {
+        acc[4 * e + 0] = __builtin_fmaf(w, v[t][e].x, acc[4 * e + 0]);
+        acc[4 * e + 1] = __builtin_fmaf(w, v[t][e].y, acc[4 * e + 1]);
+        acc[4 * e + 2] = __builtin_fmaf(w, v[t][e].z, acc[4 * e + 2]);
+        acc[4 * e + 3] = __builtin_fmaf(w, v[t][e].w, acc[4 * e + 3]);
+      }
+    }
+  }
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  float4* o4 = reinterpret_cast<float4*>(out + ((size_t)b * Hq + (size_t)h * G) * D + off);
+#pragma unroll
+  for (int e = 0; e < E / 4; ++e)
+    o4[e] = make_float4(acc[4 * e] * inv, acc[4 * e + 1] * inv, acc[4 * e + 2] * inv, acc[4 * e + 3] * inv);
+  if (lse != nullptr && lane % LPH == 0) {
+    lse[(size_t)b * Hq + h * G + hh] = lsum > 0.0f ? (M + __log2f(lsum)) * 0.69314718055994530942f : -__builtin_inff();
+  }
+}
+
 constexpr int kMergeNarrow = 5;
 constexpr int kMergeWide = 10;
 
 hipError_t launch_merge_kernel(const LaunchCommon& c, int max_slots, const int* sel_count, int k, int chunk,
                                int max_units, Partials part, Partials prefix, int n_prefix, const int* row_slots,
                                int nwaves, float* out, float* lse, hipStream_t stream) {
-  dim3 mgrid((c.B * c.Hq + 3) / 4);
   const bool narrow = max_slots <= kMergeNarrow;
+  // (the group kernel's 16-byte accesses need 16-byte aligned partials and
+  // output; workspace regions are, a caller's output normally is)
+  const uintptr_t al = reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(part.o) |
+                       reinterpret_cast<uintptr_t>(part.ml) | reinterpret_cast<uintptr_t>(prefix.o) |
+                       reinterpret_cast<uintptr_t>(prefix.ml);
+  if (c.D == 128 && (c.G == 4 || c.G == 8) && al % 16 == 0) {
+    dim3 ggrid((c.B * c.Hkv + 3) / 4);
+#define QSA_MERGE_G(GG, NB)                                                                                  \
+  hipLaunchKernelGGL((merge_group_kernel<128, GG, NB>), ggrid, dim3(256), 0, stream, c.B, c.Hkv, c.seq_lens, \
+                     sel_count, k, chunk, max_units, part.o, part.ml, prefix.o, prefix.ml, n_prefix, row_slots,  \
+                     nwaves, out, lse)
+    if (c.G == 4) {
+      if (narrow)
+        QSA_MERGE_G(4, kMergeNarrow);
+      else
+        QSA_MERGE_G(4, kMergeWide);
+    } else {
+      QSA_MERGE_G(8, kMergeNarrow);  // (16 floats per lane and slot: the narrow batch)
+    }
+#undef QSA_MERGE_G
+    return hipGetLastError();
+  }
+  dim3 mgrid((c.B * c.Hq + 3) / 4);
 #define QSA_MERGE(DD, NB)                                                                                 \
   hipLaunchKernelGGL((merge_kernel<DD, NB>), mgrid, dim3(256), 0, stream, c.B, c.Hkv, c.G, c.seq_lens,    \
                      sel_count, k, chunk, max_units, part.o, part.ml, prefix.o, prefix.ml, n_prefix, row_slots, \

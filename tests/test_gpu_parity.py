@@ -210,6 +210,30 @@ def test_decode_dense_and_sparse(label, lens, Hq, Hkv, dtype, k):
     assert_close_out(out2.cpu().numpy(), lse2.cpu().numpy(), so, sl)
 
 
+@pytest.mark.parametrize("label,lens,Hq,Hkv,dtype,k", SMALL[:2])
+def test_group_merge_equals_per_head_merge(label, lens, Hq, Hkv, dtype, k):
+    """Groups of 4 and 8 heads (D 128) merge one (b, h_kv) row per wave with
+    16-byte accesses; an output that is not 16-byte aligned takes the merge
+    with one wave per (b, h_q). Both do the same arithmetic per head, so the
+    outputs are bitwise equal (dense, and sparse on a partial selection)."""
+    c = _case(label, lens, Hq, Hkv, dtype)
+    g, kv = _kv(c)
+    n = c.B * Hq * 128
+    raw_o = torch.empty(n + 4, dtype=torch.float32, device=DEV)
+    raw_l = torch.empty(c.B * Hq + 4, dtype=torch.float32, device=DEV)
+    o_mis = raw_o[1:n + 1].view(c.B, Hq, 128)
+    l_mis = raw_l[1:c.B * Hq + 1].view(c.B, Hq)
+    assert o_mis.data_ptr() % 16 != 0
+    meta = qsa.build_page_meta(kv)
+    gs, _ = qsa.score_pages(g.q, kv, meta)
+    sel, cnt, _ = qsa.topk_pages(gs, kv, k, num_q_heads=Hq)
+    for kw in ({}, {"sel": sel, "sel_count": cnt}):
+        ref = qsa.paged_decode(g.q, kv, sm_scale=c.sm_scale, **kw)
+        mis = qsa.paged_decode(g.q, kv, sm_scale=c.sm_scale, out=(o_mis, l_mis), **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(ref[0], mis[0]) and torch.equal(ref[1], mis[1])
+
+
 @pytest.mark.parametrize("label,lens,Hq,Hkv,dtype,k", SMALL[:4])
 def test_all_pages_selected_is_bitwise_dense(label, lens, Hq, Hkv, dtype, k):
     c = _case(label, lens, Hq, Hkv, dtype)
