@@ -39,24 +39,26 @@ constexpr bool use_mfma() {
   return IsBf16<T>::value && G >= 4;
 }
 
-template <typename T, int G, bool kMfma = use_mfma<T, G>()>
+template <typename T, int G, int kW, bool kMfma = use_mfma<T, G>()>
 struct DecodeShared {
   static constexpr int D = WaveAttn<T, G>::D;
-  float p[4][WaveAttn<T, G>::kPBufFloats];  // per wave, double-buffered page probabilities
-  float o[4][G][D];                         // per-wave results for the workgroup combine
-  float ml[4][G][2];
+  float p[kW][WaveAttn<T, G>::kPBufFloats];  // per wave, double-buffered page probabilities
+  float o[kW][G][D];                         // per-wave results for the workgroup combine
+  float ml[kW][G][2];
   uint4 q[WaveAttn<T, G>::kQInLds ? G * kRowBytes / 16 : 1];  // the group's query rows
 };
-template <typename T, int G>
-struct DecodeShared<T, G, true> {
+template <typename T, int G, int kW>
+struct DecodeShared<T, G, kW, true> {
   static constexpr int D = WaveAttnMfma<G>::D;
-  alignas(16) char v[4][WaveAttnMfma<G>::kLdsBytes];  // per wave, the staged V tiles
-  alignas(16) float o[4][G][D];
-  float ml[4][G][2];
+  alignas(16) char v[kW][WaveAttnMfma<G>::kLdsBytes];  // per wave, the staged V tiles
+  alignas(16) float o[kW][G][D];
+  float ml[kW][G][2];
 };
 
-template <typename T, int G>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+constexpr int kSplitWaves = 4;  // waves per unit workgroup of the split decode
+
+template <typename T, int G, int kW>
+__global__ void __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(2)))
 decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ k_pool, const T* __restrict__ v_pool,
     int num_phys, int Hkv, const int* __restrict__ page_indptr,
@@ -68,7 +70,7 @@ decode_split_kernel(
   constexpr int EPC = WA::EPC;
   constexpr int D = WA::D;
   constexpr bool kMfma = use_mfma<T, G>();
-  __shared__ DecodeShared<T, G> sh;
+  __shared__ DecodeShared<T, G, kW> sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,9 +86,9 @@ decode_split_kernel(
   const int L = seq_lens[b];
   const int cnt_sel = sel != nullptr ? sel_count[row] : 0;
   const int tbase = page_indptr[b];
-  const int idx = ubeg + wave + 4 * lane;
+  const int idx = ubeg + wave + kW * lane;
   int jsel = idx;
-  if (sel != nullptr && lane < (chunk >> 2) && idx < k_stride) jsel = sel[row * k_stride + idx];
+  if (sel != nullptr && lane < (chunk + kW - 1) / kW && idx < k_stride) jsel = sel[row * k_stride + idx];
   const int n = L > 0 ? (L + kPage - 1) / kPage : 0;
   int count = n;
   if (sel != nullptr) {
@@ -100,7 +102,7 @@ decode_split_kernel(
   units = units < 1 ? 1 : (units < max_units ? units : max_units);
   if (u >= units) return;  // whole workgroup: nothing in this unit
   const int uend = min(ubeg + chunk, count);
-  const int npw = (uend - ubeg > wave) ? (uend - ubeg - wave + 3) / 4 : 0;
+  const int npw = (uend - ubeg > wave) ? (uend - ubeg - wave + kW - 1) / kW : 0;
 
   // This wave's pages: physical slot and valid-token count, one per lane.
   int my_p = 0, my_valid = 0;
@@ -152,19 +154,19 @@ decode_split_kernel(
       sh.ml[wave][lane][1] = lw;
     }
   }
-  // ---- the workgroup combine of the 4 waves -> one partial per (unit, head)
+  // ---- the workgroup combine of the kW waves -> one partial per (unit, head)
   __syncthreads();
 
   const size_t unit = row * (size_t)max_units + u;
-  for (int idx2 = tid; idx2 < G * D; idx2 += 256) {
+  for (int idx2 = tid; idx2 < G * D; idx2 += 64 * kW) {
     const int hh = idx2 / D;
     const int d = idx2 - hh * D;
     float M = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sh.ml[w][hh][0]);
+    for (int w = 0; w < kW; ++w) M = fmaxf(M, sh.ml[w][hh][0]);
     float acc = 0.0f, lsum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kW; ++w) {
       const float mw2 = sh.ml[w][hh][0];
       const float sc = (mw2 == -__builtin_inff()) ? 0.0f : fast_exp2(mw2 - M);
       acc += sh.o[w][hh][d] * sc;
@@ -773,8 +775,8 @@ hipError_t launch_decode_t(const LaunchCommon& c, const void* q, const int* sel,
   if (!plan.stream) {
 #define QSA_DECODE_CASE(GG)                                                                     \
   case GG:                                                                                      \
-    hipLaunchKernelGGL((decode_split_kernel<T, GG>), grid, dim3(256), 0, stream, qq, kk, vv,    \
-                       c.num_phys, c.Hkv, c.page_indptr, c.page_indices, c.seq_lens, sel,       \
+    hipLaunchKernelGGL((decode_split_kernel<T, GG, kSplitWaves>), grid, dim3(64 * kSplitWaves), 0, stream, qq, \
+                       kk, vv, c.num_phys, c.Hkv, c.page_indptr, c.page_indices, c.seq_lens, sel, \
                        sel_count, k, scale_log2, plan.chunk, plan.max_units, part.o, part.ml,  \
                        c.err);                                                                 \
     break;
