@@ -60,21 +60,21 @@ PREFIX_SRC = ["cascade.hip", "cascade_prefix.h", "qsa_device.h", "qsa_internal.h
 # (c2 dense and c3: split-K decode + merge; c5: the interleaved prefix and
 # suffix-row kernel + merge; 'cascade_sparse:overlap' is that kernel alone).
 MEASURED = {
-    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 44.84, "traffic": 197437909, "l2_hit": 0.5258,
+    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 44.63, "traffic": 197410071, "l2_hit": 0.5258,
         "sources": FUSED_SRC, "sha256_16": "2491021af04f0c03", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.00,
+    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.11,
         "sources": FUSED_SRC, "sha256_16": "2491021af04f0c03", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 102.25, "traffic": 539257047,
-        "sources": DECODE_SRC, "sha256_16": "1a419d764862d998", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
-    ('c3_dense', 'dense', 'bound'): {"kernel_us": 874.39, "traffic": 5142956248, "l2_hit": 0.0083,
-        "sources": DECODE_SRC, "sha256_16": "1a419d764862d998", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
-    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 46.22, "traffic": 271421128,
+    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 102.69, "traffic": 539262401,
+        "sources": DECODE_SRC, "sha256_16": "2b21a1989df7d86f", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
+    ('c3_dense', 'dense', 'bound'): {"kernel_us": 874.38, "traffic": 5142973645, "l2_hit": 0.0084,
+        "sources": DECODE_SRC, "sha256_16": "2b21a1989df7d86f", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
+    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 45.99, "traffic": 271419785,
         "sources": SCORE_SRC, "sha256_16": "9bfeb31cc939c874", "profile": "profiles/split_pipeline_c4_long.md"},
-    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 69.85, "traffic": 269410928, "l2_hit": 0.4265,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "c8516abc57e5ebf1", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 62.17,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "c8516abc57e5ebf1", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 36.57,
+    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 69.93, "traffic": 269718370, "l2_hit": 0.4268,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "aa7313a9788f1724", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 63.22,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "aa7313a9788f1724", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 36.69,
         "sources": PREFIX_SRC, "sha256_16": "f9c47c1fcd818f58", "profile": "profiles/cascade_c5_cascade.md"},
 }
 
@@ -350,7 +350,7 @@ def run_config(config, *, steps, warmup, replicas, path_arg, scorer, dense, grap
         step_bytes = cz["total"]
         dom_name, dom_bytes = "cascade_sparse_decode", cz["total"]
         dom_kernel = ("cascade_overlap_kernel (the prefix's workgroups on the matrix cores interleaved with the "
-                      "suffix rows' workgroups: scores, top-K, attention) + merge_kernel (LSE merge)")
+                      "suffix rows' workgroups: scores, top-K, attention) + merge_group_kernel (LSE merge)")
         dom_key = (config, "cascade_sparse", scorer)
     else:
         rows = 1 if centroid else 2

@@ -210,13 +210,21 @@ def test_decode_dense_and_sparse(label, lens, Hq, Hkv, dtype, k):
     assert_close_out(out2.cpu().numpy(), lse2.cpu().numpy(), so, sl)
 
 
-@pytest.mark.parametrize("label,lens,Hq,Hkv,dtype,k", SMALL[:2])
-def test_group_merge_equals_per_head_merge(label, lens, Hq, Hkv, dtype, k):
-    """Groups of 4 and 8 heads (D 128) merge one (b, h_kv) row per wave with
-    16-byte accesses; an output that is not 16-byte aligned takes the merge
-    with one wave per (b, h_q). Both do the same arithmetic per head, so the
-    outputs are bitwise equal (dense, and sparse on a partial selection)."""
-    c = _case(label, lens, Hq, Hkv, dtype)
+# 128 sequences x 8 KV heads: 1024 rows, enough for the merge with one wave
+# per (b, h_kv) row; ragged lengths of 1 to 40 pages
+MANY_ROWS = [37 + (i * 97) % 600 for i in range(128)]
+
+
+@pytest.mark.parametrize("Hq,k", [(32, 9), (64, 5)])
+def test_group_merge_equals_per_head_merge(Hq, k):
+    """With at least 1024 (b, h_kv) rows, groups of 4 and 8 heads (D 128)
+    merge one row per wave with 16-byte accesses; an output that is not
+    16-byte aligned takes the merge with one wave per (b, h_q). Both do the
+    same arithmetic per head, so the outputs are bitwise equal (dense, and
+    sparse on a partial selection), and both match the oracle."""
+    Hkv = 8
+    c = _case(f"many_rows_g{Hq // Hkv}", MANY_ROWS, Hq, Hkv, "bf16", seed=23)
+    d = case_np(c)
     g, kv = _kv(c)
     n = c.B * Hq * 128
     raw_o = torch.empty(n + 4, dtype=torch.float32, device=DEV)
@@ -232,6 +240,11 @@ def test_group_merge_equals_per_head_merge(label, lens, Hq, Hkv, dtype, k):
         mis = qsa.paged_decode(g.q, kv, sm_scale=c.sm_scale, out=(o_mis, l_mis), **kw)
         torch.cuda.synchronize()
         assert torch.equal(ref[0], mis[0]) and torch.equal(ref[1], mis[1])
+        osel = kw["sel"].cpu().numpy() if kw else None
+        ocnt = kw["sel_count"].cpu().numpy() if kw else None
+        oo, ol = O.paged_decode(d["q"], d["k_pool"], d["v_pool"], "bf16", d["page_indptr"], d["page_indices"],
+                                d["seq_lens"], c.sm_scale, sel=osel, sel_count=ocnt)
+        assert_close_out(ref[0].cpu().numpy(), ref[1].cpu().numpy(), oo, ol)
 
 
 @pytest.mark.parametrize("label,lens,Hq,Hkv,dtype,k", SMALL[:4])
