@@ -128,7 +128,7 @@ __device__ __forceinline__ void prefix_block(
   // all of them), so the page and its tile address are wave-uniform.
   auto page_of = [&](int bi, int pg) -> int {  // physical page, -1 if out of range
     const int i = min(2 * min(bi, last_blk) + pg, last_pg);  // < kMaxSplitPages <= 128
-    return i < 64 ? __builtin_amdgcn_readlane(pgr[0], i) : __builtin_amdgcn_readlane(pgr[1], i - 64);
+    return __builtin_amdgcn_readlane(i < 64 ? pgr[0] : pgr[1], i & 63);  // (a select, not a branch)
   };
   // pv: the staged page of each chunk, kept for stage() (-1: staged as zeros)
   auto issue = [&](int bi, uint4 (&kr)[kStageReps], uint4 (&vr)[kStageReps], int (&pv)[kStageReps]) {
@@ -140,15 +140,26 @@ __device__ __forceinline__ void prefix_block(
       vr[rep] = ld16(vbase + poff + toff);
     }
   };
+  // (a block whose keys are all in the split, on a page in range, is staged
+  // as loaded behind a wave-uniform test; otherwise the zeros come from a
+  // per-lane mask, without a divergent branch)
   auto stage = [&](int bi, int buf, const uint4 (&kr)[kStageReps], const uint4 (&vr)[kStageReps],
                    const int (&pv)[kStageReps]) {
 #pragma unroll
     for (int rep = 0; rep < kStageReps; ++rep) {
       const int idx = tid + kThreads * rep;
       const int key = idx >> 4;
-      const bool ok = bi < nblk && kbeg + bi * kKeyBlock + key < kend && pv[rep] >= 0;
-      *reinterpret_cast<uint4*>(&sh.k[buf][key][(idx & 15) * 8]) = ok ? kr[rep] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&sh.v[buf][key][(idx & 15) * 8]) = ok ? vr[rep] : make_uint4(0, 0, 0, 0);
+      uint4* kd = reinterpret_cast<uint4*>(&sh.k[buf][key][(idx & 15) * 8]);
+      uint4* vd = reinterpret_cast<uint4*>(&sh.v[buf][key][(idx & 15) * 8]);
+      if (bi < nblk && kbeg + (bi + 1) * kKeyBlock <= kend && pv[rep] >= 0) {
+        *kd = kr[rep];
+        *vd = vr[rep];
+      } else {
+        const bool ok = bi < nblk && kbeg + bi * kKeyBlock + key < kend && pv[rep] >= 0;
+        const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+        *kd = make_uint4(kr[rep].x & m, kr[rep].y & m, kr[rep].z & m, kr[rep].w & m);
+        *vd = make_uint4(vr[rep].x & m, vr[rep].y & m, vr[rep].z & m, vr[rep].w & m);
+      }
     }
   };
 
