@@ -179,8 +179,9 @@ __device__ __forceinline__ void prefix_block(
     l_run[qt] = 0.0f;
   }
 
-  // Attention over the block staged in LDS buffer buf (keys from kb).
-  auto compute = [&](int kb, int buf) {
+  // Attention over the block staged in LDS buffer buf (keys from kb);
+  // after_s runs once the S^T products are issued.
+  auto compute = [&](int kb, int buf, auto&& after_s) {
     // ---- S^T tiles: keys kb + 16 kt + c16 (A rows), dims 8g + 32 ks
     f32x4_t sacc[2][kQT];
 #pragma unroll
@@ -200,6 +201,7 @@ __device__ __forceinline__ void prefix_block(
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) sacc[kt][qt] = mfma16(a[kt], qb[qt][ks], sacc[kt][qt]);
     }
+    after_s();
     // ---- online softmax over this block, per query column c16 of each tile
     // (only a split's last block can hold keys past its end; a key tile on
     // a page out of range, staged as zeros, is masked like keys past the end)
@@ -301,8 +303,13 @@ __device__ __forceinline__ void prefix_block(
         // slot r held block bi, staged in the previous step: reload it with bi + kDepth
         issue(bi + kDepth, kr[r], vr[r], pv[r]);
         __builtin_amdgcn_sched_barrier(0);
-        compute(kbeg + bi * kKeyBlock, bi & 1);
-        stage(bi + 1, (bi + 1) & 1, kr[(r + 1) % kDepth], vr[(r + 1) % kDepth], pv[(r + 1) % kDepth]);
+        // the next block goes to the other LDS buffer (free since the last
+        // barrier) while this block's products and softmax run, so its
+        // writes have completed by the barrier; its loads were issued a step
+        // earlier and have arrived
+        compute(kbeg + bi * kKeyBlock, bi & 1, [&]() {
+          stage(bi + 1, (bi + 1) & 1, kr[(r + 1) % kDepth], vr[(r + 1) % kDepth], pv[(r + 1) % kDepth]);
+        });
         __syncthreads();
         ++bi;
       }
