@@ -60,22 +60,22 @@ PREFIX_SRC = ["cascade.hip", "cascade_prefix.h", "qsa_device.h", "qsa_internal.h
 # (c2 dense and c3: split-K decode + merge; c5: the interleaved prefix and
 # suffix-row kernel + merge; 'cascade_sparse:overlap' is that kernel alone).
 MEASURED = {
-    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 44.63, "traffic": 197410071, "l2_hit": 0.5258,
+    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 44.88, "traffic": 197796997, "l2_hit": 0.5246,
         "sources": FUSED_SRC, "sha256_16": "2491021af04f0c03", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.11,
+    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.37,
         "sources": FUSED_SRC, "sha256_16": "2491021af04f0c03", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 102.69, "traffic": 539262401,
+    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 102.60, "traffic": 539260656,
         "sources": DECODE_SRC, "sha256_16": "2b21a1989df7d86f", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
-    ('c3_dense', 'dense', 'bound'): {"kernel_us": 874.38, "traffic": 5142973645, "l2_hit": 0.0084,
+    ('c3_dense', 'dense', 'bound'): {"kernel_us": 869.70, "traffic": 5142978084, "l2_hit": 0.0084,
         "sources": DECODE_SRC, "sha256_16": "2b21a1989df7d86f", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
-    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 45.99, "traffic": 271419785,
+    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 46.02, "traffic": 271420504,
         "sources": SCORE_SRC, "sha256_16": "9bfeb31cc939c874", "profile": "profiles/split_pipeline_c4_long.md"},
-    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 69.93, "traffic": 269718370, "l2_hit": 0.4268,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "aa7313a9788f1724", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 63.22,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "aa7313a9788f1724", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 36.69,
-        "sources": PREFIX_SRC, "sha256_16": "f9c47c1fcd818f58", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 68.45, "traffic": 269738606, "l2_hit": 0.4350,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "6e05e6ac9d1db11a", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 61.64,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "6e05e6ac9d1db11a", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 35.38,
+        "sources": PREFIX_SRC, "sha256_16": "9595ec4038e0df07", "profile": "profiles/cascade_c5_cascade.md"},
 }
 
 
