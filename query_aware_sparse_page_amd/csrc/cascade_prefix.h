@@ -52,7 +52,6 @@ __device__ __forceinline__ void prefix_block(
     const int* __restrict__ prefix_pages, int prefix_len, int split_tokens, int n_splits,
     float scale_log2, float* __restrict__ pre_o, float* __restrict__ pre_ml,
     unsigned int* __restrict__ err) {
-  constexpr int kWaves = PrefixCfg<W>::kWaves;
   constexpr int kThreads = PrefixCfg<W>::kThreads;
   constexpr int kRowsPerWG = PrefixCfg<W>::kRowsPerWG;
   constexpr int kStageReps = PrefixCfg<W>::kStageReps;
