@@ -70,12 +70,12 @@ MEASURED = {
         "sources": DECODE_SRC, "sha256_16": "2b21a1989df7d86f", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
     ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 46.02, "traffic": 271420504,
         "sources": SCORE_SRC, "sha256_16": "9bfeb31cc939c874", "profile": "profiles/split_pipeline_c4_long.md"},
-    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 68.45, "traffic": 269738606, "l2_hit": 0.4350,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "6e05e6ac9d1db11a", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 61.64,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "6e05e6ac9d1db11a", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 35.38,
-        "sources": PREFIX_SRC, "sha256_16": "9595ec4038e0df07", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 68.57, "traffic": 269745511, "l2_hit": 0.4347,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "7420822c9dd17ba9", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 61.66,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "7420822c9dd17ba9", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 35.58,
+        "sources": PREFIX_SRC, "sha256_16": "c8b81d062c5405c7", "profile": "profiles/cascade_c5_cascade.md"},
 }
 
 
