@@ -107,16 +107,16 @@ qsa::LaunchCommon common(const qsa_dims* d, const qsa_paged_kv* kv) {
 
 // Compute units of the current device (queried once per device).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];  // per device, 0 until first asked (threads may ask at once)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
       v = 256;
-    cus[dev] = v;
+    cus[dev].store(v, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return v;
 }
 
 // 4-wave workgroups that run at once: two per CU (two waves per SIMD).
