@@ -64,16 +64,16 @@ MEASURED = {
         "sources": FUSED_SRC, "sha256_16": "2491021af04f0c03", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
     ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.37,
         "sources": FUSED_SRC, "sha256_16": "2491021af04f0c03", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 102.60, "traffic": 539260656,
-        "sources": DECODE_SRC, "sha256_16": "2b21a1989df7d86f", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
-    ('c3_dense', 'dense', 'bound'): {"kernel_us": 869.70, "traffic": 5142978084, "l2_hit": 0.0084,
-        "sources": DECODE_SRC, "sha256_16": "2b21a1989df7d86f", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
+    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 102.30, "traffic": 539256898,
+        "sources": DECODE_SRC, "sha256_16": "ccf7c53faa7fde30", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
+    ('c3_dense', 'dense', 'bound'): {"kernel_us": 872.94, "traffic": 5142990414, "l2_hit": 0.0083,
+        "sources": DECODE_SRC, "sha256_16": "ccf7c53faa7fde30", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
     ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 46.02, "traffic": 271420504,
         "sources": SCORE_SRC, "sha256_16": "9bfeb31cc939c874", "profile": "profiles/split_pipeline_c4_long.md"},
-    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 68.57, "traffic": 269745511, "l2_hit": 0.4347,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "7420822c9dd17ba9", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 61.66,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "7420822c9dd17ba9", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 69.29, "traffic": 269741809, "l2_hit": 0.4351,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "b95152a302128f76", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 62.41,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "b95152a302128f76", "profile": "profiles/cascade_c5_cascade.md"},
     ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 35.58,
         "sources": PREFIX_SRC, "sha256_16": "c8b81d062c5405c7", "profile": "profiles/cascade_c5_cascade.md"},
 }
