@@ -114,6 +114,7 @@ def test_short_rows_fused_matches_oracle_and_split(label, lens, Hq, Hkv, k):
     (1000, 1200, 3, 8, 2, 9),                                  # 75-page suffix rows: the split fallback
     (16, 40, 128, 32, 8, 2),                                   # a one-page prefix, 1024 suffix rows
     (9000, 64, 64, 32, 8, 3),                                  # a long prefix (18 splits), ragged last split
+    (300, 100, 1, 64, 8, 3),                                   # one sequence, groups of 8: fewer workgroups than XCDs
 ])
 def test_cascade_sparse_decode_matches_oracle(prefix_len, suffix_len, B, Hq, Hkv, k):
     c = workloads.cascade_case("cas_sparse", B, Hq, Hkv, 128, prefix_len, suffix_len, "bf16", 89, n_sentinel=3)
