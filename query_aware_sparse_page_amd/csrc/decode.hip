@@ -38,6 +38,10 @@ template <typename T, int G>
 constexpr bool use_mfma() {
   return IsBf16<T>::value && G >= 4;
 }
+// The matrix-core page loop of the split and stream kernels, whose K/V tiles
+// are read with the non-temporal hint (ld16_stream).
+template <int G>
+using DecodeMfma = WaveAttnMfma<G, 2, true>;
 
 template <typename T, int G, int kW, bool kMfma = use_mfma<T, G>()>
 struct DecodeShared {
@@ -49,8 +53,8 @@ struct DecodeShared {
 };
 template <typename T, int G, int kW>
 struct DecodeShared<T, G, kW, true> {
-  static constexpr int D = WaveAttnMfma<G>::D;
-  alignas(16) char v[kW][WaveAttnMfma<G>::kLdsBytes];  // per wave, the staged V tiles
+  static constexpr int D = DecodeMfma<G>::D;
+  alignas(16) char v[kW][DecodeMfma<G>::kLdsBytes];  // per wave, the staged V tiles
   alignas(16) float o[kW][G][D];
   float ml[kW][G][2];
 };
@@ -127,7 +131,7 @@ decode_split_kernel(
   const char* vbase = reinterpret_cast<const char*>(v_pool) + (size_t)h * kTileBytes;
   const size_t page_stride = (size_t)Hkv * kTileBytes;
   if constexpr (kMfma) {
-    WaveAttnMfma<G> wa;
+    DecodeMfma<G> wa;
     wa.init(qrows, lane);
     wa.run(src, kbase, vbase, page_stride, scale_log2, sh.v[wave], lane);
     wa.store(&sh.o[wave][0][0], &sh.ml[wave][0][0], lane);
@@ -359,10 +363,10 @@ struct StreamHook {
   float* part_ml;
   int* row_slots;
   int w, lane;
-  __device__ __forceinline__ void operator()(WaveAttnMfma<G>& wa, int word) const {
+  __device__ __forceinline__ void operator()(DecodeMfma<G>& wa, int word) const {
     const int r = word >> 3;
     const size_t slot = (size_t)w + r;
-    wa.store(part_o + slot * G * WaveAttnMfma<G>::D, part_ml + slot * G * 2, lane);
+    wa.store(part_o + slot * G * DecodeMfma<G>::D, part_ml + slot * G * 2, lane);
     if (lane == 0) {
       if (word & 2) row_slots[2 * r] = w;
       if (word & 4) row_slots[2 * r + 1] = w;
@@ -380,7 +384,7 @@ decode_stream_kernel(
     const int* __restrict__ sel, const int* __restrict__ sel_count, int k, float scale_log2,
     int nwaves, float* __restrict__ part_o, float* __restrict__ part_ml,
     int* __restrict__ row_slots, unsigned int* __restrict__ err) {
-  using WA = WaveAttnMfma<G>;
+  using WA = DecodeMfma<G>;
   __shared__ StreamTables tab;
   __shared__ alignas(16) char vl[4][WA::kLdsBytes];
   __shared__ long long wtot[4];

@@ -51,12 +51,14 @@ struct NoSegments {
 };
 
 // Two page buffers (one page in flight while one is computed) measured
-// faster than three or four.
-template <int G, int kStagesArg = 2>
+// faster than three or four. kStreamArg: the K/V tile loads carry the
+// non-temporal hint (ld16_stream).
+template <int G, int kStagesArg = 2, bool kStreamArg = false>
 struct WaveAttnMfma {
   static_assert(G >= 1 && G <= 16, "one 16-column tile of heads");
   static constexpr int D = 128;
   static constexpr int kStages = kStagesArg;     // page buffers per wave
+  static constexpr bool kStream = kStreamArg;
   static constexpr int kVPitch = 144;            // LDS row of the V tile in bf16 (256 B + 32 B pad)
   static constexpr int kVTileBytes = kPage * kVPitch * 2;
   static constexpr int kLdsBytes = 2 * kVTileBytes;  // per wave: double-buffered V tile
@@ -120,9 +122,9 @@ struct WaveAttnMfma {
       const char* kt = kbase + (size_t)p * page_stride;
       const char* vt = vbase + (size_t)p * page_stride;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kA[ks] = ld16(kt + c16 * kRowBytes + ks * 64 + grp * 16);
+      for (int ks = 0; ks < 4; ++ks) kA[ks] = ld16_as<kStream>(kt + c16 * kRowBytes + ks * 64 + grp * 16);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vB[r] = ld16(vt + r * 1024 + lane * 16);
+      for (int r = 0; r < 4; ++r) vB[r] = ld16_as<kStream>(vt + r * 1024 + lane * 16);
       return valid;
     };
 

@@ -7,7 +7,8 @@
 // comparison is an unsigned compare of order-preserving keys (IEEE total
 // order, -0 < +0), so the result is exact and independent of reduction order.
 //
-// One wave per (page, KV head) tile (tile_minmax).
+// One wave per (page, KV head) tile (tile_minmax), read with the non-temporal
+// hint (ld16_stream).
 //
 // The centroid summary (build_centroid_kernel) is the alternative page
 // summary of the Vortex digest's cache phase, laid out the same way with one
@@ -44,7 +45,7 @@ __global__ void __launch_bounds__(256) build_meta_kernel(
   const char* src = reinterpret_cast<const char*>(k_pool) + ((size_t)p * Hkv + h) * kTileBytes;
 
   uint4 vmn, vmx;
-  tile_minmax<T>(src, valid, lane, vmn, vmx);
+  tile_minmax<T, true>(src, valid, lane, vmn, vmx);
   // lanes 0..15 write the min row, lanes 16..31 the max row of this
   // sequence's logical page j
   if (lane < 32) {
@@ -80,7 +81,7 @@ __global__ void __launch_bounds__(256) build_centroid_kernel(
   }
   const int valid = min(kPage, L - kPage * j);
   const char* src = reinterpret_cast<const char*>(k_pool) + ((size_t)p * Hkv + h) * kTileBytes;
-  const uint4 mean = tile_mean<T>(src, valid, lane);
+  const uint4 mean = tile_mean<T, true>(src, valid, lane);
   if (lane < 16) {
     char* dst = reinterpret_cast<char*>(cent) + (((size_t)b * Hkv + h) * stride + j) * kRowBytes;
     st16(dst + lane * 16, mean);

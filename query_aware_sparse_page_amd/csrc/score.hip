@@ -47,7 +47,8 @@ __global__ void __launch_bounds__(256) score_kernel(
   constexpr int kRec = kCentroid ? kRowBytes : 2 * kRowBytes;  // bytes per page record
   char* mrow_base = reinterpret_cast<char*>(meta) + ((size_t)b * Hkv + h) * stride * kRec;
 
-  // Metadata loads first (any j < stride is in bounds), then the row length.
+  // Metadata loads first (any j < stride is in bounds; each record is read
+  // once, with the non-temporal hint), then the row length.
   constexpr int kSteps = kScorePagesPerBlock / 16;
   uint4 mrow[kSteps], Mrow[kSteps];
   int jj[kSteps];
@@ -56,8 +57,8 @@ __global__ void __launch_bounds__(256) score_kernel(
     jj[s] = base_j + s * 16 + wave * 4 + slot;
     if (jj[s] < stride) {
       const char* rec = mrow_base + (size_t)jj[s] * kRec;
-      mrow[s] = ld16(rec + c * 16);
-      if (!kCentroid) Mrow[s] = ld16(rec + 256 + c * 16);
+      mrow[s] = ld16_stream(rec + c * 16);
+      if (!kCentroid) Mrow[s] = ld16_stream(rec + 256 + c * 16);
     }
   }
   // Query chunks of the group's heads (split by sign for the bound).
