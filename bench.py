@@ -60,22 +60,22 @@ PREFIX_SRC = ["cascade.hip", "cascade_prefix.h", "qsa_device.h", "qsa_internal.h
 # (c2 dense and c3: split-K decode + merge; c5: the interleaved prefix and
 # suffix-row kernel + merge; 'cascade_sparse:overlap' is that kernel alone).
 MEASURED = {
-    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 44.88, "traffic": 197796997, "l2_hit": 0.5246,
-        "sources": FUSED_SRC, "sha256_16": "2491021af04f0c03", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.37,
-        "sources": FUSED_SRC, "sha256_16": "2491021af04f0c03", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 102.30, "traffic": 539256898,
-        "sources": DECODE_SRC, "sha256_16": "ccf7c53faa7fde30", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
-    ('c3_dense', 'dense', 'bound'): {"kernel_us": 872.94, "traffic": 5142990414, "l2_hit": 0.0083,
-        "sources": DECODE_SRC, "sha256_16": "ccf7c53faa7fde30", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
-    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 46.02, "traffic": 271420504,
-        "sources": SCORE_SRC, "sha256_16": "9bfeb31cc939c874", "profile": "profiles/split_pipeline_c4_long.md"},
-    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 69.29, "traffic": 269741809, "l2_hit": 0.4351,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "b95152a302128f76", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 62.41,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "b95152a302128f76", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 35.58,
-        "sources": PREFIX_SRC, "sha256_16": "c8b81d062c5405c7", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 44.77, "traffic": 197299400, "l2_hit": 0.5255,
+        "sources": FUSED_SRC, "sha256_16": "27385a1d121cc9a2", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.08,
+        "sources": FUSED_SRC, "sha256_16": "27385a1d121cc9a2", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 99.45, "traffic": 547445920,
+        "sources": DECODE_SRC, "sha256_16": "5990ad4b04820c96", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
+    ('c3_dense', 'dense', 'bound'): {"kernel_us": 796.98, "traffic": 5163542859, "l2_hit": 0.3350,
+        "sources": DECODE_SRC, "sha256_16": "5990ad4b04820c96", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
+    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 41.65, "traffic": 271415394,
+        "sources": SCORE_SRC, "sha256_16": "b47b63bbecfa3e2e", "profile": "profiles/split_pipeline_c4_long.md"},
+    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 68.91, "traffic": 269760361, "l2_hit": 0.4345,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "be6da69ca8997cdd", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 62.06,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "be6da69ca8997cdd", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 35.07,
+        "sources": PREFIX_SRC, "sha256_16": "41d8497b9c13e0a4", "profile": "profiles/cascade_c5_cascade.md"},
 }
 
 
