@@ -195,6 +195,9 @@ def run_config(config, *, steps, warmup, replicas, path_arg, scorer, dense, grap
         # the one-call selective cascade step
         path = "cascade_sparse"
         ws_bytes = qsa.cascade_sparse_decode_workspace_size(kvs[0], Hq, case.prefix_len, stride, k)
+    if path == "fused":
+        ws_bytes = qsa.sparse_decode_workspace_size(kvs[0], Hq, stride, k, "fused")
+    # (zeroed once: the fused path's row counters are left zero by every call)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def stage_score(r):
@@ -218,7 +221,7 @@ def run_config(config, *, steps, warmup, replicas, path_arg, scorer, dense, grap
 
     def stage_fused(r):
         qsa.sparse_decode(case.q, kvs[r], metas[r], k, sm_scale=case.sm_scale, refresh_tail=True, path="fused",
-                          out=(out, lse), scorer=scorer)
+                          out=(out, lse), scorer=scorer, workspace=ws)
 
     def stage_cascade_sparse(r):
         qsa.cascade_sparse_decode(case.q, case.prefix_pages, case.prefix_len, kvs[r], metas[r], k,

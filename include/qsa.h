@@ -264,16 +264,24 @@ qsa_status qsa_paged_decode_noalloc(const qsa_dims* dims, const void* q,
  * Optional outputs (each may be NULL): group_scores [B, Hkv, stride] fp32,
  * sel [B, Hkv, k] int32 (ascending, -1 padded), sel_count [B, Hkv] int32.
  * path selects the kernels:
- *   QSA_PATH_FUSED - one launch, no workspace: one workgroup per (b, h)
- *     row scores, selects, attends and merges in LDS; rows of at most 4096
- *     pages (max_b n_b <= 4096) with min(k, max_b n_b) <= 512, else
- *     QSA_ERR_UNSUPPORTED. Rows of at most 64 pages with bf16 groups of 4 or
- *     8 heads and the bound scorer take one wave per row instead;
+ *   QSA_PATH_FUSED - one launch: one workgroup per (b, h) row scores,
+ *     selects, attends and merges in LDS; rows of at most 4096 pages
+ *     (max_b n_b <= 4096) with min(k, max_b n_b) <= 512, else
+ *     QSA_ERR_UNSUPPORTED. With fewer rows than the GPU has CUs, two
+ *     workgroups share each row, each attending over half of the selected
+ *     pages, and the second to finish merges the two partial results
+ *     through the workspace (the result does not depend on which one that
+ *     is). Rows of at most 64 pages with bf16 groups of 4 or 8 heads and the
+ *     bound scorer take one wave per row instead;
  *   QSA_PATH_SPLIT - the separate score, top-K and split-K decode kernels,
  *     which spread one row over many workgroups (long rows, few rows);
  *   QSA_PATH_AUTO - FUSED when supported and B * Hkv >= 64, else SPLIT.
- * Workspace: qsa_sparse_decode_workspace_size(...) with the same path (0 for
- * the fused path; ws may then be NULL). */
+ * Workspace: qsa_sparse_decode_workspace_size(...) with the same path, 16-byte
+ * aligned; too small returns QSA_ERR_WORKSPACE. For the fused path it is 0
+ * (ws may be NULL) unless rows are shared: then its first B * Hkv * 4 bytes
+ * are per-row arrival counters, which must be zero before the workspace's
+ * first use with this path; every call leaves them zero. A workspace serves
+ * one call at a time (calls that overlap on one GPU need their own). */
 typedef enum qsa_path {
   QSA_PATH_AUTO = 0,
   QSA_PATH_FUSED = 1,

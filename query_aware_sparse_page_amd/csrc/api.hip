@@ -250,6 +250,26 @@ struct SparseWs {
   size_t total() const { return align_up(gs) + align_up(sel) + align_up(cnt) + dec.total(); }
 };
 
+// The fused path's exchange: with fewer (b, h) rows than CUs two workgroups
+// share each row and merge their partial results through the workspace
+// (per-row arrival counters, then per (row, part) G * (D + 2) floats).
+bool fused_pair_split(const qsa_dims* d) { return d->num_seqs * d->num_kv_heads < device_cus(); }
+
+struct PairWs {
+  size_t counters = 0, partials = 0;
+  size_t total() const { return counters == 0 ? 0 : align_up(counters) + align_up(partials); }
+};
+
+PairWs pair_ws(const qsa_dims* d) {
+  PairWs w;
+  if (!fused_pair_split(d)) return w;
+  const size_t rows = (size_t)d->num_seqs * d->num_kv_heads;
+  const size_t g = (size_t)(d->num_q_heads / d->num_kv_heads);
+  w.counters = rows * sizeof(unsigned int);
+  w.partials = rows * 2 * g * (d->head_dim + 2) * sizeof(float);
+  return w;
+}
+
 SparseWs sparse_ws(const qsa_dims* d, const int32_t* lens, int stride, int k) {
   const size_t rows = (size_t)d->num_seqs * d->num_kv_heads;
   SparseWs w;
@@ -652,7 +672,7 @@ size_t qsa_sparse_decode_workspace_size(const qsa_dims* dims, const int32_t* seq
                                         int32_t stride, int32_t k, int32_t path) {
   qsa_path chosen;
   if (qsa_sparse_decode_path(dims, seq_lens_host, stride, k, path, &chosen) != QSA_OK) return 0;
-  if (chosen == QSA_PATH_FUSED) return 0;
+  if (chosen == QSA_PATH_FUSED) return pair_ws(dims).total();
   return sparse_ws(dims, seq_lens_host, stride, k).total();
 }
 
@@ -692,13 +712,21 @@ qsa_status sparse_decode_impl(const qsa_dims* dims, const void* q, const qsa_pag
                    stream);
   }
   if (chosen == QSA_PATH_FUSED) {
-    // fewer rows than CUs: two workgroups per row, each attending for half
-    // of the group's query heads
-    const int rows = dims->num_seqs * dims->num_kv_heads;
-    const int head_split = (c.G >= 2 && rows < device_cus()) ? 2 : 1;
+    // fewer rows than CUs: two workgroups per row, each attending over half
+    // of the selected pages, merged through the workspace's exchange
+    qsa::RowExchange x;
+    const PairWs pw = pair_ws(dims);
+    if (pw.total() > 0) {
+      if (ws == nullptr || ws_bytes < pw.total())
+        return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, pw.total());
+      if (reinterpret_cast<uintptr_t>(ws) % 16 != 0)
+        return fail(QSA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+      x.counters = static_cast<unsigned int*>(ws);
+      x.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(pw.counters));
+    }
     if ((s = chk.begin(c, stream)) != QSA_OK) return s;
     return chk.end(device_status(qsa::launch_sparse_row(c, q, meta, stride, refresh_tail, k,
-                                                        scale_log2, head_split, centroid, out, lse,
+                                                        scale_log2, x, centroid, out, lse,
                                                         group_scores, sel, sel_count, stream),
                                  "sparse_decode (fused) launch"),
                    stream);

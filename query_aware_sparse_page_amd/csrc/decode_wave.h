@@ -32,13 +32,15 @@ constexpr float kLazyTau = 8.0f;  // log2 headroom before the reference max move
 // one is computed); the default is what the register file holds at two
 // waves per SIMD: three at g <= 4, two at g = 8. At g = 8 the query rows
 // (8 VGPRs per head) are read from LDS for every page instead of being held
-// in registers (the caller stages them in LDS).
-template <typename T, int G, int kStagesArg = 2>
+// in registers (the caller stages them in LDS). kStreamArg: the K/V tile
+// loads carry the non-temporal hint (ld16_stream).
+template <typename T, int G, int kStagesArg = 2, bool kStreamArg = false>
 struct WaveAttn {
   static constexpr int EPC = Elem<T>::kPerChunk;
   static constexpr int D = 16 * EPC;
   static constexpr int NP = (2 * G + 7) / 8;         // (row, head) pairs owned per lane
   static constexpr int kStages = kStagesArg;         // page buffers per wave
+  static constexpr bool kStream = kStreamArg;
   static constexpr bool kQInLds = G >= 8;            // query rows read from LDS
   static constexpr int kPBufFloats = 2 * kPage * G;  // LDS per wave: double-buffered probabilities
   // s_waitcnt immediate (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt
@@ -103,11 +105,11 @@ struct WaveAttn {
       const char* vt = vbase + (size_t)p * page_stride;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        kA[s2][0] = ld16(kt + (gi + 8 * s2) * kRowBytes + qa * 16);
-        kA[s2][1] = ld16(kt + (gi + 8 * s2) * kRowBytes + (qa + 8) * 16);
+        kA[s2][0] = ld16_as<kStream>(kt + (gi + 8 * s2) * kRowBytes + qa * 16);
+        kA[s2][1] = ld16_as<kStream>(kt + (gi + 8 * s2) * kRowBytes + (qa + 8) * 16);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vB[r] = ld16(vt + r * 1024 + lane * 16);
+      for (int r = 0; r < 4; ++r) vB[r] = ld16_as<kStream>(vt + r * 1024 + lane * 16);
       return valid;
     };
 

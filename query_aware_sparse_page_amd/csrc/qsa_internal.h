@@ -91,18 +91,26 @@ hipError_t launch_decode(const LaunchCommon& c, const void* q, const int* sel, c
                          hipStream_t stream);
 
 // Fused per-row sparse decode step (score -> top-K -> attention -> merge in
-// one workgroup per (b, h) row, or head_split = 2 workgroups per row that
-// each attend for half of the group's query heads). Rows of at most
+// one workgroup per (b, h) row, or two workgroups per row that each attend
+// over half of the selected pages and merge through a RowExchange). Rows of at most
 // kRowMaxPages pages, at most kRowMaxSelect selected pages.
 constexpr int kRowMaxPages = 4096;
 constexpr int kRowMaxSelect = 512;
 
 // centroid: meta holds centroid rows (256 bytes per page) scored as q . c
 // instead of [m | M] records scored by the bound.
+// The exchange of the fused kernel's two workgroups per row (both NULL: one
+// workgroup per row): per-row arrival counters (zero before the first call,
+// left zero by every call) and per (row, part) partial results of
+// G * (D + 2) floats.
+struct RowExchange {
+  unsigned int* counters = nullptr;
+  float* partials = nullptr;
+};
 hipError_t launch_sparse_row(const LaunchCommon& c, const void* q, void* meta, int stride,
-                             int refresh_tail, int k, float scale_log2, int head_split, bool centroid,
-                             float* out, float* lse, float* group_scores, int* sel, int* sel_count,
-                             hipStream_t stream);
+                             int refresh_tail, int k, float scale_log2, const RowExchange& x,
+                             bool centroid, float* out, float* lse, float* group_scores, int* sel,
+                             int* sel_count, hipStream_t stream);
 
 // Steps 2-4 for rows of at most kShortMaxPages pages, one wave per (b, h)
 // row (bf16, D = 128, G = 4 or 8, the bound scorer): scores with the

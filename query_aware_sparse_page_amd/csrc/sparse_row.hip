@@ -22,9 +22,11 @@
 //     threshold, plus the first ones equal to it (ties go to the smaller
 //     logical page). The list is in ascending page order.
 //  3. Attend: wave w takes list entries w, w+8, ... through the per-wave
-//     paged attention of decode_wave.h.
+//     paged attention of decode_wave.h (K/V read with the non-temporal hint:
+//     each selected tile is read by one wave of one workgroup).
 //  4. Merge: the 8 waves' (max, sum, o) are combined by log-sum-exp in LDS and
-//     the normalised output and LSE are written; no partials leave the chip.
+//     the normalised output and LSE are written; with one workgroup per row
+//     no partials leave the chip.
 // kCentroid = true runs phase 1 on centroid rows instead (the Vortex digest's
 // mean-key page summary: 256-byte records scored as q . c, the tail page's
 // centroid rebuilt with tile_mean); phases 2-4 are unchanged.
@@ -47,7 +49,7 @@ constexpr int row_stages(int gw) { return 2; }
 
 template <typename T, int GW>
 struct RowShared {
-  using WA = WaveAttn<T, GW, row_stages(GW)>;
+  using WA = WaveAttn<T, GW, row_stages(GW), true>;
   static constexpr int D = WA::D;
   union {
     struct {
@@ -70,13 +72,22 @@ struct RowShared {
   int chunk_cursor;  // next score chunk to hand out
 };
 
-// S workgroups share one row when there are too few rows to fill the chip:
-// each scores and selects the whole row (the group score needs every head of
-// the group) and attends for G/S of its query heads. Workgroup w serves part
-// (w / 8) % S of row (w % 8) + 8 * (w / (8 S)), so the S workgroups of a row
-// are dispatched to the same XCD (workgroups go round-robin over the 8 XCDs)
-// and share its L2 for the row's records and K/V tiles, which they stream in
-// the same order at the same time.
+// S = 2 workgroups share one row when there are too few rows to fill the
+// chip: each scores and selects the whole row (the group score needs every
+// head of the group) and attends for every head over its share of the
+// selected pages (list entries part, part + 2, ...), so that each K/V tile is
+// read once. Workgroup w serves part (w / 8) % S of row (w % 8) + 8 * (w / (8
+// S)), so the two workgroups of a row are dispatched to the same XCD
+// (workgroups go round-robin over the 8 XCDs) and share its L2 for the row's
+// records, which both stream. The two partial results (per head: max, sum
+// and unnormalised output, G * (D + 2) floats) meet in the exchange buffer:
+// each workgroup stores its own with agent-scope stores, waits for them to
+// complete, then adds one to the row's arrival counter (agent scope); the
+// one that finds the counter at 1 arrived second. It sets the counter back to
+// 0 for the next call, reads the other partial (agent-scope loads), merges
+// and writes O and LSE. The merge adds part 0's term to part 1's whichever
+// workgroup does it, so the result does not depend on the arrival order. The
+// counters must be zero before the first call and every call leaves them zero.
 template <typename T, int G, int S, bool kCentroid>
 __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     const T* __restrict__ q, T* __restrict__ meta, int stride, const T* __restrict__ k_pool,
@@ -84,12 +95,13 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     const int* __restrict__ page_indptr, const int* __restrict__ page_indices,
     const int* __restrict__ seq_lens, int refresh_tail, int k, float scale_log2,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ group_scores,
-    int* __restrict__ sel, int* __restrict__ sel_count, unsigned int* __restrict__ err) {
-  constexpr int GW = G / S;  // query heads attended by this workgroup
-  using WA = typename RowShared<T, GW>::WA;
+    int* __restrict__ sel, int* __restrict__ sel_count, unsigned int* __restrict__ xcnt,
+    float* __restrict__ xpart, unsigned int* __restrict__ err) {
+  static_assert(S == 1 || S == 2, "one or two workgroups per row");
+  using WA = typename RowShared<T, G>::WA;
   constexpr int EPC = WA::EPC;
   constexpr int D = WA::D;
-  __shared__ RowShared<T, GW> sh;
+  __shared__ RowShared<T, G> sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,7 +116,6 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     sel = nullptr;
     sel_count = nullptr;
   }
-  const int hq0 = part * GW;  // first attended head within the group
   const int b = row_i / Hkv;
   const int h = row_i - b * Hkv;
   const int Hq = Hkv * G;
@@ -162,9 +173,8 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   // after the chunk loop: a store would wait for the records in flight)
   uint4 qstage = make_uint4(0, 0, 0, 0);
   if constexpr (WA::kQInLds) {
-    if (tid < GW * kRowBytes / 16)
-      qstage = ld16(reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G + hq0) * kRowBytes +
-                    tid * 16);
+    if (tid < G * kRowBytes / 16)
+      qstage = ld16(reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G) * kRowBytes + tid * 16);
   }
   const int nchunks = (n + kChunkPages - 1) / kChunkPages;
 
@@ -256,7 +266,7 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     if (j < n) sh.u.s.phys[j] = ph[i];
   }
   if constexpr (WA::kQInLds) {
-    if (tid < GW * kRowBytes / 16) sh.q[tid] = qstage;
+    if (tid < G * kRowBytes / 16) sh.q[tid] = qstage;
   }
   if (tid < 256) sh.hist[0][tid] = 0u;
 
@@ -395,12 +405,14 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   __syncthreads();
 
   // ---- phase 3: attention over the selected pages --------------------------
-  // Wave w takes list entries w, w + 8, ... (a fixed split keeps the
-  // summation order, and so the result, the same from run to run).
-  const int npw = keff > wave ? (keff - wave + kRowWaves - 1) / kRowWaves : 0;
+  // Wave w of part p takes list entries p + S (w + 8 i), i = 0, 1, ... (a
+  // fixed split keeps the summation order, and so the result, the same from
+  // run to run).
+  const int first_e = part + S * wave;
+  const int npw = keff > first_e ? (keff - first_e + S * kRowWaves - 1) / (S * kRowWaves) : 0;
   int my_p = 0, my_valid = 0;
   if (lane < npw) {
-    const int e = wave + kRowWaves * lane;
+    const int e = first_e + S * kRowWaves * lane;
     const int pp = sh.plist[e];
     if (pp >= 0) {
       my_p = pp;
@@ -411,7 +423,7 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
 
   WA wa;
   wa.init(WA::kQInLds ? reinterpret_cast<const char*>(sh.q)
-                      : reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G + hq0) * kRowBytes,
+                      : reinterpret_cast<const char*>(q) + ((size_t)b * Hq + h * G) * kRowBytes,
           lane);
   wa.run(src, reinterpret_cast<const char*>(k_pool) + (size_t)h * kTileBytes,
          reinterpret_cast<const char*>(v_pool) + (size_t)h * kTileBytes,
@@ -422,59 +434,119 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   wa.reduce(&mw, &lw);
   if (lane < 16) {
 #pragma unroll
-    for (int hh = 0; hh < GW; ++hh)
+    for (int hh = 0; hh < G; ++hh)
 #pragma unroll
       for (int e = 0; e < EPC; ++e) sh.u.c.o[wave][hh][lane * EPC + e] = wa.o[hh][e];
   }
-  if (lane < GW) {
+  if (lane < G) {
     sh.u.c.ml[wave][lane][0] = mw;
     sh.u.c.ml[wave][lane][1] = lw;
   }
   __syncthreads();
-  for (int idx = tid; idx < GW * D; idx += kRowThreads) {
-    const int hh = idx / D;
-    const int d = idx - hh * D;
-    float M = -__builtin_inff();
+  // this workgroup's result per (head, dim): max, sum, unnormalised output
+  constexpr int kPer = (G * D + kRowThreads - 1) / kRowThreads;
+  float accv[kPer], mv[kPer], lv[kPer];
 #pragma unroll
-    for (int w = 0; w < kRowWaves; ++w) M = fmaxf(M, sh.u.c.ml[w][hh][0]);
-    float acc = 0.0f, lsum = 0.0f;
+  for (int i = 0; i < kPer; ++i) {
+    const int idx = tid + i * kRowThreads;
+    accv[i] = 0.0f;
+    mv[i] = -__builtin_inff();
+    lv[i] = 0.0f;
+    if (idx < G * D) {
+      const int hh = idx / D;
+      const int d = idx - hh * D;
+      float M = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < kRowWaves; ++w) {
-      const float m2 = sh.u.c.ml[w][hh][0];
-      const float sc = (m2 == -__builtin_inff()) ? 0.0f : fast_exp2(m2 - M);
-      acc += sh.u.c.o[w][hh][d] * sc;
-      lsum += sh.u.c.ml[w][hh][1] * sc;
+      for (int w = 0; w < kRowWaves; ++w) M = fmaxf(M, sh.u.c.ml[w][hh][0]);
+      float acc = 0.0f, lsum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kRowWaves; ++w) {
+        const float m2 = sh.u.c.ml[w][hh][0];
+        const float sc = (m2 == -__builtin_inff()) ? 0.0f : fast_exp2(m2 - M);
+        acc += sh.u.c.o[w][hh][d] * sc;
+        lsum += sh.u.c.ml[w][hh][1] * sc;
+      }
+      accv[i] = acc;
+      mv[i] = M;
+      lv[i] = lsum;
+      if constexpr (S == 2) {
+        // exchange slot of (row, part): [G][D] outputs, then [G][2] (max, sum)
+        float* xo = xpart + (row * 2 + part) * (size_t)(G * (D + 2));
+        __hip_atomic_store(xo + idx, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) {
+          __hip_atomic_store(xo + G * D + 2 * hh, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(xo + G * D + 2 * hh + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
     }
-    const size_t qrow = (size_t)b * Hq + h * G + hq0 + hh;
-    out[qrow * D + d] = lsum > 0.0f ? acc / lsum : 0.0f;
-    if (lse != nullptr && d == 0)
-      lse[qrow] = lsum > 0.0f ? (M + __log2f(lsum)) * 0.69314718055994530942f : -__builtin_inff();
+  }
+  if constexpr (S == 2) {
+    // every thread's stores complete before the arrival is counted
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      sh.pick[0] = __hip_atomic_fetch_add(xcnt + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (sh.pick[0] == 0u) return;  // first to arrive: the other workgroup merges
+    if (tid == 0) __hip_atomic_store(xcnt + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int idx = tid + i * kRowThreads;
+    if (idx < G * D) {
+      const int hh = idx / D;
+      const int d = idx - hh * D;
+      float M = mv[i], acc = accv[i], lsum = lv[i];
+      if constexpr (S == 2) {
+        const float* xo = xpart + (row * 2 + (1 - part)) * (size_t)(G * (D + 2));
+        const float acc1 = __hip_atomic_load(xo + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float m1 = __hip_atomic_load(xo + G * D + 2 * hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float l1 = __hip_atomic_load(xo + G * D + 2 * hh + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // part 0's term first, whichever part merges (a fused multiply-add
+        // takes the first product: the same rounding either way)
+        const bool p0 = part == 0;
+        const float aA = p0 ? acc : acc1, aB = p0 ? acc1 : acc;
+        const float mA = p0 ? M : m1, mB = p0 ? m1 : M;
+        const float lA = p0 ? lsum : l1, lB = p0 ? l1 : lsum;
+        const float mn = fmaxf(mA, mB);
+        const float sA = (mA == -__builtin_inff()) ? 0.0f : fast_exp2(mA - mn);
+        const float sB = (mB == -__builtin_inff()) ? 0.0f : fast_exp2(mB - mn);
+        acc = aA * sA + aB * sB;
+        lsum = lA * sA + lB * sB;
+        M = mn;
+      }
+      const size_t qrow = (size_t)b * Hq + h * G + hh;
+      out[qrow * D + d] = lsum > 0.0f ? acc / lsum : 0.0f;
+      if (lse != nullptr && d == 0)
+        lse[qrow] = lsum > 0.0f ? (M + __log2f(lsum)) * 0.69314718055994530942f : -__builtin_inff();
+    }
   }
 }
 
 template <typename T, int G, int S, bool kCentroid>
 void launch_row(const LaunchCommon& c, const void* q, void* meta, int stride, int refresh_tail,
                 int k, float scale_log2, float* out, float* lse, float* group_scores, int* sel,
-                int* sel_count, hipStream_t stream) {
+                int* sel_count, const RowExchange& x, hipStream_t stream) {
   const int rows = c.B * c.Hkv;
   const int wgs = S == 1 ? rows : S * ((rows + 7) / 8 * 8);
   hipLaunchKernelGGL((sparse_row_kernel<T, G, S, kCentroid>), dim3(wgs), dim3(kRowThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<T*>(meta), stride,
                      static_cast<const T*>(c.k_pool), static_cast<const T*>(c.v_pool), c.num_phys,
                      c.Hkv, rows, c.page_indptr, c.page_indices, c.seq_lens, refresh_tail, k,
-                     scale_log2, out, lse, group_scores, sel, sel_count, c.err);
+                     scale_log2, out, lse, group_scores, sel, sel_count, x.counters, x.partials,
+                     c.err);
 }
 
 template <typename T, bool kCen>
 hipError_t launch_sparse_row_t(const LaunchCommon& c, const void* q, void* meta, int stride,
-                               int refresh_tail, int k, float scale_log2, int head_split,
+                               int refresh_tail, int k, float scale_log2, const RowExchange& x,
                                float* out, float* lse, float* group_scores, int* sel,
                                int* sel_count, hipStream_t stream) {
-  const bool two = head_split == 2;
+  const bool two = x.counters != nullptr;
 #define QSA_ROW_ARGS c, q, meta, stride, refresh_tail, k, scale_log2, out, lse, group_scores, sel, \
-                     sel_count, stream
+                     sel_count, x, stream
   switch (c.G) {
-    case 1: launch_row<T, 1, 1, kCen>(QSA_ROW_ARGS); break;
+    case 1: two ? launch_row<T, 1, 2, kCen>(QSA_ROW_ARGS) : launch_row<T, 1, 1, kCen>(QSA_ROW_ARGS); break;
     case 2: two ? launch_row<T, 2, 2, kCen>(QSA_ROW_ARGS) : launch_row<T, 2, 1, kCen>(QSA_ROW_ARGS); break;
     case 4: two ? launch_row<T, 4, 2, kCen>(QSA_ROW_ARGS) : launch_row<T, 4, 1, kCen>(QSA_ROW_ARGS); break;
     case 8: two ? launch_row<T, 8, 2, kCen>(QSA_ROW_ARGS) : launch_row<T, 8, 1, kCen>(QSA_ROW_ARGS); break;
@@ -488,11 +560,11 @@ hipError_t launch_sparse_row_t(const LaunchCommon& c, const void* q, void* meta,
 }  // namespace
 
 hipError_t launch_sparse_row(const LaunchCommon& c, const void* q, void* meta, int stride,
-                             int refresh_tail, int k, float scale_log2, int head_split, bool centroid,
-                             float* out, float* lse, float* group_scores, int* sel, int* sel_count,
-                             hipStream_t stream) {
+                             int refresh_tail, int k, float scale_log2, const RowExchange& x,
+                             bool centroid, float* out, float* lse, float* group_scores, int* sel,
+                             int* sel_count, hipStream_t stream) {
 #define QSA_ROW_CALL(TT, CC)                                                                      \
-  launch_sparse_row_t<TT, CC>(c, q, meta, stride, refresh_tail, k, scale_log2, head_split, out, lse, \
+  launch_sparse_row_t<TT, CC>(c, q, meta, stride, refresh_tail, k, scale_log2, x, out, lse,      \
                               group_scores, sel, sel_count, stream)
   if (c.bf16) return centroid ? QSA_ROW_CALL(bf16s, true) : QSA_ROW_CALL(bf16s, false);
   return centroid ? QSA_ROW_CALL(float, true) : QSA_ROW_CALL(float, false);

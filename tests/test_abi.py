@@ -158,11 +158,13 @@ def _path(L, d, lens, stride, k, path):
 
 def test_sparse_decode_path_choice(L):
     AUTO, FUSED, SPLIT = qsa.PATHS["auto"], qsa.PATHS["fused"], qsa.PATHS["split"]
-    # 16 x 8 rows of 512 pages, 153 selected: fused by default, no workspace
+    # 16 x 8 rows of 512 pages, 153 selected: fused by default
     d = _dims(B=16)
     lens = _lens([8192] * 16)
     assert _path(L, d, lens, 512, 153, AUTO) == (0, FUSED)
-    assert L.qsa_sparse_decode_workspace_size(ctypes.byref(d), lens, 512, 153, AUTO) == 0
+    # (128 rows, fewer than the CUs: the two-workgroup exchange, 512 bytes of
+    # counters then 128 x 2 x 4 x (128 + 2) floats)
+    assert L.qsa_sparse_decode_workspace_size(ctypes.byref(d), lens, 512, 153, AUTO) == 512 + 128 * 2 * 4 * 130 * 4
     # the split path needs scores + selection + decode partials
     assert _path(L, d, lens, 512, 153, SPLIT) == (0, SPLIT)
     ws = L.qsa_sparse_decode_workspace_size(ctypes.byref(d), lens, 512, 153, SPLIT)
@@ -185,6 +187,14 @@ def test_sparse_decode_path_choice(L):
     assert _path(L, d, lens, 512, 0, AUTO)[0] == qsa.QSA_ERR_INVALID_ARG        # k < 1
     assert _path(L, d, lens, 512, 153, 7)[0] == qsa.QSA_ERR_INVALID_ARG         # unknown path
     assert L.qsa_sparse_decode_workspace_size(ctypes.byref(d), lens, 512, 0, AUTO) == 0
+    # fewer rows than CUs on the fused path: two workgroups per row exchange
+    # partial results through the workspace (8 rows: 32 bytes of counters,
+    # aligned to 256, then 8 rows x 2 parts x 4 heads x (128 + 2) floats)
+    assert L.qsa_sparse_decode_workspace_size(ctypes.byref(d1), _lens([8192]), 512, 153, FUSED) == \
+        256 + 8 * 2 * 4 * 130 * 4
+    # a row per CU (256 rows): one workgroup per row, no workspace
+    d32 = _dims(B=32)
+    assert L.qsa_sparse_decode_workspace_size(ctypes.byref(d32), _lens([8192] * 32), 512, 153, FUSED) == 0
 
 
 def test_sparse_decode_validation(L):
@@ -207,6 +217,17 @@ def test_sparse_decode_validation(L):
     # the split path checks its workspace before launching anything
     st = call(args(path=qsa.PATHS["split"]))
     assert st == qsa.QSA_ERR_WORKSPACE and b"workspace" in L.qsa_last_error()
+    # so does the fused path when two workgroups share each row (4 x 8 rows
+    # of 512 pages): its exchange lives in the workspace, 16-byte aligned
+    long_lens = _lens([8192] * 4)
+    kv2 = qsa.PagedKVStruct(1, 1, 10, 1, 1, 1, ctypes.cast(long_lens, ctypes.POINTER(ctypes.c_int32)))
+
+    def call_fused(ws, wsb):
+        return L.qsa_sparse_decode(ctypes.byref(d), 1, ctypes.byref(kv2), 1, 512, 1, 153, ctypes.c_float(1.0), 1,
+                                   None, None, None, None, qsa.PATHS["fused"], ws, wsb, None)
+
+    assert call_fused(None, 0) == qsa.QSA_ERR_WORKSPACE and b"workspace" in L.qsa_last_error()
+    assert call_fused(1, 1 << 20) == qsa.QSA_ERR_INVALID_ARG and b"aligned" in L.qsa_last_error()
 
 
 def test_topk_approx_validation(L):

@@ -163,6 +163,48 @@ def test_fused_without_optional_outputs_and_repeatable():
     assert torch.equal(o1, o4) and torch.equal(l1, l4)
 
 
+def test_fused_pair_exchange_reuses_one_workspace():
+    """With fewer rows than CUs the fused kernel's two workgroups per row
+    merge their partial results through the workspace. One zeroed workspace
+    serves call after call (every call leaves the row counters at zero),
+    eagerly and replayed in a graph with eager calls between the replays,
+    and gives the bits of a call with a fresh workspace."""
+    c = _case("plain", [1000, 1537, 700, 16], 8, 2, "bf16")
+    g = c.to(DEV)
+    kv = qsa.PagedKV.from_case(g)
+    meta = qsa.build_page_meta(kv)
+    stride, k = int(meta.shape[2]), 30
+    rows, grp = c.B * c.Hkv, c.Hq // c.Hkv
+    need = qsa.sparse_decode_workspace_size(kv, c.Hq, stride, k, "fused")
+    assert need >= rows * 4 + rows * 2 * grp * (128 + 2) * 4
+    ref_o, ref_l = qsa.sparse_decode(g.q, kv, meta, k, sm_scale=c.sm_scale, path="fused")
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    counters = ws[:rows * 4].view(torch.int32)
+    for _ in range(3):
+        o, l = qsa.sparse_decode(g.q, kv, meta, k, sm_scale=c.sm_scale, path="fused", workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+        assert int(counters.abs().sum()) == 0
+    out, lse = torch.empty_like(ref_o), torch.empty_like(ref_l)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            qsa.sparse_decode(g.q, kv, meta, k, sm_scale=c.sm_scale, path="fused", workspace=ws, out=(out, lse))
+    torch.cuda.current_stream().wait_stream(cap)
+    for _ in range(3):
+        out.zero_()
+        lse.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+        assert int(counters.abs().sum()) == 0
+        o, l = qsa.sparse_decode(g.q, kv, meta, k, sm_scale=c.sm_scale, path="fused", workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
 def test_sparse_decode_rejects_unsupported_fused_shape():
     c = _case("long", [70000], 4, 1, "bf16")          # 4375 pages > 4096 per row
     g = c.to(DEV)
