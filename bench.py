@@ -60,22 +60,22 @@ PREFIX_SRC = ["cascade.hip", "cascade_prefix.h", "qsa_device.h", "qsa_internal.h
 # (c2 dense and c3: split-K decode + merge; c5: the interleaved prefix and
 # suffix-row kernel + merge; 'cascade_sparse:overlap' is that kernel alone).
 MEASURED = {
-    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 44.77, "traffic": 197299400, "l2_hit": 0.5255,
-        "sources": FUSED_SRC, "sha256_16": "27385a1d121cc9a2", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 43.08,
-        "sources": FUSED_SRC, "sha256_16": "27385a1d121cc9a2", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 99.45, "traffic": 547445920,
-        "sources": DECODE_SRC, "sha256_16": "5990ad4b04820c96", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
-    ('c3_dense', 'dense', 'bound'): {"kernel_us": 796.98, "traffic": 5163542859, "l2_hit": 0.3350,
-        "sources": DECODE_SRC, "sha256_16": "5990ad4b04820c96", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
-    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 41.65, "traffic": 271415394,
-        "sources": SCORE_SRC, "sha256_16": "b47b63bbecfa3e2e", "profile": "profiles/split_pipeline_c4_long.md"},
-    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 68.91, "traffic": 269760361, "l2_hit": 0.4345,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "be6da69ca8997cdd", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 62.06,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "be6da69ca8997cdd", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 35.07,
-        "sources": PREFIX_SRC, "sha256_16": "41d8497b9c13e0a4", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 42.19, "traffic": 207563310, "l2_hit": 0.2079,
+        "sources": FUSED_SRC, "sha256_16": "0bdc5987e47f0b54", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 40.37,
+        "sources": FUSED_SRC, "sha256_16": "0bdc5987e47f0b54", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 99.33, "traffic": 547388793,
+        "sources": DECODE_SRC, "sha256_16": "42e90db95028aa46", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
+    ('c3_dense', 'dense', 'bound'): {"kernel_us": 797.62, "traffic": 5163931411, "l2_hit": 0.3349,
+        "sources": DECODE_SRC, "sha256_16": "42e90db95028aa46", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
+    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 41.90, "traffic": 271414319,
+        "sources": SCORE_SRC, "sha256_16": "e234310d97adae86", "profile": "profiles/split_pipeline_c4_long.md"},
+    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 67.56, "traffic": 269745259, "l2_hit": 0.4345,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "488ae812ffcdffa1", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 60.87,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "488ae812ffcdffa1", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 35.37,
+        "sources": PREFIX_SRC, "sha256_16": "01fa55082fb46f08", "profile": "profiles/cascade_c5_cascade.md"},
 }
 
 
