@@ -205,6 +205,34 @@ def test_fused_pair_exchange_reuses_one_workspace():
         assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
 
 
+def test_fused_pair_exchange_concurrent_calls_with_own_workspaces():
+    """Two fused calls on two streams, each with its own workspace, may
+    overlap on the GPU: repeated several times, each gives the bits of the
+    same call run alone."""
+    cases = [_case("plain", [1000, 1537, 700, 16], 8, 2, "bf16", seed=23 + i) for i in range(2)]
+    gs = [c.to(DEV) for c in cases]
+    kvs = [qsa.PagedKV.from_case(g) for g in gs]
+    metas = [qsa.build_page_meta(kv) for kv in kvs]
+    k = 30
+    refs = [qsa.sparse_decode(g.q, kv, m, k, sm_scale=c.sm_scale, path="fused")
+            for c, g, kv, m in zip(cases, gs, kvs, metas)]
+    torch.cuda.synchronize()
+    wss = [torch.zeros(qsa.sparse_decode_workspace_size(kv, c.Hq, int(m.shape[2]), k, "fused"),
+                       dtype=torch.uint8, device=DEV) for c, kv, m in zip(cases, kvs, metas)]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    outs = [(torch.empty_like(r[0]), torch.empty_like(r[1])) for r in refs]
+    for _ in range(5):
+        for i in range(2):
+            streams[i].wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(streams[i]):
+                for _ in range(3):
+                    qsa.sparse_decode(gs[i].q, kvs[i], metas[i], k, sm_scale=cases[i].sm_scale, path="fused",
+                                      workspace=wss[i], out=outs[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i][0], refs[i][0]) and torch.equal(outs[i][1], refs[i][1])
+
+
 def test_sparse_decode_rejects_unsupported_fused_shape():
     c = _case("long", [70000], 4, 1, "bf16")          # 4375 pages > 4096 per row
     g = c.to(DEV)
