@@ -267,8 +267,8 @@ qsa_status qsa_paged_decode_noalloc(const qsa_dims* dims, const void* q,
  *   QSA_PATH_FUSED - one launch: one workgroup per (b, h) row scores,
  *     selects, attends and merges in LDS; rows of at most 4096 pages
  *     (max_b n_b <= 4096) with min(k, max_b n_b) <= 512, else
- *     QSA_ERR_UNSUPPORTED. With fewer rows than the GPU has CUs, two
- *     workgroups share each row, each attending over half of the selected
+ *     QSA_ERR_UNSUPPORTED. With at most half as many rows as the GPU has
+ *     CUs, two workgroups share each row, each attending over half of the selected
  *     pages, and the second to finish merges the two partial results
  *     through the workspace (the result does not depend on which one that
  *     is). Rows of at most 64 pages with bf16 groups of 4 or 8 heads and the

@@ -162,7 +162,7 @@ def test_sparse_decode_path_choice(L):
     d = _dims(B=16)
     lens = _lens([8192] * 16)
     assert _path(L, d, lens, 512, 153, AUTO) == (0, FUSED)
-    # (128 rows, fewer than the CUs: the two-workgroup exchange, 512 bytes of
+    # (128 rows, half the CUs: the two-workgroup exchange, 512 bytes of
     # counters then 128 x 2 x 4 x (128 + 2) floats)
     assert L.qsa_sparse_decode_workspace_size(ctypes.byref(d), lens, 512, 153, AUTO) == 512 + 128 * 2 * 4 * 130 * 4
     # the split path needs scores + selection + decode partials
@@ -187,14 +187,15 @@ def test_sparse_decode_path_choice(L):
     assert _path(L, d, lens, 512, 0, AUTO)[0] == qsa.QSA_ERR_INVALID_ARG        # k < 1
     assert _path(L, d, lens, 512, 153, 7)[0] == qsa.QSA_ERR_INVALID_ARG         # unknown path
     assert L.qsa_sparse_decode_workspace_size(ctypes.byref(d), lens, 512, 0, AUTO) == 0
-    # fewer rows than CUs on the fused path: two workgroups per row exchange
+    # at most half as many rows as CUs on the fused path: two workgroups per row exchange
     # partial results through the workspace (8 rows: 32 bytes of counters,
     # aligned to 256, then 8 rows x 2 parts x 4 heads x (128 + 2) floats)
     assert L.qsa_sparse_decode_workspace_size(ctypes.byref(d1), _lens([8192]), 512, 153, FUSED) == \
         256 + 8 * 2 * 4 * 130 * 4
-    # a row per CU (256 rows): one workgroup per row, no workspace
-    d32 = _dims(B=32)
-    assert L.qsa_sparse_decode_workspace_size(ctypes.byref(d32), _lens([8192] * 32), 512, 153, FUSED) == 0
+    # more rows than half the CUs (136 and 256 rows): one workgroup per row, no workspace
+    for nb in (17, 32):
+        dn = _dims(B=nb)
+        assert L.qsa_sparse_decode_workspace_size(ctypes.byref(dn), _lens([8192] * nb), 512, 153, FUSED) == 0
 
 
 def test_sparse_decode_validation(L):

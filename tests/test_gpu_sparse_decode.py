@@ -29,8 +29,8 @@ CASES = [
     # rows longer than one key per thread (563 and 2500 pages) and at the limit (4096 pages)
     ("two_keys", [9000, 40000], 8, 2, "bf16", 153),
     ("max_row", [65536, 3], 4, 1, "bf16", 512),
-    # 256 rows: one workgroup per row (fewer rows than CUs split each row's
-    # query heads over two workgroups)
+    # 256 rows: one workgroup per row (with at most half as many rows as CUs
+    # two workgroups split each row's selected pages)
     ("many_rows", [100 + (37 * i) % 900 for i in range(64)], 16, 4, "bf16", 12),
 ]
 
@@ -164,7 +164,7 @@ def test_fused_without_optional_outputs_and_repeatable():
 
 
 def test_fused_pair_exchange_reuses_one_workspace():
-    """With fewer rows than CUs the fused kernel's two workgroups per row
+    """With at most half as many rows as CUs the fused kernel's two workgroups per row
     merge their partial results through the workspace. One zeroed workspace
     serves call after call (every call leaves the row counters at zero),
     eagerly and replayed in a graph with eager calls between the replays,
