@@ -60,21 +60,21 @@ PREFIX_SRC = ["cascade.hip", "cascade_prefix.h", "qsa_device.h", "qsa_internal.h
 # (c2 dense and c3: split-K decode + merge; c5: the interleaved prefix and
 # suffix-row kernel + merge; 'cascade_sparse:overlap' is that kernel alone).
 MEASURED = {
-    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 42.19, "traffic": 207563310, "l2_hit": 0.2079,
+    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 41.68, "traffic": 207151690, "l2_hit": 0.2086,
         "sources": FUSED_SRC, "sha256_16": "0bdc5987e47f0b54", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 40.37,
+    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 40.96,
         "sources": FUSED_SRC, "sha256_16": "0bdc5987e47f0b54", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 99.33, "traffic": 547388793,
-        "sources": DECODE_SRC, "sha256_16": "42e90db95028aa46", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
-    ('c3_dense', 'dense', 'bound'): {"kernel_us": 797.62, "traffic": 5163931411, "l2_hit": 0.3349,
-        "sources": DECODE_SRC, "sha256_16": "42e90db95028aa46", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
-    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 41.90, "traffic": 271414319,
+    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 99.55, "traffic": 547399714,
+        "sources": DECODE_SRC, "sha256_16": "781f712fbe401a67", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
+    ('c3_dense', 'dense', 'bound'): {"kernel_us": 795.84, "traffic": 5164019640, "l2_hit": 0.3350,
+        "sources": DECODE_SRC, "sha256_16": "781f712fbe401a67", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
+    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 41.30, "traffic": 271414423,
         "sources": SCORE_SRC, "sha256_16": "e234310d97adae86", "profile": "profiles/split_pipeline_c4_long.md"},
-    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 67.56, "traffic": 269745259, "l2_hit": 0.4345,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "488ae812ffcdffa1", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 60.87,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "488ae812ffcdffa1", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 35.37,
+    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 69.37, "traffic": 269750326, "l2_hit": 0.4346,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "0b08b1428d509ce1", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 62.46,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "0b08b1428d509ce1", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 34.85,
         "sources": PREFIX_SRC, "sha256_16": "01fa55082fb46f08", "profile": "profiles/cascade_c5_cascade.md"},
 }
 
