@@ -60,10 +60,10 @@ PREFIX_SRC = ["cascade.hip", "cascade_prefix.h", "qsa_device.h", "qsa_internal.h
 # (c2 dense and c3: split-K decode + merge; c5: the interleaved prefix and
 # suffix-row kernel + merge; 'cascade_sparse:overlap' is that kernel alone).
 MEASURED = {
-    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 41.68, "traffic": 207151690, "l2_hit": 0.2086,
-        "sources": FUSED_SRC, "sha256_16": "0bdc5987e47f0b54", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 40.96,
-        "sources": FUSED_SRC, "sha256_16": "0bdc5987e47f0b54", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 42.55, "traffic": 207354451, "l2_hit": 0.2082,
+        "sources": FUSED_SRC, "sha256_16": "df5aa880f58cb83e", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 40.65,
+        "sources": FUSED_SRC, "sha256_16": "df5aa880f58cb83e", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
     ('c2_sparse', 'dense', 'bound'): {"kernel_us": 99.55, "traffic": 547399714,
         "sources": DECODE_SRC, "sha256_16": "781f712fbe401a67", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
     ('c3_dense', 'dense', 'bound'): {"kernel_us": 795.84, "traffic": 5164019640, "l2_hit": 0.3350,

@@ -82,7 +82,9 @@ struct RowShared {
 // records, which both stream. The two partial results (per head: max, sum
 // and unnormalised output, G * (D + 2) floats) meet in the exchange buffer:
 // each workgroup stores its own with agent-scope stores, waits for them to
-// complete, then adds one to the row's arrival counter (agent scope); the
+// complete (s_waitcnt 0: the stores have reached the agent's coherence point
+// before the counter is touched), then adds one to the row's arrival counter
+// (agent scope); the
 // one that finds the counter at 1 arrived second. It sets the counter back to
 // 0 for the next call, reads the other partial (agent-scope loads), merges
 // and writes O and LSE. The merge adds part 0's term to part 1's whichever
@@ -502,8 +504,9 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
         const float acc1 = __hip_atomic_load(xo + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const float m1 = __hip_atomic_load(xo + G * D + 2 * hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const float l1 = __hip_atomic_load(xo + G * D + 2 * hh + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // part 0's term first, whichever part merges (a fused multiply-add
-        // takes the first product: the same rounding either way)
+        // part 0's term first, whichever part merges: both workgroups then
+        // evaluate the same expression on the same operands, so however it is
+        // contracted into a fused multiply-add the rounding is the same
         const bool p0 = part == 0;
         const float aA = p0 ? acc : acc1, aB = p0 ? acc1 : acc;
         const float mA = p0 ? M : m1, mB = p0 ? m1 : M;
