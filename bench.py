@@ -60,22 +60,22 @@ PREFIX_SRC = ["cascade.hip", "cascade_prefix.h", "qsa_device.h", "qsa_internal.h
 # (c2 dense and c3: split-K decode + merge; c5: the interleaved prefix and
 # suffix-row kernel + merge; 'cascade_sparse:overlap' is that kernel alone).
 MEASURED = {
-    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 42.55, "traffic": 207354451, "l2_hit": 0.2082,
-        "sources": FUSED_SRC, "sha256_16": "df5aa880f58cb83e", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 40.65,
-        "sources": FUSED_SRC, "sha256_16": "df5aa880f58cb83e", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 99.55, "traffic": 547399714,
-        "sources": DECODE_SRC, "sha256_16": "781f712fbe401a67", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
-    ('c3_dense', 'dense', 'bound'): {"kernel_us": 795.84, "traffic": 5164019640, "l2_hit": 0.3350,
-        "sources": DECODE_SRC, "sha256_16": "781f712fbe401a67", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
-    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 41.30, "traffic": 271414423,
-        "sources": SCORE_SRC, "sha256_16": "e234310d97adae86", "profile": "profiles/split_pipeline_c4_long.md"},
-    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 69.37, "traffic": 269750326, "l2_hit": 0.4346,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "0b08b1428d509ce1", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 62.46,
-        "sources": CASCADE_SPARSE_SRC, "sha256_16": "0b08b1428d509ce1", "profile": "profiles/cascade_c5_cascade.md"},
-    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 34.85,
-        "sources": PREFIX_SRC, "sha256_16": "01fa55082fb46f08", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 42.10, "traffic": 207247127, "l2_hit": 0.2100,
+        "sources": FUSED_SRC, "sha256_16": "268a6d06db0ce2aa", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 40.79,
+        "sources": FUSED_SRC, "sha256_16": "268a6d06db0ce2aa", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'dense', 'bound'): {"kernel_us": 99.26, "traffic": 547351053,
+        "sources": DECODE_SRC, "sha256_16": "b6341b0be119dc22", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
+    ('c3_dense', 'dense', 'bound'): {"kernel_us": 794.40, "traffic": 5163543546, "l2_hit": 0.3350,
+        "sources": DECODE_SRC, "sha256_16": "b6341b0be119dc22", "profile": "profiles/decode_stream_kernel_c3_dense.md"},
+    ('c4_long', 'split:score+meta_tail', 'bound'): {"kernel_us": 41.52, "traffic": 271415435,
+        "sources": SCORE_SRC, "sha256_16": "062382de5d0f94e0", "profile": "profiles/split_pipeline_c4_long.md"},
+    ('c5_cascade', 'cascade_sparse', 'bound'): {"kernel_us": 68.28, "traffic": 269737417, "l2_hit": 0.4347,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "7ad90a787fb80f98", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade_sparse:overlap', 'bound'): {"kernel_us": 61.49,
+        "sources": CASCADE_SPARSE_SRC, "sha256_16": "7ad90a787fb80f98", "profile": "profiles/cascade_c5_cascade.md"},
+    ('c5_cascade', 'cascade:prefix', 'bound'): {"kernel_us": 34.87,
+        "sources": PREFIX_SRC, "sha256_16": "63bad53dd08d7a57", "profile": "profiles/cascade_c5_cascade.md"},
 }
 
 

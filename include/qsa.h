@@ -372,7 +372,9 @@ qsa_status qsa_decode_plan(const qsa_dims* dims, const int32_t* seq_lens_host,
  * being dereferenced run in every call (see Robustness above); checked mode
  * adds their report: each compute call clears a per-device error word on
  * its stream, passes it to its kernels, then waits for the stream and
- * returns QSA_ERR_DEVICE if any kernel skipped an out-of-range entry. The
+ * returns QSA_ERR_DEVICE if any kernel skipped an out-of-range entry, or if
+ * a fused-path row counter in the workspace was neither 0 nor 1 (a workspace
+ * not zeroed before its first use; that call's outputs are not valid). The
  * wait makes checked calls synchronous, so they are meant for debugging and
  * tests, not for graph capture; concurrent checked calls on one device share
  * the word, so a report may name another call's entry. The top-K calls read

@@ -363,6 +363,12 @@ qsa_status Checked::end(qsa_status s, hipStream_t stream) {
   if (v & qsa::kErrPhys) what += " a page table entry outside [0, num_phys_pages);";
   if (v & qsa::kErrSel) what += " a selected logical page outside [0, n_b);";
   if (v & qsa::kErrCount) what += " a sel_count entry outside [1, min(k, n_b)];";
+  if (v == qsa::kErrExchange)
+    return fail(QSA_ERR_DEVICE,
+                "device check (word 0x%x): a fused-path row counter in the workspace was neither 0 nor 1 "
+                "(the workspace was not zeroed before its first use); the outputs are not valid", v);
+  if (v & qsa::kErrExchange)
+    what += " a fused-path row counter in the workspace was neither 0 nor 1 (not zeroed before first use);";
   return fail(QSA_ERR_DEVICE, "device range check (word 0x%x):%s the entries were skipped", v,
               what.c_str());
 }

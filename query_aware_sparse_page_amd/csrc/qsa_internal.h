@@ -27,6 +27,7 @@ struct LaunchCommon {
 constexpr unsigned int kErrPhys = 1u;   // a physical page id outside [0, num_phys_pages)
 constexpr unsigned int kErrSel = 2u;    // a selected logical page outside [0, n_b)
 constexpr unsigned int kErrCount = 4u;  // a sel_count entry outside [1, k]
+constexpr unsigned int kErrExchange = 8u;  // a fused row's arrival counter was neither 0 nor 1
 
 // Records a skipped out-of-range entry in the error word (one lane per call
 // site is enough; every lane may call it). A vector atomic to global memory.

@@ -486,8 +486,11 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     // every thread's stores complete before the arrival is counted
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0)
-      sh.pick[0] = __hip_atomic_fetch_add(xcnt + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      const unsigned int old = __hip_atomic_fetch_add(xcnt + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old > 1u) report_bad(err, kErrExchange);  // the counters were not zero before the call
+      sh.pick[0] = old;
+    }
     __syncthreads();
     if (sh.pick[0] == 0u) return;  // first to arrive: the other workgroup merges
     if (tid == 0) __hip_atomic_store(xcnt + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -8,7 +8,8 @@ bit-identical results. Covered: the metadata build, the score's tail-page
 refresh, dense and selective decode on the units and the stream splits (the
 matrix-core and vector-ALU page loops), both paths of the sparse step, and
 the cascade prefix (a single bad page, and a whole prefix split of bad
-pages).
+pages). Checked mode also reports a fused-path workspace whose row counters
+were not zeroed.
 
 The bad ids are planted in copies of the device tables; the oracle always
 reads the original, valid tables (CS336 lecture 10 page, §9.2: the block
@@ -301,3 +302,34 @@ def test_meta_build_and_tail_refresh_skip_bad_ids():
     gs2, _ = qsa.score_pages(g.q, kv, m2, refresh_tail=True)
     qsa.set_checked(False)
     assert qsa.get_checked() is False
+
+
+def test_fused_exchange_reports_an_unzeroed_workspace():
+    """The fused path's two workgroups per row count their arrivals in the
+    workspace, whose counters must be zero before its first use. In checked
+    mode a counter found at neither 0 nor 1 is reported (QSA_ERR_DEVICE);
+    with the counters zeroed the same call is clean and leaves them zero."""
+    c = _case("exch", [1000, 1537, 700, 16], 8, 2)
+    g = c.to(DEV)
+    kv = qsa.PagedKV.from_case(g)
+    meta = qsa.build_page_meta(kv)
+    stride, k = int(meta.shape[2]), 30
+    rows = c.B * c.Hkv
+    need = qsa.sparse_decode_workspace_size(kv, c.Hq, stride, k, "fused")
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    counters = ws[:rows * 4].view(torch.int32)
+    counters[1] = 5  # row 1's counter left nonzero (a workspace that was not zeroed)
+    msg = _checked_error(lambda: qsa.sparse_decode(g.q, kv, meta, k, sm_scale=c.sm_scale, path="fused",
+                                                   workspace=ws))
+    assert "not zeroed" in msg, msg
+    counters.zero_()
+    qsa.set_checked(True)
+    try:
+        ref = qsa.sparse_decode(g.q, kv, meta, k, sm_scale=c.sm_scale, path="fused")
+        out = qsa.sparse_decode(g.q, kv, meta, k, sm_scale=c.sm_scale, path="fused", workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        qsa.set_checked(False)
+    assert torch.equal(out[0], ref[0]) and torch.equal(out[1], ref[1])
+    assert int(counters.abs().sum()) == 0
