@@ -69,7 +69,6 @@ struct RowShared {
   uint32_t red[2][kRowWaves];
   uint32_t wsum[kRowWaves];
   uint32_t pick[3];
-  int chunk_cursor;  // next score chunk to hand out
 };
 
 // S = 2 workgroups share one row when there are too few rows to fill the
@@ -126,10 +125,11 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
   const int slot = lane >> 4;  // which of the wave's 4 pages of a step
 
   // ---- phase 1: scores ---------------------------------------------------
-  // The row's pages are scored in chunks of kChunkPages consecutive pages:
-  // chunks w and w + W first, then whichever chunk an LDS counter hands out
-  // next, so that waves whose loads return late score fewer chunks (a
-  // page's score does not depend on which wave computes it).
+  // The row's pages are scored in chunks of kChunkPages consecutive pages,
+  // wave w taking chunks w, w + W, w + 2W, ... (W waves). With two
+  // workgroups per row both then read a chunk's records at about the same
+  // time; this measured faster than handing chunks out on demand from an
+  // LDS counter (and needs no barrier before the loop).
   const int L = seq_lens[b];
   const int tbase = page_indptr[b];
   // page records: [m | M] (512 bytes) or a centroid row (256 bytes)
@@ -161,7 +161,6 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     issue(cc[u], bm[u], bM[u]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (tid == 0) sh.chunk_cursor = kScoreBufs * kRowWaves;
   if constexpr (!kCentroid) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -211,7 +210,6 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
     }
     return gmax;
   };
-  __syncthreads();  // the chunk counter (waits for LDS and scalar loads only)
   if (tail_ok && wave == 0) {
     uint4 tmn, tmx;
     const int valid = min(kPage, L - kPage * jt);
@@ -240,11 +238,6 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
       if (c == 0 && ok) sh.u.s.key[j] = score_key(gmax);
     }
   };
-  auto grab = [&]() -> int {
-    int e = 0;
-    if (lane == 0) e = atomicAdd(&sh.chunk_cursor, 1);
-    return __builtin_amdgcn_readfirstlane(e);
-  };
   // kScoreBufs buffers in rotation: while one buffer's chunk is scored the
   // others' records are in flight; a scored buffer is refilled with the next
   // chunk at once. The loop body has no early exit (chunks past the row are
@@ -255,7 +248,7 @@ __global__ void __launch_bounds__(kRowThreads) sparse_row_kernel(
 #pragma unroll
     for (int u = 0; u < kScoreBufs; ++u) {
       score(cc[u], bm[u], bM[u]);
-      cc[u] = grab();
+      cc[u] += kScoreBufs * kRowWaves;
       issue(min(cc[u], nchunks), bm[u], bM[u]);
       __builtin_amdgcn_sched_barrier(0);
       more |= cc[u] < nchunks;
