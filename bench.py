@@ -60,10 +60,10 @@ PREFIX_SRC = ["cascade.hip", "cascade_prefix.h", "qsa_device.h", "qsa_internal.h
 # (c2 dense and c3: split-K decode + merge; c5: the interleaved prefix and
 # suffix-row kernel + merge; 'cascade_sparse:overlap' is that kernel alone).
 MEASURED = {
-    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 42.10, "traffic": 207247127, "l2_hit": 0.2100,
-        "sources": FUSED_SRC, "sha256_16": "268a6d06db0ce2aa", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
-    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 40.79,
-        "sources": FUSED_SRC, "sha256_16": "268a6d06db0ce2aa", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'fused', 'bound'): {"kernel_us": 41.72, "traffic": 207499046, "l2_hit": 0.2089,
+        "sources": FUSED_SRC, "sha256_16": "0bfe74208e0ae10c", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
+    ('c2_sparse', 'fused', 'centroid'): {"kernel_us": 40.53,
+        "sources": FUSED_SRC, "sha256_16": "0bfe74208e0ae10c", "profile": "profiles/sparse_row_kernel_c2_sparse.md"},
     ('c2_sparse', 'dense', 'bound'): {"kernel_us": 99.26, "traffic": 547351053,
         "sources": DECODE_SRC, "sha256_16": "b6341b0be119dc22", "profile": "profiles/sparse_vs_dense_traffic_c2_sparse.md"},
     ('c3_dense', 'dense', 'bound'): {"kernel_us": 794.40, "traffic": 5163543546, "l2_hit": 0.3350,
