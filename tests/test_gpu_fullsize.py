@@ -230,6 +230,20 @@ def test_c2_fused_full_size(scorer):
     print(f"[c2 fused {scorer}] rows with the oracle's exact page set: {same}/{len(rows)}", flush=True)
 
 
+def test_c2_shape_fused_one_workgroup_per_row():
+    """c2's rows with one more sequence (136 rows: more than half the CUs,
+    so one workgroup per row instead of two): sampled rows against the
+    oracle, and the same bits from the call without the optional outputs."""
+    print("[case] c2 shape with 17 sequences, fused one-call step (one workgroup per row)", flush=True)
+    case = workloads.c2_sparse(device=DEV, B=17, n_sentinel=16)
+    kv = qsa.PagedKV.from_case(case)
+    assert qsa.sparse_decode_path(kv, case.Hq, 512, case.k_pages) == "fused"
+    assert qsa.sparse_decode_workspace_size(kv, case.Hq, 512, case.k_pages, "fused") == 0
+    meta, gs, sel, cnt, out, lse = _one_call_step(case, kv, "bound", "fused")
+    for b, h in ((0, 0), (5, 3), (11, 7), (16, 2), (16, 7)):
+        _check_step_row(case, "bound", "fused", b, h, meta, gs, sel, cnt, out, lse)
+
+
 def test_c4_long_full_size_every_sequence():
     """The long-context step as benchmarked (one qsa_sparse_decode call; the
     library takes the split path for 8192-page rows), every sequence checked
