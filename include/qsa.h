@@ -280,8 +280,11 @@ qsa_status qsa_paged_decode_noalloc(const qsa_dims* dims, const void* q,
  * aligned; too small returns QSA_ERR_WORKSPACE. For the fused path it is 0
  * (ws may be NULL) unless rows are shared: then its first B * Hkv * 4 bytes
  * are per-row arrival counters, which must be zero before the workspace's
- * first use with this path; every call leaves them zero. A workspace serves
- * one call at a time (calls that overlap on one GPU need their own). */
+ * first use with this path; every fused call leaves them zero, but any other
+ * call given the same workspace may overwrite them (zero them again before
+ * the next fused call; checked mode reports counters that are not). A
+ * workspace serves one call at a time (calls that overlap on one GPU need
+ * their own). */
 typedef enum qsa_path {
   QSA_PATH_AUTO = 0,
   QSA_PATH_FUSED = 1,

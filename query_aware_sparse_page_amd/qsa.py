@@ -396,8 +396,9 @@ def sparse_decode(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, k: int, sm_s
     scorer="centroid": meta holds centroid rows (build_page_centroids) and
     pages are scored by q . centroid. workspace: a uint8 tensor of at least
     sparse_decode_workspace_size(...) bytes, zeroed before its first use (the
-    fused path keeps per-row counters in it and leaves them zero); without
-    one, a zeroed workspace is allocated for the call."""
+    fused path keeps per-row counters in it and leaves them zero; zero it
+    again after lending it to any other call); without one, a zeroed
+    workspace is allocated for the call."""
     if scorer not in ("bound", "centroid"):
         raise ValueError(f"scorer {scorer!r}")
     B, Hq, D = q.shape
